@@ -1,0 +1,413 @@
+"""fp64 CPU oracle for MLA absorbed decode over a paged latent KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library or its binding imports or
+calls this module; only the test-suite, the smoke check and the benchmark's
+CPU-baseline leg do.  It shares no code with the HIP path.
+
+Every function computes the plain definition of what the method reaches, in
+numpy float64, with library matmuls as the only building blocks and no
+blocking or fusion beyond what the definitions state.  Inputs are the exact
+values of the stored tensors (bf16 bit patterns, fp8 codes times their fp32
+group scales), widened to float64.
+
+Sources (cited by title and section):
+  [Su]   "The Ultimate Tug-of-War Between Cache and Performance: From MHA, MQA,
+         GQA to MLA" -- the MHA equation, the MLA Part 1 absorption identity,
+         the Part 2 decoupled-RoPE equation, and the Part 3 MHA form
+         (eq:mla-mha) and decoding-stage MQA form (eq:mla-mqa).
+  [Riju] "Multi-Head Latent Attention vs GQA vs MQA: KV-Cache Compression
+         Explained" -- "A latent KV projection in PyTorch" (rope function,
+         non-absorbed module, absorbed decode sketch, the equivalence test),
+         "Worked numbers from real configs", "Interaction with quantisation
+         and paging".
+  [DL0107] "DL0107 Multi-head Latent Attention MLA" -- the cache holds the
+         latent and the decoupled RoPE key in rotated form.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes): interleaved RoPE pairs; the decode query sits at position
+S-1 and attends to itself; softmax scale 1/sqrt(d_nope + d_rope) on the sum of
+the latent and rotary score parts; empty sequence -> zero output and
+lse = -inf; fp8 = OCP E4M3 (max 448) with one fp32 scale per 128-wide group,
+scale = amax/448 in fp32 and codes by round-to-nearest-even after an fp32
+division.
+
+Parity pins: every function here is pinned by a test under tests/ against a
+closed form, a brute-force evaluation, a library routine or a number printed
+on the pages.  The fp8 scale formula is pinned only by internal consistency
+(parity unpinned against the pages, which give no quantiser).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F64 = np.float64
+
+# --------------------------------------------------------------------------
+# storage formats
+# --------------------------------------------------------------------------
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact: bf16 is the top half of a float32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(F64)
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """OCP E4M3 (e4m3fn) byte codes -> float64.
+
+    Layout s.eeee.mmm, exponent bias 7; e == 0 encodes subnormals m/8 * 2^-6;
+    S.1111.111 is NaN; there is no infinity, so the largest finite value is
+    1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = s * mag
+    return np.where((e == 15) & (m == 7), np.nan, val).astype(F64)
+
+
+_E4M3_POS = e4m3_to_f64(np.arange(0, 127, dtype=np.uint8))   # codes 0..126, ascending
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code to each value (ties to the even code), saturating at +-448.
+
+    Implemented as a nearest-neighbour search over the table of the 127
+    non-negative finite values, so it shares nothing with a bit-twiddling
+    encoder.
+    """
+    x = np.asarray(x, dtype=F64)
+    if np.isnan(x).any():
+        raise ValueError("NaN has no saturating e4m3 encoding here")
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_hi = _E4M3_POS[hi] - a
+    d_lo = a - _E4M3_POS[lo]
+    take_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(take_lo, lo, hi).astype(np.uint8)
+    neg = (x < 0) & (code != 0)
+    return np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def fp8_quantize_latent(c_bits, group=128):
+    """Quantise bf16 latent rows [..., 512] into e4m3 codes and fp32 group scales.
+
+    Per row and per group of `group` values: scale = amax / 448 computed as an
+    IEEE float32 division (1 when amax == 0); code = round-to-nearest-even of
+    float32(c / scale), saturated to +-448.  Both divisions are float32, as the
+    GPU computes them, so the integer codes are decided in the same precision.
+    """
+    c = np.asarray(bf16_to_f64(c_bits), dtype=np.float32)      # exact widening
+    shp = c.shape
+    g = c.reshape(shp[:-1] + (shp[-1] // group, group))
+    amax = np.abs(g).max(axis=-1)
+    scale = np.where(amax == 0, np.float32(1.0), amax / np.float32(448.0)).astype(np.float32)
+    q = (g / scale[..., None]).astype(np.float32)
+    codes = e4m3_encode(q.astype(F64)).reshape(shp)
+    return codes, scale
+
+
+def fp8_row_decode(rec):
+    """Packed fp8 cache records [..., 656] bytes -> (latent [...,512], rope [...,64]) float64."""
+    rec = np.asarray(rec, dtype=np.uint8)
+    codes = rec[..., :512]
+    rope_bits = np.ascontiguousarray(rec[..., 512:640]).view(np.uint16)
+    scales = np.ascontiguousarray(rec[..., 640:656]).view(np.float32).astype(F64)
+    c = e4m3_to_f64(codes).reshape(codes.shape[:-1] + (4, 128)) * scales[..., None]
+    return c.reshape(codes.shape), bf16_to_f64(rope_bits)
+
+
+# --------------------------------------------------------------------------
+# rotary position embedding  ([Riju] rope function; [Su] Part 2, R_m)
+# --------------------------------------------------------------------------
+
+
+def rope(v, pos, theta=10000.0) -> np.ndarray:
+    """Rotate interleaved pairs (v[2i], v[2i+1]) by angle pos * theta^(-2i/d).
+
+    v: [..., d] (d even); pos: scalar or array broadcastable to v[..., 0].
+    The pair convention and frequencies are those of the rope function in
+    [Riju], section "A latent KV projection in PyTorch"; R_m R_n^T = R_{m-n}
+    ([Su], Part 2) holds for this block-diagonal rotation.
+    """
+    v = np.asarray(v, dtype=F64)
+    d = v.shape[-1]
+    inv = 1.0 / (F64(theta) ** (np.arange(0, d, 2, dtype=F64) / d))
+    ang = np.asarray(pos, dtype=F64)[..., None] * inv
+    cos, sin = np.cos(ang), np.sin(ang)
+    x1, x2 = v[..., 0::2], v[..., 1::2]
+    out = np.empty(np.broadcast_shapes(v.shape, ang.shape[:-1] + (d,)), dtype=F64)
+    out[..., 0::2] = x1 * cos - x2 * sin
+    out[..., 1::2] = x1 * sin + x2 * cos
+    return out
+
+
+# --------------------------------------------------------------------------
+# absorption ([Su] MLA Part 1 identity and eq:mla-mqa)
+# --------------------------------------------------------------------------
+
+
+def absorb_q(q_nope, w_uk) -> np.ndarray:
+    """q_lat[..., h, :] = q_nope[..., h, :] W_UK[h]   (W_UK: [H, d_nope, d_c]).
+
+    The query side of the absorbed score: q^(s) k_i^(s)T = (x W_q^(s)) W_k^(s)T c_i^T
+    evaluated in the sequential order ([Su], MLA additional notes 1-2).
+    """
+    q = np.asarray(q_nope, dtype=F64)
+    w = np.asarray(w_uk, dtype=F64)
+    return np.einsum("...hn,hnc->...hc", q, w)
+
+
+def absorb_out(o_lat, w_uv) -> np.ndarray:
+    """o[..., h, :] = o_lat[..., h, :] W_UV[h]   (W_UV: [H, d_c, d_v]); [Su] eq:mla-mqa first line."""
+    o = np.asarray(o_lat, dtype=F64)
+    w = np.asarray(w_uv, dtype=F64)
+    return np.einsum("...hc,hcv->...hv", o, w)
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+
+
+def softmax_lse(s):
+    """Row softmax of scores s [..., S] and its log-sum-exp; empty rows give (zeros, -inf).
+
+    [Su] MHA equation: weights exp(q k^T) / sum_i exp(q k^T), evaluated with the
+    row maximum subtracted.
+    """
+    s = np.asarray(s, dtype=F64)
+    if s.shape[-1] == 0:
+        return np.zeros(s.shape, F64), np.full(s.shape[:-1], -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=-1, keepdims=True)
+    return e / z, (m + np.log(z))[..., 0]
+
+
+def decode_explicit(q_nope, q_rot, c, kr, w_uk, w_uv, scale, heads=None):
+    """One decode step of one sequence with per-head K and V rebuilt explicitly.
+
+    q_nope [H, d_nope], q_rot [H, d_r] (already rotated at the query position),
+    c [S, d_c] latents and kr [S, d_r] rotated shared keys of the S visible
+    tokens, W_UK [H, d_nope, d_c], W_UV [H, d_c, d_v].
+
+    For each head h ([Su] Part 2 decoupled-RoPE equation / eq:mla-mha;
+    [Riju] non-absorbed module):
+        K_h = [c W_UK[h]^T | kr],  V_h = c W_UV[h]
+        s   = scale * [q_nope[h] | q_rot[h]] . K_h^T
+        p   = softmax(s),  o[h] = p V_h
+    Also returns o_lat[h] = p c (the latent-weighted sum the absorbed form
+    produces, from the same p) and lse[h].
+    """
+    c = np.asarray(c, F64)
+    kr = np.asarray(kr, F64)
+    H = np.asarray(q_nope).shape[0]
+    heads = range(H) if heads is None else heads
+    o, o_lat, lse = [], [], []
+    for h in heads:
+        k_h = np.concatenate([c @ np.asarray(w_uk[h], F64).T, kr], axis=1)
+        v_h = c @ np.asarray(w_uv[h], F64)
+        qh = np.concatenate([np.asarray(q_nope[h], F64), np.asarray(q_rot[h], F64)])
+        p, l = softmax_lse(scale * (k_h @ qh))
+        o.append(p @ v_h if len(p) else np.zeros(v_h.shape[1]))
+        o_lat.append(p @ c if len(p) else np.zeros(c.shape[1]))
+        lse.append(l)
+    return np.array(o), np.array(o_lat), np.array(lse)
+
+
+def decode_absorbed(q_lat, q_rot, c, kr, scale):
+    """The decoding-stage MQA form ([Su] eq:mla-mqa; [Riju] absorbed decode sketch).
+
+    q_lat [H, d_c], q_rot [H, d_r]; every head scores the shared key [c | kr]:
+        s = scale * (q_lat . c^T + q_rot . kr^T),  o_lat = softmax(s) c.
+    Used by the self-checks; the parity references use decode_explicit.
+    """
+    c = np.asarray(c, F64)
+    kr = np.asarray(kr, F64)
+    s = scale * (np.asarray(q_lat, F64) @ c.T + np.asarray(q_rot, F64) @ kr.T)
+    p, lse = softmax_lse(s)
+    o_lat = p @ c if c.shape[0] else np.zeros((s.shape[0], c.shape[1]))
+    return o_lat, lse
+
+
+def combine_partials(o_parts, lse_parts):
+    """Merge attention over disjoint token chunks from (o_c, lse_c) pairs.
+
+    o = sum_c w_c o_c / sum_c w_c with w_c = exp(lse_c - L), L = max_c lse_c;
+    lse = L + log sum_c w_c.  Chunks with lse = -inf carry weight 0; if all are
+    empty the result is (0, -inf).  This is the softmax definition regrouped
+    over a partition of the tokens.
+    """
+    o_parts = np.asarray(o_parts, F64)
+    lse_parts = np.asarray(lse_parts, F64)
+    L = lse_parts.max(axis=0)
+    finite = np.isfinite(L)
+    Ls = np.where(finite, L, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - Ls), 0.0)
+    z = w.sum(axis=0)
+    zs = np.where(z > 0, z, 1.0)
+    o = (w[..., None] * o_parts).sum(axis=0) / zs[..., None]
+    lse = np.where(finite, Ls + np.log(zs), -np.inf)
+    return np.where(finite[..., None], o, 0.0), lse
+
+
+# --------------------------------------------------------------------------
+# paged cache access ([Riju] "Interaction with quantisation and paging")
+# --------------------------------------------------------------------------
+
+
+def gather_rows(pool, block_table, b, n_tokens, block_size=64):
+    """Logical rows 0..n_tokens-1 of sequence b from a paged pool [N_blk, block, ...].
+
+    block_table[b][j] is the physical page holding tokens [j*block, (j+1)*block).
+    """
+    idx = np.arange(n_tokens)
+    pages = np.asarray(block_table)[b, idx // block_size]
+    return np.asarray(pool)[pages, idx % block_size]
+
+
+def rows_to_latent_rope(rows, kv_fp8=False, d_c=512):
+    """Stored rows -> (c [S,d_c], kr [S,d_r]) as float64."""
+    if kv_fp8:
+        return fp8_row_decode(rows)
+    r = bf16_to_f64(rows)
+    return r[:, :d_c], r[:, d_c:]
+
+
+# --------------------------------------------------------------------------
+# whole-step references over a synthetic workload
+# --------------------------------------------------------------------------
+
+
+def reference_decode(inp, b, heads=None):
+    """Decode-only reference for sequence b: the stored cache and query as given.
+
+    Q = inp["q_decode"] [B,H,576] (latent query | rotated query), all S_b rows of
+    inp["cache_full"] attended.  Returns (o_lat [h,512], lse [h]).
+    """
+    S = int(inp["seq_lens"][b])
+    fp8 = inp["kv_dtype"] == 1
+    rows = gather_rows(inp["cache_full"], inp["block_table"], b, S, inp["block_size"])
+    c, kr = rows_to_latent_rope(rows, fp8)
+    q = bf16_to_f64(inp["q_decode"][b])
+    heads = list(range(q.shape[0])) if heads is None else list(heads)
+    return decode_absorbed(q[heads, :512], q[heads, 512:], c, kr, inp["scale"])
+
+
+def reference_step(inp, b, heads=None):
+    """Full decode step for sequence b from the step inputs (explicit K/V form).
+
+    The new token (position S_b - 1) contributes [c_new | RoPE(kr_new, S_b-1)]
+    (fp8 caches: c_new quantised and dequantised by this module's quantiser);
+    the query is [q_nope | RoPE(q_pe, S_b-1)].  Returns a dict with
+    q_lat, q_rot, new_c, new_kr (and fp8 codes/scales), o_lat, lse and o
+    for the requested heads.
+    """
+    S = int(inp["seq_lens"][b])
+    H = inp["H"]
+    heads = list(range(H)) if heads is None else list(heads)
+    fp8 = inp["kv_dtype"] == 1
+    theta = inp["theta"]
+    pos = max(S - 1, 0)
+    q_nope = bf16_to_f64(inp["q_nope"][b])
+    q_rot = rope(bf16_to_f64(inp["q_pe"][b]), pos, theta)
+    new = inp["kv_new"][b]
+    new_kr = rope(bf16_to_f64(new[512:]), pos, theta)
+    w_uk_h = bf16_to_f64(np.asarray(inp["w_uk"])[heads])
+    out = dict(q_rot=q_rot[heads], q_lat=absorb_q(q_nope[heads], w_uk_h), new_kr=new_kr)
+    if fp8:
+        codes, scales = fp8_quantize_latent(new[:512])
+        out["new_codes"], out["new_scales"] = codes, scales
+        new_c = (e4m3_to_f64(codes).reshape(4, 128) * scales.astype(F64)[:, None]).reshape(512)
+    else:
+        new_c = bf16_to_f64(new[:512])
+    out["new_c"] = new_c
+    if S == 0:
+        n = len(heads)
+        out.update(o_lat=np.zeros((n, 512)), lse=np.full(n, -np.inf), o=np.zeros((n, 128)))
+        return out
+    rows = gather_rows(inp["cache_step"], inp["block_table"], b, S - 1, inp["block_size"])
+    c, kr = rows_to_latent_rope(rows, fp8)
+    c = np.concatenate([c, new_c[None]], 0)
+    kr = np.concatenate([kr, new_kr[None]], 0)
+    w_uk = bf16_to_f64(inp["w_uk"])
+    w_uv = bf16_to_f64(inp["w_uv"])
+    o, o_lat, lse = decode_explicit(q_nope, q_rot, c, kr, w_uk, w_uv, inp["scale"], heads)
+    out.update(o=o, o_lat=o_lat, lse=lse)
+    return out
+
+
+# --------------------------------------------------------------------------
+# MHA-form prefill (tiny fp32 workload): [Su] eq:mla-mha without the query
+# latent, i.e. the Part 2 equation; [Riju] non-absorbed module with is_causal
+# --------------------------------------------------------------------------
+
+
+def prefill_mha_form(x, w_dkv, w_kr, w_q, w_uk, w_uv, d_nope, d_r, scale, theta=10000.0):
+    """Causal attention over all positions of x [S, d] in the explicit (MHA) form.
+
+    c_t = x_t W_DKV, kr_t = RoPE(x_t W_KR, t), q_t^(h) = [x_t W_Q^(h)_nope |
+    RoPE(x_t W_Q^(h)_rope, t)], K^(h) = [c W_UK[h]^T | kr], V^(h) = c W_UV[h];
+    o_t^(h) = sum_{i<=t} softmax_i(scale q_t^(h) . K_i^(h)) V_i^(h).
+    Returns (o [S,H,d_v], c [S,d_c], kr [S,d_r], q_nope [S,H,d_nope], q_rot [S,H,d_r]).
+    """
+    x = np.asarray(x, F64)
+    S = x.shape[0]
+    H = np.asarray(w_uk).shape[0]
+    pos = np.arange(S, dtype=F64)
+    c = x @ np.asarray(w_dkv, F64)
+    kr = rope(x @ np.asarray(w_kr, F64), pos, theta)
+    q = (x @ np.asarray(w_q, F64)).reshape(S, H, d_nope + d_r)
+    q_nope = q[..., :d_nope]
+    q_rot = rope(q[..., d_nope:], pos[:, None], theta)
+    o = np.zeros((S, H, np.asarray(w_uv).shape[2]))
+    for h in range(H):
+        k_h = np.concatenate([c @ np.asarray(w_uk[h], F64).T, kr], 1)
+        v_h = c @ np.asarray(w_uv[h], F64)
+        q_h = np.concatenate([q_nope[:, h], q_rot[:, h]], 1)
+        s = scale * (q_h @ k_h.T)
+        s = np.where(np.tril(np.ones((S, S), bool)), s, -np.inf)
+        p, _ = softmax_lse(s)
+        o[:, h] = p @ v_h
+    return o, c, kr, q_nope, q_rot
+
+
+# --------------------------------------------------------------------------
+# cache-size arithmetic ([Riju] "The Cache Arithmetic", "Worked numbers")
+# --------------------------------------------------------------------------
+
+
+def cache_elements_per_token(kind, layers=1, n_heads=0, d_h=0, n_groups=0, d_c=0, d_r=0):
+    """Cached scalars per token: MHA 2 n_h d_h, MQA 2 d_h, GQA 2 n_g d_h, MLA d_c + d_r (per layer)."""
+    per_layer = {
+        "mha": 2 * n_heads * d_h,
+        "mqa": 2 * d_h,
+        "gqa": 2 * n_groups * d_h,
+        "mla": d_c + d_r,
+    }[kind]
+    return per_layer * layers
+
+
+def fp8_row_bytes(d_c=512, d_r=64, group=128):
+    """Bytes of one packed fp8 cache record: codes + bf16 rotary key + fp32 group scales."""
+    return d_c + 2 * d_r + 4 * (d_c // group)
+
+
+def quantise_roundtrip_bound(scale, x):
+    """Half the e4m3 spacing at |x|/scale, times scale: the rounding bound of one value."""
+    a = np.minimum(np.abs(np.asarray(x, F64)) / scale, E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="right"), 1, 126)
+    return 0.5 * (_E4M3_POS[hi] - _E4M3_POS[hi - 1]) * scale
+
+
+def sdpa_scale(d_nope, d_r):
+    """Softmax scale 1/sqrt(d_nope + d_rope) ([Riju] absorbed decode sketch)."""
+    return 1.0 / math.sqrt(d_nope + d_r)

@@ -1,0 +1,392 @@
+"""Pins for the fp64 oracle: each check ties it to something other than itself.
+
+Closed forms, brute-force evaluation, library routines (torch SDPA, torch's
+float8_e4m3fn dtype) and the numbers the pages print.  A plausible mistake in
+the oracle -- a dropped rotary part, a transposed weight, a wrong pair
+convention, a missing scale, a wrong combine weight -- fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(12345)
+
+
+def _rand(*shape, rng=RNG):
+    return rng.standard_normal(shape)
+
+
+# ---------------------------------------------------------------- RoPE (PIN-3)
+def test_rope_pair_convention_closed_form():
+    # d = 4, theta = 100: pair 0 turns at 1 rad/position, pair 1 at 100^(-1/2) = 0.1.
+    for pos in [0.0, 1.0, 3.7, 1000.0]:
+        e = np.eye(4)
+        r = oracle.rope(e, pos, theta=100.0)
+        c0, s0 = math.cos(pos), math.sin(pos)
+        c1, s1 = math.cos(0.1 * pos), math.sin(0.1 * pos)
+        np.testing.assert_allclose(r[0], [c0, s0, 0, 0], atol=1e-12)
+        np.testing.assert_allclose(r[1], [-s0, c0, 0, 0], atol=1e-12)
+        np.testing.assert_allclose(r[2], [0, 0, c1, s1], atol=1e-12)
+        np.testing.assert_allclose(r[3], [0, 0, -s1, c1], atol=1e-12)
+
+
+def test_rope_frequencies_d64():
+    theta = 10000.0
+    e = np.eye(64)[0::2]          # unit vectors on the first element of each pair
+    r = oracle.rope(e, 1.0, theta)
+    for i in range(32):
+        w = theta ** (-2.0 * i / 64)
+        assert abs(r[i, 2 * i] - math.cos(w)) < 1e-14
+        assert abs(r[i, 2 * i + 1] - math.sin(w)) < 1e-14
+
+
+def test_rope_identity_norm_and_relative_position():
+    q, k = _rand(64), _rand(64)
+    np.testing.assert_allclose(oracle.rope(q, 0.0), q, atol=0, rtol=0)
+    for m in [0, 5, 4095, 32767]:
+        assert abs(np.linalg.norm(oracle.rope(q, m)) - np.linalg.norm(q)) < 1e-12
+    # <R_m q, R_n k> depends only on m - n (R_m R_n^T = R_{m-n}).
+    for m, n, s in [(3, 1, 7), (4095, 10, 20000), (32768, 32760, -30000), (0, 9, 12345)]:
+        a = oracle.rope(q, m) @ oracle.rope(k, n)
+        b = oracle.rope(q, m + s) @ oracle.rope(k, n + s)
+        assert abs(a - b) < 1e-10 * (1 + abs(a))
+
+
+def test_rope_broadcast_positions():
+    v = _rand(5, 8)
+    pos = np.arange(5.0)
+    r = oracle.rope(v, pos)
+    for t in range(5):
+        np.testing.assert_allclose(r[t], oracle.rope(v[t], float(t)), atol=1e-15)
+
+
+# ----------------------------------------------------- brute-force attention
+def _brute_decode(q_nope, q_rot, c, kr, w_uk, w_uv, scale):
+    """Pure-Python loops over the explicit form; no numpy algebra."""
+    H, dn = len(q_nope), len(q_nope[0])
+    S, dc = len(c), len(c[0])
+    dr, dv = len(kr[0]), len(w_uv[0][0])
+    out, lses = [], []
+    for h in range(H):
+        scores = []
+        for t in range(S):
+            k = [sum(c[t][j] * w_uk[h][n][j] for j in range(dc)) for n in range(dn)]
+            k += [kr[t][r] for r in range(dr)]
+            q = list(q_nope[h]) + list(q_rot[h])
+            scores.append(scale * sum(qa * ka for qa, ka in zip(q, k)))
+        m = max(scores)
+        ex = [math.exp(s - m) for s in scores]
+        z = sum(ex)
+        lses.append(m + math.log(z))
+        o = [0.0] * dv
+        for t in range(S):
+            v = [sum(c[t][j] * w_uv[h][j][e] for j in range(dc)) for e in range(dv)]
+            for e in range(dv):
+                o[e] += ex[t] / z * v[e]
+        out.append(o)
+    return np.array(out), np.array(lses)
+
+
+def test_decode_explicit_matches_brute_force():
+    rng = np.random.default_rng(7)
+    H, dn, dc, dr, dv, S = 3, 3, 5, 2, 4, 6
+    q_nope, q_rot = _rand(H, dn, rng=rng), _rand(H, dr, rng=rng)
+    c, kr = _rand(S, dc, rng=rng), _rand(S, dr, rng=rng)
+    w_uk, w_uv = _rand(H, dn, dc, rng=rng), _rand(H, dc, dv, rng=rng)
+    o, o_lat, lse = oracle.decode_explicit(q_nope, q_rot, c, kr, w_uk, w_uv, 0.37)
+    ob, lb = _brute_decode(q_nope, q_rot, c, kr, w_uk, w_uv, 0.37)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lb, rtol=1e-13)
+    # o_lat is the latent-weighted sum with the same weights: o = o_lat W_UV.
+    np.testing.assert_allclose(oracle.absorb_out(o_lat, w_uv), o, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------- absorption (PIN-1)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_absorbed_equals_explicit_random(seed):
+    rng = np.random.default_rng(seed)
+    H, dn, dc, dr, dv, S = 4, 6, 10, 4, 5, 17
+    q_nope, q_rot = _rand(H, dn, rng=rng), _rand(H, dr, rng=rng)
+    c, kr = _rand(S, dc, rng=rng), _rand(S, dr, rng=rng)
+    w_uk, w_uv = _rand(H, dn, dc, rng=rng), _rand(H, dc, dv, rng=rng)
+    scale = 1 / math.sqrt(dn + dr)
+    o, o_lat_e, lse_e = oracle.decode_explicit(q_nope, q_rot, c, kr, w_uk, w_uv, scale)
+    q_lat = oracle.absorb_q(q_nope, w_uk)
+    o_lat, lse = oracle.decode_absorbed(q_lat, q_rot, c, kr, scale)
+    np.testing.assert_allclose(o_lat, o_lat_e, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_e, rtol=1e-12)
+    np.testing.assert_allclose(oracle.absorb_out(o_lat, w_uv), o, rtol=1e-11, atol=1e-13)
+
+
+def test_absorbed_equals_explicit_workload0():
+    w = synth.workload(0)
+    o, c, kr, q_nope, q_rot = oracle.prefill_mha_form(
+        w["x"], w["w_dkv"], w["w_kr"], w["w_q"], w["w_uk"], w["w_uv"],
+        w["d_nope"], w["d_r"], w["scale"], w["theta"])
+    t = w["S"] - 1
+    oe, _, _ = oracle.decode_explicit(q_nope[t], q_rot[t], c, kr, w["w_uk"], w["w_uv"], w["scale"])
+    q_lat = oracle.absorb_q(q_nope[t], w["w_uk"])
+    o_lat, _ = oracle.decode_absorbed(q_lat, q_rot[t], c, kr, w["scale"])
+    oa = oracle.absorb_out(o_lat, w["w_uv"])
+    np.testing.assert_allclose(oa, oe, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(oe, o[t], rtol=1e-11, atol=1e-13)
+
+
+def test_rotary_part_is_not_dropped():
+    # With the latent query zero, scores come from the rotary part alone: a
+    # rotary key aligned with the query must dominate the softmax.
+    S, dc, dr = 8, 6, 4
+    c = np.eye(S, dc) if S <= dc else _rand(S, dc)
+    kr = np.zeros((S, dr))
+    kr[5] = [10, 0, 0, 0]
+    q_lat, q_rot = np.zeros((1, dc)), np.array([[10.0, 0, 0, 0]])
+    o_lat, _ = oracle.decode_absorbed(q_lat, q_rot, c, kr, 1.0)
+    np.testing.assert_allclose(o_lat[0], c[5], atol=1e-30 + 1e-40)
+
+
+# ----------------------------------------------------------- softmax (PIN-4)
+def test_softmax_rows_sum_to_one():
+    s = _rand(7, 300) * 20
+    p, lse = oracle.softmax_lse(s)
+    assert (p >= 0).all()
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.log(np.exp(s - s.max(-1, keepdims=True)).sum(-1)) + s.max(-1), rtol=1e-13)
+    import scipy.special
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=1e-13)
+
+
+# ------------------------------------------------------ closed forms (PIN-5)
+def test_closed_forms():
+    dc, dr, H = 12, 4, 3
+    c, kr = _rand(9, dc), _rand(9, dr)
+    q_lat, q_rot = _rand(H, dc), _rand(H, dr)
+    # one visible token: weight 1 on it, lse equals its score
+    o1, l1 = oracle.decode_absorbed(q_lat, q_rot, c[:1], kr[:1], 0.5)
+    np.testing.assert_array_equal(o1, np.broadcast_to(c[0], o1.shape))
+    np.testing.assert_allclose(l1, 0.5 * (q_lat @ c[0] + q_rot @ kr[0]), rtol=1e-14)
+    # all rows equal: the output is that row; lse = score + log S
+    ce, ke = np.repeat(c[:1], 9, 0), np.repeat(kr[:1], 9, 0)
+    oe, le = oracle.decode_absorbed(q_lat, q_rot, ce, ke, 0.5)
+    np.testing.assert_allclose(oe, np.broadcast_to(c[0], oe.shape), rtol=1e-14)
+    np.testing.assert_allclose(le, 0.5 * (q_lat @ c[0] + q_rot @ kr[0]) + math.log(9), rtol=1e-14)
+    # zero query (or zero scale): uniform weights -> mean of the latents
+    oz, lz = oracle.decode_absorbed(np.zeros((H, dc)), np.zeros((H, dr)), c, kr, 0.5)
+    np.testing.assert_allclose(oz, np.broadcast_to(c.mean(0), oz.shape), rtol=1e-13)
+    np.testing.assert_allclose(lz, math.log(9), rtol=1e-14)
+    # empty sequence
+    o0, l0 = oracle.decode_absorbed(q_lat, q_rot, c[:0], kr[:0], 0.5)
+    assert (o0 == 0).all() and np.isneginf(l0).all()
+
+
+# ---------------------------------------------------- library routine (PIN-6)
+def test_mqa_form_equals_torch_sdpa_fp64():
+    rng = np.random.default_rng(3)
+    H, S = 8, 200
+    c, kr = rng.standard_normal((S, 512)), rng.standard_normal((S, 64))
+    q = rng.standard_normal((H, 576)) * 0.05
+    scale = 1 / math.sqrt(192)
+    o_lat, _ = oracle.decode_absorbed(q[:, :512], q[:, 512:], c, kr, scale)
+    tq = torch.from_numpy(q)[None, :, None, :]
+    tk = torch.from_numpy(np.concatenate([c, kr], 1))[None, None].expand(1, H, S, 576)
+    tv = torch.from_numpy(c)[None, None].expand(1, H, S, 512)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)[0, :, 0].numpy()
+    np.testing.assert_allclose(o_lat, ref, rtol=1e-11, atol=1e-14)
+
+
+# --------------------------------------------------- split combine (PIN-7)
+@pytest.mark.parametrize("cuts", [[256], [1, 2, 300], [64, 128, 192, 256, 320, 384, 448, 512]])
+def test_split_combine_reproduces_unsplit(cuts):
+    rng = np.random.default_rng(11)
+    S, H = 530, 4
+    c, kr = rng.standard_normal((S, 512)), rng.standard_normal((S, 64))
+    q = rng.standard_normal((H, 576)) * 0.06
+    full, lse = oracle.decode_absorbed(q[:, :512], q[:, 512:], c, kr, 0.07)
+    bounds = [0] + cuts + [S, S]          # the last chunk is empty
+    parts = [oracle.decode_absorbed(q[:, :512], q[:, 512:], c[a:b], kr[a:b], 0.07)
+             for a, b in zip(bounds[:-1], bounds[1:])]
+    o, l = oracle.combine_partials([p[0] for p in parts], [p[1] for p in parts])
+    np.testing.assert_allclose(o, full, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l, lse, rtol=1e-13)
+
+
+def test_combine_all_empty():
+    o, l = oracle.combine_partials(np.zeros((3, 2, 5)), np.full((3, 2), -np.inf))
+    assert (o == 0).all() and np.isneginf(l).all()
+
+
+# ---------------------------------------------------------- paging (PIN-8)
+def test_page_permutation_and_contiguous_identity():
+    rng = np.random.default_rng(5)
+    S, blk = 200, 64
+    rows = rng.standard_normal((S, 576))
+    nb = (S + blk - 1) // blk
+    contiguous = np.zeros((nb, blk, 576))
+    contiguous.reshape(-1, 576)[:S] = rows
+    perm = rng.permutation(nb + 3)[:nb]
+    pool = np.full((nb + 3, blk, 576), np.nan)
+    for j in range(nb):
+        pool[perm[j], :min(blk, S - j * blk)] = rows[j * blk:(j + 1) * blk]
+    g1 = oracle.gather_rows(contiguous, np.arange(nb)[None], 0, S, blk)
+    g2 = oracle.gather_rows(pool, perm[None], 0, S, blk)
+    np.testing.assert_array_equal(g1, rows)
+    np.testing.assert_array_equal(g2, rows)
+
+
+def test_token_order_invariance():
+    rng = np.random.default_rng(6)
+    c, kr = rng.standard_normal((77, 512)), rng.standard_normal((77, 64))
+    q = rng.standard_normal((3, 576)) * 0.05
+    p = rng.permutation(77)
+    a, la = oracle.decode_absorbed(q[:, :512], q[:, 512:], c, kr, 0.07)
+    b, lb = oracle.decode_absorbed(q[:, :512], q[:, 512:], c[p], kr[p], 0.07)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(la, lb, rtol=1e-13)
+
+
+# ---------------------------------------------------------- prefix (PIN-9)
+def test_prefill_rows_equal_absorbed_decode_of_prefix():
+    w = synth.workload(0)
+    o, c, kr, q_nope, q_rot = oracle.prefill_mha_form(
+        w["x"], w["w_dkv"], w["w_kr"], w["w_q"], w["w_uk"], w["w_uv"],
+        w["d_nope"], w["d_r"], w["scale"], w["theta"])
+    for t in range(w["S"]):
+        q_lat = oracle.absorb_q(q_nope[t], w["w_uk"])
+        o_lat, _ = oracle.decode_absorbed(q_lat, q_rot[t], c[:t + 1], kr[:t + 1], w["scale"])
+        np.testing.assert_allclose(oracle.absorb_out(o_lat, w["w_uv"]), o[t], rtol=1e-10, atol=1e-12)
+    # position 0 attends only to itself: o_0 = c_0 W_UV
+    np.testing.assert_allclose(o[0], oracle.absorb_out(np.broadcast_to(c[0], (4, 32)), w["w_uv"]), rtol=1e-12)
+
+
+# -------------------------------------------------------------- fp8 (PIN-10)
+def test_e4m3_decode_matches_format_and_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    v = oracle.e4m3_to_f64(codes)
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0
+    assert v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6 and v[0x38] == 1.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.isfinite(v).sum() == 254
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(v[np.isfinite(v)], t[np.isfinite(v)])
+
+
+def test_e4m3_encode_rne_and_saturation():
+    enc = oracle.e4m3_encode
+    assert enc(1.0) == 0x38
+    assert enc(1.0625) == 0x38          # halfway 1 | 1.125 -> even mantissa (1.0)
+    assert enc(1.1875) == 0x3A          # halfway 1.125 | 1.25 -> even mantissa (1.25)
+    assert enc(449.0) == 0x7E and enc(1e9) == 0x7E and enc(-1e9) == 0xFE
+    assert enc(2.0 ** -10) == 0x00      # halfway 0 | 2^-9 -> even (0)
+    assert enc(1.5 * 2.0 ** -9) == 0x02  # halfway 2^-9 | 2^-8 -> even code 2
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF, 0x80)]
+    back = enc(oracle.e4m3_to_f64(np.array(finite, np.uint8)))
+    np.testing.assert_array_equal(back, np.array(finite, np.uint8))
+    x = (np.random.default_rng(9).standard_normal(20000) * 100).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(enc(x.astype(np.float64)), ref)
+
+
+def test_fp8_quantise_bounds():
+    rng = np.random.default_rng(4)
+    rows = synth.f32_to_bf16_bits(rng.standard_normal((50, 512)).astype(np.float32))
+    codes, scales = oracle.fp8_quantize_latent(rows)
+    x = oracle.bf16_to_f64(rows).reshape(50, 4, 128)
+    deq = oracle.e4m3_to_f64(codes).reshape(50, 4, 128) * scales[..., None]
+    bound = np.stack([oracle.quantise_roundtrip_bound(float(s), xg) for s, xg in
+                      zip(scales.reshape(-1), x.reshape(-1, 128))]).reshape(x.shape)
+    assert (np.abs(deq - x) <= bound * (1 + 1e-6) + 1e-30).all()
+    # the group's largest magnitude maps to +-448
+    amax_idx = np.abs(x).argmax(-1)
+    top = np.take_along_axis(codes.reshape(50, 4, 128), amax_idx[..., None], -1)[..., 0]
+    assert np.isin(top, [0x7E, 0xFE]).all()
+    # zero group -> scale 1 and zero codes
+    z_codes, z_scales = oracle.fp8_quantize_latent(np.zeros((1, 512), np.uint16))
+    assert (z_codes == 0).all() and (z_scales == 1).all()
+
+
+def test_fp8_row_decode_layout():
+    codes = np.array([0x38] * 128 + [0xB8] * 128 + [0x40] * 128 + [0x00] * 128, np.uint8)[None]
+    rope_bits = synth.f32_to_bf16_bits(np.arange(64, dtype=np.float32))[None]
+    scales = np.array([[0.5, 2.0, 0.25, 8.0]], np.float32)
+    rec = synth.pack_fp8_rows(codes, rope_bits, scales)
+    assert rec.shape[1] == oracle.fp8_row_bytes() == 656
+    c, r = oracle.fp8_row_decode(rec)
+    np.testing.assert_array_equal(c[0, :128], 0.5)
+    np.testing.assert_array_equal(c[0, 128:256], -2.0)
+    np.testing.assert_array_equal(c[0, 256:384], 0.5)   # 2.0 * 0.25
+    np.testing.assert_array_equal(c[0, 384:], 0.0)
+    np.testing.assert_array_equal(r[0], np.arange(64))
+
+
+# ------------------------------------------------ cache arithmetic (PIN-2)
+def test_cache_arithmetic_matches_printed_numbers():
+    g = json.load(open(os.path.join(GOLDEN, "cache_arithmetic.json")))
+    v3 = g["deepseek_v3"]
+    per = oracle.cache_elements_per_token("mla", 1, d_c=v3["kv_lora_rank"], d_r=v3["qk_rope_head_dim"])
+    assert per == v3["mla_elements_per_layer"] == synth.ROW
+    tot = oracle.cache_elements_per_token("mla", v3["layers"], d_c=512, d_r=64)
+    assert tot == v3["mla_elements_all_layers"]
+    assert 2 * tot == v3["mla_bytes_bf16_all_layers"]
+    assert round(2 * tot / 1024, 1) == v3["mla_kib_bf16_all_layers_rounded_1dp"]
+    mha1 = oracle.cache_elements_per_token("mha", 1, n_heads=128, d_h=128)
+    mha = oracle.cache_elements_per_token("mha", 61, n_heads=128, d_h=128)
+    assert mha1 == v3["mha_twin_elements_per_layer"] and mha == v3["mha_twin_elements_all_layers"]
+    assert round(mha / tot, 1) == v3["mha_over_mla_ratio_rounded_1dp"]
+    assert round(100 * (1 - tot / mha), 1) == v3["reduction_vs_mha_percent_rounded_1dp"]
+    gqa1 = oracle.cache_elements_per_token("gqa", 1, n_groups=8, d_h=128)
+    assert round(100 * (1 - per / gqa1), 1) == v3["reduction_vs_gqa8_percent_rounded_1dp"]
+    q = g["qwen25_72b_gqa"]
+    gq = oracle.cache_elements_per_token("gqa", q["layers"], n_groups=q["kv_heads"], d_h=q["d_h"])
+    assert gq == q["gqa_elements_all_layers"] and 2 * gq == q["gqa_bytes_bf16_all_layers"]
+    mh = oracle.cache_elements_per_token("mha", 80, n_heads=q["query_heads"], d_h=128)
+    assert 2 * mh / 2 ** 20 == q["mha_mib_bf16_per_token"]
+    assert 2 * oracle.cache_elements_per_token("mqa", 80, d_h=128) / 1024 == q["mqa_kib_bf16_per_token"]
+    seq = g["sequence_128k_gib_bf16"]
+    n = 128 * 1024
+    assert 2 * mh * n / 2 ** 30 == seq["mha"] and 2 * gq * n / 2 ** 30 == seq["gqa8"]
+    assert 2 * oracle.cache_elements_per_token("mqa", 80, d_h=128) * n / 2 ** 30 == seq["mqa"]
+    assert round(2 * tot * n / 2 ** 30, 1) == seq["mla_v3_rounded_1dp"]
+    cc = g["concurrency_32k_tokens_100gib"]
+    assert 2 * gq * 32768 / 2 ** 30 == cc["gqa8_gib_per_seq"]
+    assert round(2 * tot * 32768 / 2 ** 30, 2) == cc["mla_gib_per_seq_rounded_2dp"]
+    assert int(100 * 2 ** 30 // (2 * gq * 32768)) == cc["gqa8_sequences"]
+    assert int(100 * 2 ** 30 // (2 * tot * 32768)) == cc["mla_sequences"]
+    # DeepSeek-V2: d_c = 4 d_h, d_r = d_h/2 -> 4.5 d_h per layer = 2.25 groups of 2 d_h
+    assert oracle.cache_elements_per_token("mla", 1, d_c=4 * 128, d_r=64) / (2 * 128) == \
+        g["deepseek_v2_equivalent_gqa_groups"]
+
+
+# ----------------------------------------- whole-workload references (CPU)
+def test_reference_step_consistent_forms_workload1():
+    w = synth.workload(1)
+    for b in [0, 5]:
+        r = oracle.reference_step(w, b, heads=[0, 7, 15])
+        S = int(w["seq_lens"][b])
+        rows = oracle.gather_rows(w["cache_step"], w["block_table"], b, S - 1)
+        c, kr = oracle.rows_to_latent_rope(rows)
+        c = np.concatenate([c, r["new_c"][None]])
+        kr = np.concatenate([kr, r["new_kr"][None]])
+        o_lat, lse = oracle.decode_absorbed(r["q_lat"], r["q_rot"], c, kr, w["scale"])
+        np.testing.assert_allclose(o_lat, r["o_lat"], rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(lse, r["lse"], rtol=1e-12)
+        w_uv = oracle.bf16_to_f64(w["w_uv"])[[0, 7, 15]]
+        np.testing.assert_allclose(oracle.absorb_out(o_lat, w_uv), r["o"], rtol=1e-9, atol=1e-12)
+
+
+def test_reference_decode_empty_sequence():
+    w = synth.gaussian_workload(1, B=3, H=2, seq_lens=[0, 1, 65])
+    o, l = oracle.reference_decode(w, 0)
+    assert (o == 0).all() and np.isneginf(l).all()
+    o1, _ = oracle.reference_decode(w, 1)
+    c, _ = oracle.rows_to_latent_rope(oracle.gather_rows(w["cache_full"], w["block_table"], 1, 1))
+    np.testing.assert_array_equal(o1, np.broadcast_to(c[0], o1.shape))
+    r = oracle.reference_step(w, 0)
+    assert (r["o"] == 0).all() and np.isneginf(r["lse"]).all()
