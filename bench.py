@@ -1,0 +1,283 @@
+"""MLA absorbed-decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload: one decode step of a DeepSeek-V3-shaped MLA layer, B = 32 sequences
+of 4096 cached tokens, H = 128 heads, bf16 paged latent cache (64-token pages
+in a random permutation), inputs from the seeded generator (synth.workload(2)).
+A step is the whole hot path through the C ABI:
+  mla_absorb_q -> mla_rope_append_cache -> mla_decode_partial -> mla_decode_combine
+  -> mla_absorb_out
+(partial + combine are exactly mla_decode_paged split in two, so the decode
+kernel can be timed on its own with HIP events on the launch stream).
+
+Keeping reads honest: three copies of the latent cache (3 x 151 MB) and of the
+absorption weights rotate from step to step, so each step streams a cache that
+was last touched two steps (> 256 MB of traffic) earlier and cannot be served
+from the 256 MB Infinity Cache.
+
+Prints ONE JSON line: value = latent-cache bytes of the step / step time
+(GB/s, whole step); roofline = the decode kernel's algorithmic bytes / its
+average launch duration against 8 TB/s; cpu_baseline = the fp64 oracle on a
+bounded sample of the same workload, on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode latent-KV GB/s + TFLOP/s (% roofline), H=128 B=32 ctx=4K, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+ROW_BYTES = 576 * 2
+COPIES = 3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
+
+
+def cpu_baseline(w, budget_s):
+    """Time the oracle (explicit per-head K/V reconstruction, fp64) on whole sequences."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = len(os.sched_getaffinity(0))
+    S = int(w["seq_lens"][0])
+    t0 = time.perf_counter()
+    done = 0
+    while done < w["B"]:
+        oracle.reference_step(w, done)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_seq = dt / done
+    step_s = per_seq * w["B"]
+    return {
+        "value": round(w["B"] * S * ROW_BYTES / step_s / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} of {w['B']} sequences, all {w['H']} heads, full decode step in fp64 "
+                  f"(explicit K/V per head), {dt:.1f} s; scaled to the whole batch "
+                  f"({step_s:.1f} s per step)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path shards "
+              "by sequence with no exchange, so N GPUs run N independent copies of this step.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import mla_latent_kv_32_amd as mla
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    mla.lib()
+    dev = "cuda"
+    w = synth.workload(2)
+    B, H = w["B"], w["H"]
+    S = int(w["seq_lens"].max())
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    caches = [bf16(w["cache_step"]) for _ in range(COPIES)]
+    w_uks = [bf16(w["w_uk"]) for _ in range(COPIES)]
+    w_uvs = [bf16(w["w_uv"]) for _ in range(COPIES)]
+    q_nope, q_pe, kv_new = bf16(w["q_nope"]), bf16(w["q_pe"]), bf16(w["kv_new"])
+    sl = torch.from_numpy(w["seq_lens"]).to(dev)
+    bt = torch.from_numpy(w["block_table"]).to(dev)
+    split = args.split_tokens or mla.mla_decode_split_tokens(B, H, S)
+    ws = torch.empty(mla.mla_decode_workspace_bytes(B, H, S, split), dtype=torch.uint8, device=dev)
+    q = torch.empty((B, H, 576), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    o = torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c = i % COPIES
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_absorb_q(q_nope, w_uks[c], q)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.mla_rope_append_cache(q_pe, kv_new, sl, bt, caches[c], mla.KV_BF16, w["theta"], q)
+        if ev is not None:
+            ev[2].record(stream)
+        mla.mla_decode_partial(q, caches[c], mla.KV_BF16, bt, sl, S, w["scale"], ws, split_tokens=split)
+        if ev is not None:
+            ev[3].record(stream)
+        mla.mla_decode_combine(ws, sl, S, o_lat, lse, split_tokens=split)
+        if ev is not None:
+            ev[4].record(stream)
+        mla.mla_absorb_out(o_lat, w_uvs[c], o)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps.  Each step is replayed from a HIP graph
+    # captured once per rotating cache copy (the eager Python launch path costs
+    # more host time per step than the GPU needs).
+    graphs = []
+    try:
+        for c in range(COPIES):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for c in range(COPIES):
+            graphs[c].replay()
+        torch.cuda.synchronize()
+        mode = "hip-graph replay"
+    except Exception as e:  # pragma: no cover - falls back to eager launches
+        graphs = []
+        mode = f"eager launches (graph capture failed: {type(e).__name__})"
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    g0.record(stream)
+    for i in range(args.steps):
+        if graphs:
+            graphs[i % COPIES].replay()
+        else:
+            step(i)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = g0.elapsed_time(g1)
+    print(f"timed {args.steps} steps ({mode}) in {wall:.4f} s wall, {gpu_ms:.3f} ms GPU",
+          file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations: the same steps launched eagerly behind a GPU
+    # sleep, so every launch is queued before the GPU reaches it and the HIP
+    # events on the launch stream bracket kernel time only.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)      # long enough for every launch below to be queued first
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    names = ["absorb_q", "rope_append", "decode", "combine", "absorb_out"]
+    per = {n: [] for n in names}
+    for ev in events:
+        for k, n in enumerate(names):
+            per[n].append(ev[k].elapsed_time(ev[k + 1]) * 1e3)     # us
+    avg_us = {n: float(np.mean(v)) for n, v in per.items()}
+    eager_step_us = float(np.mean([ev[0].elapsed_time(ev[5]) * 1e3 for ev in events]))
+
+    cache_bytes = B * S * ROW_BYTES                    # algorithmic: every cached row read once
+    flops = 2.0 * B * H * S * (576 + 512)
+    ms_per_step = wall / args.steps * 1e3
+    value = cache_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_s = avg_us["decode"] * 1e-6
+    achieved = cache_bytes / dec_s / 1e9
+
+    # parity of the benchmarked buffers (last step wrote o, o_lat, lse; q holds this step's query)
+    parity = None
+    try:
+        import oracle
+        worst = 0.0
+        for b, heads in [(0, [0, 127]), (31, [64])]:
+            r = oracle.reference_step(w, b, heads)
+            got = o[b, heads].float().cpu().numpy().astype(np.float64)
+            err = np.abs(got - r["o"])
+            assert (err <= 2e-3 + 2e-2 * np.abs(r["o"])).all(), "benchmarked output differs from the oracle"
+            worst = max(worst, float(err.max()))
+        parity = {"checked": "o for (b,h) in (0,0),(0,127),(31,64)", "max_abs_err": worst, "ok": True}
+    except AssertionError as e:
+        parity = {"ok": False, "error": str(e)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "DeepSeek-V3-shaped MLA absorbed decode step, one layer: B=32, H=128, context 4096, "
+                        "bf16 paged latent cache [2048 pages, 64, 576], d_c=512, d_rope=64, d_nope=d_v=128",
+            "B": B, "H": H, "seq_len": S, "block_size": 64, "split_tokens": split,
+            "parallelism": "single GPU",
+        },
+        "step_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "decode_kernel": {
+            "avg_us": round(avg_us["decode"], 3),
+            "latent_gbs": round(achieved, 1),
+            "tflops": round(flops / dec_s / 1e12, 1),
+            "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(flops / dec_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        },
+        "kernels_avg_us": {k: round(v, 3) for k, v in avg_us.items()},
+        "timing": {"timed_region": mode, "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+                   "eager_step_gpu_us": round(eager_step_us, 3),
+                   "kernel_events": "HIP events on the launch stream around each call, launches queued "
+                                    "behind a GPU sleep"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "parity": parity,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) MLA absorbed-decode library.
+ *
+ * One decode step of one Multi-head Latent Attention layer, in the
+ * decoding-stage "MQA form": every head scores the same cached per-token row
+ * [c_KV (d_c = 512) | rotated shared RoPE key (d_r = 64)] = 576 values, so the
+ * per-head keys and values are never materialised.
+ *   Su, "The Ultimate Tug-of-War Between Cache and Performance: From MHA, MQA,
+ *   GQA to MLA", MLA Part 3, decoding-stage form (eq:mla-mqa);
+ *   Riju, "Multi-Head Latent Attention vs GQA vs MQA", "A latent KV projection
+ *   in PyTorch" (absorbed decode sketch) and "Interaction with quantisation
+ *   and paging".
+ *
+ * A step is four calls on one stream:
+ *   mla_absorb_q          q[:, :, 0:512]   = q_nope . W_UK          (query absorption)
+ *   mla_rope_append_cache q[:, :, 512:576] = RoPE(q_pe, S_b - 1); cache row S_b - 1 written
+ *   mla_decode_paged      o_latent = softmax(scale * q . rows^T) . rows[:, 0:512]
+ *   mla_absorb_out        o = o_latent . W_UV                      (value absorption)
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers owned by the caller; tensors are dense and
+ *     row-major (innermost dimension contiguous), strides implied by the
+ *     shapes.  Every tensor pointer must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *     enqueue work: they never synchronise, copy to the host or allocate.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     non-zero return nothing was launched.  Values that live in device memory
+ *     (seq_lens, block_table) are trusted: out-of-range page ids or lengths
+ *     beyond max_seq_len are undefined behaviour.
+ *   - bf16 is IEEE binary16-brain (1-8-7); every float -> bf16 conversion
+ *     rounds to nearest, ties to even.
+ *   - The library holds no global state; calls on different streams are
+ *     independent as long as their output buffers do not overlap.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+/* Longest chunk (tokens) one decode workgroup handles. */
+#define MLA_MAX_SPLIT_TOKENS 131072
+
+/* Status codes. */
+enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = -1,  /* null/misaligned pointer, non-positive or inconsistent size */
+  MLA_ERR_UNSUPPORTED = -2,       /* a size the kernels are not built for (d_c != 512, ...) */
+  MLA_ERR_WORKSPACE_TOO_SMALL = -3,
+  MLA_ERR_LAUNCH = -4             /* the HIP runtime rejected a kernel launch */
+};
+
+/* Latent-cache storage formats. */
+enum {
+  /* bf16 rows of 576 values: [c_KV (512) | rotated k_R (64)], 1152 bytes. */
+  MLA_KV_BF16 = 0,
+  /* Packed 656-byte rows: [512 e4m3 codes | 64 bf16 rotated k_R | 4 fp32
+     scales], one scale per 128-wide group of c_KV; c = code * scale.  OCP
+     E4M3 (max 448, no infinity).  The pages store the latent in FP8
+     ("Interaction with quantisation and paging") without fixing a layout;
+     this packing is this library's. */
+  MLA_KV_FP8_E4M3 = 1
+};
+
+/* Sizes the kernels are built for.  Other values return MLA_ERR_UNSUPPORTED. */
+#define MLA_D_C 512        /* kv_lora_rank */
+#define MLA_D_R 64         /* qk_rope_head_dim */
+#define MLA_D_NOPE 128     /* qk_nope_head_dim */
+#define MLA_D_V 128        /* v_head_dim */
+#define MLA_BLOCK_SIZE 64  /* tokens per cache page */
+
+/* Human-readable text for a status code (static storage). */
+const char *mla_status_string(int status);
+
+/* MLA_ABI_VERSION of the loaded library. */
+int mla_abi_version(void);
+
+/*
+ * Query absorption: q[b,h,0:d_c] = bf16( sum_k q_nope[b,h,k] * W_UK[h,k,:] ).
+ * The content part of every head's score is q_nope W_UK . c, so folding W_UK
+ * into the query lets the cached latent c serve as the key (Su, MLA Part 1
+ * identity; Riju, "Inside MLA: Absorption").  Evaluated in the sequential
+ * order (q_nope first, then W_UK), never through a pre-merged W_UQ W_UK
+ * (Su, MLA additional notes 1-2).  fp32 accumulation.
+ *   q_nope [B, H, d_nope] bf16     W_UK [H, d_nope, d_c] bf16
+ *   q      [B, H, d_c + d_r] bf16  (columns [0, d_c) written, the rest untouched)
+ * Requires d_nope == 128, d_c == 512, d_r == 64; B >= 1, H >= 1.
+ */
+int mla_absorb_q(const void *q_nope, const void *w_uk, void *q,
+                 int B, int H, int d_nope, int d_c, int d_r, void *stream);
+
+/*
+ * Decoupled RoPE and cache append for the token at position p_b = seq_lens[b]-1
+ * (Su, MLA Part 2: the rotary key is shared by all heads and computed from the
+ * hidden state; DL0107: it is cached already rotated).  Rotation: interleaved
+ * pairs (v[2i], v[2i+1]) turned by p_b * theta^(-2i/d_r) (Riju, rope function in
+ * "A latent KV projection in PyTorch"); angles in float64, rotation in float32.
+ *   q_pe        [B, H, d_r] bf16, unrotated
+ *   kv_new      [B, d_c + d_r] bf16: latent c_KV then the unrotated shared key
+ *   seq_lens    [B] int32, counts the token being appended (0 = idle slot)
+ *   block_table [B, max_blocks_per_seq] int32: page of tokens [64j, 64j+64)
+ *   kv_cache    [num_blocks, block_size, row] in format kv_dtype
+ *   q           [B, H, d_c + d_r] bf16: columns [d_c, d_c + d_r) receive RoPE(q_pe, p_b)
+ * The row (page block_table[b][p_b / 64], slot p_b % 64) receives
+ * [c_KV | RoPE(k_R, p_b)]; for MLA_KV_FP8_E4M3 the latent is quantised per
+ * 128-group with scale = amax / 448 (fp32 division; 1 if amax == 0) and
+ * code = round-to-nearest-even(c / scale) saturated to +-448.
+ * seq_lens[b] == 0: no row is written and the query is rotated at position 0.
+ */
+int mla_rope_append_cache(const void *q_pe, const void *kv_new, const int32_t *seq_lens,
+                          const int32_t *block_table, int max_blocks_per_seq,
+                          void *kv_cache, int kv_dtype, int num_blocks, int block_size,
+                          float rope_theta, void *q, int B, int H, int d_c, int d_r,
+                          void *stream);
+
+/*
+ * Bytes of the split-KV workspace for these sizes: partial outputs
+ * o_part[B][n_chunks][H][512] fp32 followed (at the next 256-byte boundary)
+ * by lse_part[B][n_chunks][H] fp32, n_chunks = ceil(max_seq_len / split).
+ * split_tokens as passed to the decode calls (0 = library choice).
+ * mla_decode_paged needs the workspace only when n_chunks > 1.
+ * Returns 0 for invalid sizes or max_seq_len == 0.
+ */
+size_t mla_decode_workspace_bytes(int B, int H, int max_seq_len, int split_tokens);
+
+/* Split size (tokens) mla_decode_paged uses for split_tokens == 0. */
+int mla_decode_split_tokens(int B, int H, int max_seq_len);
+
+/*
+ * Absorbed decode attention over the paged latent cache (Su, eq:mla-mqa:
+ * o^(s) = sum_i exp(q^(s) k_i) c_i / sum_i exp(q^(s) k_i) with the shared key
+ * k_i = [c_i | rotated k_R,i]; Riju, absorbed decode sketch):
+ *   s[b,h,t]  = softmax_scale * (q[b,h,:] . row_t)            t < seq_lens[b]
+ *   o_latent  = sum_t softmax(s)_t row_t[0:d_c],   lse = log sum_t exp(s_t)
+ * The row of the newest token (t = seq_lens[b]-1) is included.  Rows are
+ * streamed once per head group of up to 128 heads; MFMA with the heads as the
+ * matrix dimension, online softmax in fp32, P rounded to bf16 for P.V.
+ *   q           [B, H, 576] bf16
+ *   kv_cache    as in mla_rope_append_cache
+ *   seq_lens    [B] int32, each in [0, max_seq_len]
+ *   max_seq_len host-side upper bound on seq_lens (sizes the grid), >= 0,
+ *               <= max_blocks_per_seq * block_size
+ *   split_tokens tokens per split-KV chunk: 0 = library choice, else a
+ *               positive multiple of 64, at most MLA_MAX_SPLIT_TOKENS.  With more than one chunk per
+ *               sequence, partial (o, lse) pairs go to the workspace and a
+ *               log-sum-exp combine kernel merges them (every choice gives
+ *               the same result up to rounding).
+ *   workspace   device buffer of at least mla_decode_workspace_bytes(...)
+ *               bytes, needed when there is more than one chunk (may be NULL
+ *               otherwise); contents on entry ignored.
+ *   o_latent    [B, H, 512] bf16 output
+ *   lse         [B, H] fp32 natural-log log-sum-exp output, or NULL
+ * seq_lens[b] == 0 gives o_latent = 0 and lse = -inf.
+ */
+int mla_decode_paged(const void *q, const void *kv_cache, int kv_dtype,
+                     const int32_t *block_table, int max_blocks_per_seq,
+                     const int32_t *seq_lens, int max_seq_len, int num_blocks,
+                     int block_size, float softmax_scale, int split_tokens,
+                     void *workspace, size_t workspace_bytes,
+                     void *o_latent, float *lse, int B, int H, void *stream);
+
+/*
+ * The two halves of mla_decode_paged, for callers that merge chunks
+ * themselves (e.g. chunks computed on different devices, which is the same
+ * log-sum-exp merge).
+ *
+ * mla_decode_partial: attention of every head over each chunk of split_tokens
+ * tokens; writes o_part = (sum_t e^{s_t - m} row_t[0:512]) / (sum_t e^{s_t - m})
+ * and lse_part = m + log sum_t e^{s_t - m} (natural log) into the workspace
+ * layout above.  Chunks that start at or beyond seq_lens[b] are not written.
+ * Arguments as for mla_decode_paged.
+ *
+ * mla_decode_combine: o_latent[b,h] = sum_c w_c o_part[b,c,h] / sum_c w_c with
+ * w_c = exp(lse_part[b,c,h] - max_c lse_part), over the first
+ * ceil(seq_lens[b] / split) chunks; lse = max + log sum_c w_c.  An empty
+ * sequence gives zeros and lse = -inf.  split_tokens must be the value used
+ * for the partial call (0 = library choice, resolved identically).
+ */
+int mla_decode_partial(const void *q, const void *kv_cache, int kv_dtype,
+                       const int32_t *block_table, int max_blocks_per_seq,
+                       const int32_t *seq_lens, int max_seq_len, int num_blocks,
+                       int block_size, float softmax_scale, int split_tokens,
+                       void *workspace, size_t workspace_bytes, int B, int H, void *stream);
+
+int mla_decode_combine(const void *workspace, size_t workspace_bytes, const int32_t *seq_lens,
+                       int max_seq_len, int split_tokens, void *o_latent, float *lse,
+                       int B, int H, void *stream);
+
+/*
+ * Value absorption: o[b,h,:] = bf16( sum_c o_latent[b,h,c] * W_UV[h,c,:] ).
+ * The per-head value up-projection applied after the latent-weighted sum
+ * (Su, eq:mla-mqa first line: o_t = [o^(1) W_v^(1), ..., o^(h) W_v^(h)];
+ * Riju, "Inside MLA: Absorption").  The output projection W_O is the caller's.
+ *   o_latent [B, H, d_c] bf16   W_UV [H, d_c, d_v] bf16   o [B, H, d_v] bf16
+ * Requires d_c == 512, d_v == 128.
+ */
+int mla_absorb_out(const void *o_latent, const void *w_uv, void *o,
+                   int B, int H, int d_c, int d_v, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,208 @@
+"""MI355X (gfx950) MLA absorbed decode over a paged 576-wide latent cache.
+
+Thin ctypes binding over libmla.so (declared in include/mla.h).  The functions
+carry the C names and only marshal arguments: shapes are read from the torch
+tensors, pointers and the current HIP stream are passed through, and every
+step of the computation runs in the library's kernels.  There is no fallback:
+if libmla.so is missing or fails to load, every call raises.
+
+torch is used for device memory and streams only.  It is imported before the
+library is loaded so that both share torch's HIP runtime.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MLAError", "KV_BF16", "KV_FP8_E4M3", "D_C", "D_R", "D_NOPE", "D_V", "BLOCK_SIZE",
+    "FP8_ROW_BYTES", "library_path", "lib", "abi_version",
+    "mla_absorb_q", "mla_rope_append_cache", "mla_decode_paged", "mla_absorb_out",
+    "mla_decode_workspace_bytes", "mla_decode_split_tokens", "mla_decode_partial", "mla_decode_combine",
+]
+
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+D_C, D_R, D_NOPE, D_V, BLOCK_SIZE = 512, 64, 128, 128, 64
+FP8_ROW_BYTES = 656
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size or format",
+           -3: "workspace too small", -4: "kernel launch failed"}
+
+
+class MLAError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed with status {status} ({_STATUS.get(status, 'unknown')})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("MLA_LIBRARY", os.path.join(_HERE, "libmla.so"))
+
+
+def lib():
+    """Load libmla.so once; raises if it is absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() or "
+                           "python -m mla_latent_kv_32_amd.build")
+    L = ctypes.CDLL(path)
+    vp, i32p, c_int, c_float, c_size = (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_float, ctypes.c_size_t)
+    L.mla_status_string.argtypes = [c_int]
+    L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_abi_version.argtypes = []
+    L.mla_abi_version.restype = c_int
+    L.mla_absorb_q.argtypes = [vp, vp, vp, c_int, c_int, c_int, c_int, c_int, vp]
+    L.mla_absorb_q.restype = c_int
+    L.mla_rope_append_cache.argtypes = [vp, vp, i32p, i32p, c_int, vp, c_int, c_int, c_int, c_float,
+                                        vp, c_int, c_int, c_int, c_int, vp]
+    L.mla_rope_append_cache.restype = c_int
+    L.mla_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
+    L.mla_decode_workspace_bytes.restype = c_size
+    L.mla_decode_split_tokens.argtypes = [c_int, c_int, c_int]
+    L.mla_decode_split_tokens.restype = c_int
+    L.mla_decode_paged.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
+                                   vp, c_size, vp, vp, c_int, c_int, vp]
+    L.mla_decode_paged.restype = c_int
+    L.mla_decode_partial.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
+                                     vp, c_size, c_int, c_int, vp]
+    L.mla_decode_partial.restype = c_int
+    L.mla_decode_combine.argtypes = [vp, c_size, i32p, c_int, c_int, vp, vp, c_int, c_int, vp]
+    L.mla_decode_combine.restype = c_int
+    L.mla_absorb_out.argtypes = [vp, vp, vp, c_int, c_int, c_int, c_int, vp]
+    L.mla_absorb_out.restype = c_int
+    _LIB = L
+    return L
+
+
+def abi_version() -> int:
+    return lib().mla_abi_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MLAError(fn, status)
+
+
+def _dense(t, name, dtype=None):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def mla_absorb_q(q_nope, w_uk, q, stream=None):
+    """q[:, :, :512] = q_nope . W_UK (per head).  q_nope [B,H,128], w_uk [H,128,512], q [B,H,576]; bf16."""
+    B, H, dn = q_nope.shape
+    for t, n in ((q_nope, "q_nope"), (w_uk, "w_uk"), (q, "q")):
+        _dense(t, n, torch.bfloat16)
+    _check("mla_absorb_q", lib().mla_absorb_q(_ptr(q_nope), _ptr(w_uk), _ptr(q), B, H, dn,
+                                              w_uk.shape[2], q.shape[2] - w_uk.shape[2], _stream(stream)))
+
+
+def mla_rope_append_cache(q_pe, kv_new, seq_lens, block_table, kv_cache, kv_dtype, rope_theta, q,
+                          stream=None):
+    """Rotate q_pe into q[:, :, 512:] and append [c | RoPE(k_R)] at position seq_lens-1 of each sequence."""
+    B, H, dr = q_pe.shape
+    _dense(q_pe, "q_pe", torch.bfloat16)
+    _dense(kv_new, "kv_new", torch.bfloat16)
+    _dense(q, "q", torch.bfloat16)
+    _dense(seq_lens, "seq_lens", torch.int32)
+    _dense(block_table, "block_table", torch.int32)
+    _dense(kv_cache, "kv_cache")
+    _check("mla_rope_append_cache", lib().mla_rope_append_cache(
+        _ptr(q_pe), _ptr(kv_new), _ptr(seq_lens), _ptr(block_table), block_table.shape[1],
+        _ptr(kv_cache), int(kv_dtype), kv_cache.shape[0], kv_cache.shape[1], float(rope_theta),
+        _ptr(q), B, H, kv_new.shape[1] - dr, dr, _stream(stream)))
+
+
+def mla_decode_workspace_bytes(B, H, max_seq_len, split_tokens=0) -> int:
+    return int(lib().mla_decode_workspace_bytes(B, H, max_seq_len, split_tokens))
+
+
+def mla_decode_split_tokens(B, H, max_seq_len) -> int:
+    return int(lib().mla_decode_split_tokens(B, H, max_seq_len))
+
+
+def mla_decode_paged(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, softmax_scale, o_latent,
+                     lse=None, split_tokens=0, workspace=None, stream=None):
+    """o_latent = softmax(scale q . rows^T) rows[:, :512] over each sequence's paged rows.
+
+    q [B,H,576] bf16; kv_cache [num_blocks, 64, 576] bf16 (or [num_blocks, 64, 656] uint8 for
+    fp8); block_table [B, max_blocks] int32; seq_lens [B] int32; o_latent [B,H,512] bf16;
+    lse [B,H] float32 or None.  A workspace of mla_decode_workspace_bytes(...) bytes is
+    allocated with torch when not given.
+    """
+    B, H, _ = q.shape
+    _dense(q, "q", torch.bfloat16)
+    _dense(o_latent, "o_latent", torch.bfloat16)
+    _dense(kv_cache, "kv_cache")
+    _dense(block_table, "block_table", torch.int32)
+    _dense(seq_lens, "seq_lens", torch.int32)
+    if lse is not None:
+        _dense(lse, "lse", torch.float32)
+    sp = split_tokens or mla_decode_split_tokens(B, H, max_seq_len)
+    need = mla_decode_workspace_bytes(B, H, max_seq_len, split_tokens) if max_seq_len > sp else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_decode_paged", lib().mla_decode_paged(
+        _ptr(q), _ptr(kv_cache), int(kv_dtype), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+        int(max_seq_len), kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(split_tokens),
+        _ptr(workspace), ws_bytes, _ptr(o_latent), _ptr(lse), B, H, _stream(stream)))
+
+
+def mla_decode_partial(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, softmax_scale, workspace,
+                       split_tokens=0, stream=None):
+    """Per-chunk (o_part, lse_part) into `workspace` (layout in include/mla.h)."""
+    B, H, _ = q.shape
+    _dense(q, "q", torch.bfloat16)
+    _dense(kv_cache, "kv_cache")
+    _dense(block_table, "block_table", torch.int32)
+    _dense(seq_lens, "seq_lens", torch.int32)
+    _dense(workspace, "workspace")
+    _check("mla_decode_partial", lib().mla_decode_partial(
+        _ptr(q), _ptr(kv_cache), int(kv_dtype), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+        int(max_seq_len), kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(split_tokens),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, _stream(stream)))
+
+
+def mla_decode_combine(workspace, seq_lens, max_seq_len, o_latent, lse=None, split_tokens=0, stream=None):
+    """Log-sum-exp merge of the workspace partials into o_latent [B,H,512] bf16 (and lse)."""
+    B, H, _ = o_latent.shape
+    _dense(workspace, "workspace")
+    _dense(seq_lens, "seq_lens", torch.int32)
+    _dense(o_latent, "o_latent", torch.bfloat16)
+    if lse is not None:
+        _dense(lse, "lse", torch.float32)
+    _check("mla_decode_combine", lib().mla_decode_combine(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(seq_lens), int(max_seq_len),
+        int(split_tokens), _ptr(o_latent), _ptr(lse), B, H, _stream(stream)))
+
+
+def mla_absorb_out(o_latent, w_uv, o, stream=None):
+    """o = o_latent . W_UV (per head).  o_latent [B,H,512], w_uv [H,512,128], o [B,H,128]; bf16."""
+    B, H, dc = o_latent.shape
+    for t, n in ((o_latent, "o_latent"), (w_uv, "w_uv"), (o, "o")):
+        _dense(t, n, torch.bfloat16)
+    _check("mla_absorb_out", lib().mla_absorb_out(_ptr(o_latent), _ptr(w_uv), _ptr(o), B, H, dc,
+                                                  w_uv.shape[2], _stream(stream)))

@@ -1,0 +1,240 @@
+// C ABI of the MLA absorbed-decode library: argument validation, split
+// planning and kernel launches on the caller's stream.  See include/mla.h for
+// the contract of every entry point.
+#include <math.h>
+#include <stdint.h>
+
+#include "mla.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMinSplitTokens = 256;   // smallest chunk the planner picks
+constexpr int kDefaultCUs = 256;
+
+bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return kDefaultCUs;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return kDefaultCUs;
+  return cus;
+}
+
+int head_groups(int H) { return mla::decode_head_groups(H); }
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Chunk size giving roughly one workgroup per compute unit, never below
+// kMinSplitTokens, a multiple of the page size.
+int plan_split(int B, int H, int max_seq_len) {
+  int full = round_up(max_seq_len > 0 ? max_seq_len : 1, MLA_BLOCK_SIZE);
+  if (full > MLA_MAX_SPLIT_TOKENS) full = MLA_MAX_SPLIT_TOKENS;
+  const long items = static_cast<long>(B) * head_groups(H);
+  const int cus = device_cus();
+  if (items >= cus) return full;
+  const int n = static_cast<int>((cus + items - 1) / items);
+  int split = round_up((max_seq_len + n - 1) / n, MLA_BLOCK_SIZE);
+  if (split < kMinSplitTokens) split = kMinSplitTokens;
+  return split < full ? split : full;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t workspace_for(int B, int H, int n_splits) {
+  const size_t rows = static_cast<size_t>(B) * n_splits * H;
+  return align256(rows * MLA_D_C * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported size or format";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+int mla_absorb_q(const void *q_nope, const void *w_uk, void *q, int B, int H, int d_nope, int d_c,
+                 int d_r, void *stream) {
+  if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q) || B < 1 || H < 1)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (B > 65535 * 32 || H > 65535) return MLA_ERR_UNSUPPORTED;
+  if (d_nope != MLA_D_NOPE || d_c != MLA_D_C || d_r != MLA_D_R) return MLA_ERR_UNSUPPORTED;
+  return status_of(mla::launch_absorb_q(static_cast<const uint16_t *>(q_nope), static_cast<const uint16_t *>(w_uk),
+                                        static_cast<uint16_t *>(q), B, H, static_cast<hipStream_t>(stream)));
+}
+
+int mla_rope_append_cache(const void *q_pe, const void *kv_new, const int32_t *seq_lens,
+                          const int32_t *block_table, int max_blocks_per_seq, void *kv_cache, int kv_dtype,
+                          int num_blocks, int block_size, float rope_theta, void *q, int B, int H, int d_c,
+                          int d_r, void *stream) {
+  if (!aligned16(q_pe) || !aligned16(kv_new) || !aligned16(seq_lens) || !aligned16(block_table) ||
+      !aligned16(kv_cache) || !aligned16(q) || B < 1 || H < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      !(rope_theta > 0.0f) || !isfinite(rope_theta))
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_INVALID_ARGUMENT;
+  if (d_c != MLA_D_C || d_r != MLA_D_R || block_size != MLA_BLOCK_SIZE)
+    return MLA_ERR_UNSUPPORTED;
+  mla::RopeAppendArgs a;
+  a.q_pe = static_cast<const uint16_t *>(q_pe);
+  a.kv_new = static_cast<const uint16_t *>(kv_new);
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.cache = static_cast<uint8_t *>(kv_cache);
+  a.kv_fp8 = kv_dtype == MLA_KV_FP8_E4M3;
+  a.theta = static_cast<double>(rope_theta);
+  a.q = static_cast<uint16_t *>(q);
+  a.B = B;
+  a.H = H;
+  return status_of(mla::launch_rope_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int mla_decode_split_tokens(int B, int H, int max_seq_len) {
+  if (B < 1 || H < 1 || max_seq_len < 0) return 0;
+  return plan_split(B, H, max_seq_len);
+}
+
+size_t mla_decode_workspace_bytes(int B, int H, int max_seq_len, int split_tokens) {
+  if (B < 1 || H < 1 || max_seq_len <= 0 || split_tokens < 0 || split_tokens % MLA_BLOCK_SIZE ||
+      split_tokens > MLA_MAX_SPLIT_TOKENS)
+    return 0;
+  const int split = split_tokens ? split_tokens : plan_split(B, H, max_seq_len);
+  return workspace_for(B, H, (max_seq_len + split - 1) / split);
+}
+
+}  // extern "C"
+
+namespace {
+
+enum class DecodeMode { Paged, Partial };
+
+// Shared validation and argument set-up of mla_decode_paged / mla_decode_partial.
+int prepare_decode(DecodeMode mode, const void *q, const void *kv_cache, int kv_dtype,
+                   const int32_t *block_table, int max_blocks_per_seq, const int32_t *seq_lens,
+                   int max_seq_len, int num_blocks, int block_size, float softmax_scale, int split_tokens,
+                   void *workspace, size_t workspace_bytes, void *o_latent, float *lse, int B, int H,
+                   mla::DecodeArgs *a) {
+  const bool paged = mode == DecodeMode::Paged;
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(block_table) || !aligned16(seq_lens) ||
+      (paged && !aligned16(o_latent)) || (lse != nullptr && !aligned16(lse)) || B < 1 || H < 1 ||
+      max_blocks_per_seq < 1 || num_blocks < 1 || max_seq_len < 0 || !isfinite(softmax_scale) ||
+      split_tokens < 0 || split_tokens % MLA_BLOCK_SIZE != 0)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_INVALID_ARGUMENT;
+  if (block_size != MLA_BLOCK_SIZE) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<long>(max_seq_len) > static_cast<long>(max_blocks_per_seq) * block_size)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (kv_dtype != MLA_KV_BF16) return MLA_ERR_UNSUPPORTED;
+  if (split_tokens > MLA_MAX_SPLIT_TOKENS) return MLA_ERR_UNSUPPORTED;
+  const int split = split_tokens ? split_tokens : plan_split(B, H, max_seq_len);
+  const int n_splits = max_seq_len > 0 ? (max_seq_len + split - 1) / split : 1;
+  if (static_cast<long>(B) * n_splits > 2147483647L) return MLA_ERR_UNSUPPORTED;
+  const bool direct = paged && n_splits == 1;
+  const size_t need = direct ? 0 : workspace_for(B, H, n_splits);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return MLA_ERR_WORKSPACE_TOO_SMALL;
+  a->q = static_cast<const uint16_t *>(q);
+  a->cache = static_cast<const uint8_t *>(kv_cache);
+  a->block_table = block_table;
+  a->seq_lens = seq_lens;
+  a->max_blocks = max_blocks_per_seq;
+  a->B = B;
+  a->H = H;
+  a->split_tokens = split;
+  a->n_splits = n_splits;
+  a->direct = direct ? 1 : 0;
+  a->scale_log2 = softmax_scale * 1.44269504088896340736f;
+  a->o_latent = static_cast<uint16_t *>(o_latent);
+  a->lse = lse;
+  const size_t rows = static_cast<size_t>(B) * n_splits * H;
+  a->o_part = need ? static_cast<float *>(workspace) : nullptr;
+  a->lse_part = need ? reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
+                                                 align256(rows * MLA_D_C * sizeof(float)))
+                     : nullptr;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_paged(const void *q, const void *kv_cache, int kv_dtype, const int32_t *block_table,
+                     int max_blocks_per_seq, const int32_t *seq_lens, int max_seq_len, int num_blocks,
+                     int block_size, float softmax_scale, int split_tokens, void *workspace,
+                     size_t workspace_bytes, void *o_latent, float *lse, int B, int H, void *stream) {
+  mla::DecodeArgs a;
+  const int st = prepare_decode(DecodeMode::Paged, q, kv_cache, kv_dtype, block_table, max_blocks_per_seq,
+                                seq_lens, max_seq_len, num_blocks, block_size, softmax_scale, split_tokens,
+                                workspace, workspace_bytes, o_latent, lse, B, H, &a);
+  if (st != MLA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = mla::launch_decode(a, s);
+  if (e != hipSuccess || a.direct) return status_of(e);
+  return status_of(mla::launch_combine(a, s));
+}
+
+int mla_decode_partial(const void *q, const void *kv_cache, int kv_dtype, const int32_t *block_table,
+                       int max_blocks_per_seq, const int32_t *seq_lens, int max_seq_len, int num_blocks,
+                       int block_size, float softmax_scale, int split_tokens, void *workspace,
+                       size_t workspace_bytes, int B, int H, void *stream) {
+  if (max_seq_len <= 0) return MLA_ERR_INVALID_ARGUMENT;
+  mla::DecodeArgs a;
+  const int st = prepare_decode(DecodeMode::Partial, q, kv_cache, kv_dtype, block_table, max_blocks_per_seq,
+                                seq_lens, max_seq_len, num_blocks, block_size, softmax_scale, split_tokens,
+                                workspace, workspace_bytes, nullptr, nullptr, B, H, &a);
+  if (st != MLA_OK) return st;
+  return status_of(mla::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int mla_decode_combine(const void *workspace, size_t workspace_bytes, const int32_t *seq_lens, int max_seq_len,
+                       int split_tokens, void *o_latent, float *lse, int B, int H, void *stream) {
+  if (!aligned16(workspace) || !aligned16(seq_lens) || !aligned16(o_latent) ||
+      (lse != nullptr && !aligned16(lse)) || B < 1 || H < 1 || max_seq_len <= 0 || split_tokens < 0 ||
+      split_tokens % MLA_BLOCK_SIZE != 0)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (split_tokens > MLA_MAX_SPLIT_TOKENS) return MLA_ERR_UNSUPPORTED;
+  const int split = split_tokens ? split_tokens : plan_split(B, H, max_seq_len);
+  const int n_splits = (max_seq_len + split - 1) / split;
+  const size_t need = workspace_for(B, H, n_splits);
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  mla::DecodeArgs a = {};
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.H = H;
+  a.split_tokens = split;
+  a.n_splits = n_splits;
+  a.o_latent = static_cast<uint16_t *>(o_latent);
+  a.lse = lse;
+  const size_t rows = static_cast<size_t>(B) * n_splits * H;
+  a.o_part = static_cast<float *>(const_cast<void *>(workspace));
+  a.lse_part = reinterpret_cast<float *>(static_cast<uint8_t *>(const_cast<void *>(workspace)) +
+                                         align256(rows * MLA_D_C * sizeof(float)));
+  return status_of(mla::launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+int mla_absorb_out(const void *o_latent, const void *w_uv, void *o, int B, int H, int d_c, int d_v,
+                   void *stream) {
+  if (!aligned16(o_latent) || !aligned16(w_uv) || !aligned16(o) || B < 1 || H < 1)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (B > 65535 * 32 || H > 65535) return MLA_ERR_UNSUPPORTED;
+  if (d_c != MLA_D_C || d_v != MLA_D_V) return MLA_ERR_UNSUPPORTED;
+  return status_of(mla::launch_absorb_out(static_cast<const uint16_t *>(o_latent),
+                                          static_cast<const uint16_t *>(w_uv), static_cast<uint16_t *>(o), B, H,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Launch interfaces between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+
+struct DecodeArgs {
+  const uint16_t *q;            // [B, H, 576] bf16
+  const uint8_t *cache;         // paged pool
+  const int32_t *block_table;   // [B, max_blocks]
+  const int32_t *seq_lens;      // [B]
+  int max_blocks;
+  int B, H;
+  int split_tokens;             // multiple of 64
+  int n_splits;                 // chunks per sequence in the grid
+  int direct;                   // 1: one chunk, write o_latent / lse directly
+  float scale_log2;             // softmax_scale * log2(e)
+  uint16_t *o_latent;           // [B, H, 512] bf16
+  float *lse;                   // [B, H] or null
+  float *o_part;                // [B, n_splits, H, 512] fp32 (n_splits > 1)
+  float *lse_part;              // [B, n_splits, H] fp32
+};
+
+// Attention over each chunk; direct mode writes o_latent/lse, else partials.
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// Log-sum-exp merge of the partials into o_latent/lse.
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);
+
+// Waves per decode workgroup (16 heads each) and heads per workgroup.  At
+// least two waves share a block's copies so that three blocks in flight stay
+// within the 6-bit vector-memory counter (3 x 18 copies per wave).
+inline int decode_waves(int H) { return H <= 32 ? 2 : (H <= 64 ? 4 : 8); }
+inline int decode_head_groups(int H) { return (H + 16 * decode_waves(H) - 1) / (16 * decode_waves(H)); }
+
+// q[b,h,0:512] = q_nope[b,h,:] . W_UK[h]
+hipError_t launch_absorb_q(const uint16_t *q_nope, const uint16_t *w_uk, uint16_t *q, int B, int H,
+                           hipStream_t stream);
+// o[b,h,:] = o_latent[b,h,:] . W_UV[h]
+hipError_t launch_absorb_out(const uint16_t *o_latent, const uint16_t *w_uv, uint16_t *o, int B, int H,
+                             hipStream_t stream);
+
+struct RopeAppendArgs {
+  const uint16_t *q_pe;         // [B, H, 64]
+  const uint16_t *kv_new;       // [B, 576]
+  const int32_t *seq_lens;
+  const int32_t *block_table;
+  int max_blocks;
+  uint8_t *cache;
+  int kv_fp8;
+  double theta;
+  uint16_t *q;                  // [B, H, 576]
+  int B, H;
+};
+
+hipError_t launch_rope_append(const RopeAppendArgs &a, hipStream_t stream);
+
+}  // namespace mla

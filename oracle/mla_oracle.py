@@ -223,18 +223,23 @@ def decode_explicit(q_nope, q_rot, c, kr, w_uk, w_uv, scale, heads=None):
     return np.array(o), np.array(o_lat), np.array(lse)
 
 
-def decode_absorbed(q_lat, q_rot, c, kr, scale):
+def decode_absorbed(q_lat, q_rot, c, kr, scale, with_magnitude=False):
     """The decoding-stage MQA form ([Su] eq:mla-mqa; [Riju] absorbed decode sketch).
 
     q_lat [H, d_c], q_rot [H, d_r]; every head scores the shared key [c | kr]:
         s = scale * (q_lat . c^T + q_rot . kr^T),  o_lat = softmax(s) c.
-    Used by the self-checks; the parity references use decode_explicit.
+    with_magnitude also returns sum_t p_t |c_t|, the scale against which a
+    relative perturbation of the weights p moves o_lat (used to state
+    tolerances; it is not part of the method).
     """
     c = np.asarray(c, F64)
     kr = np.asarray(kr, F64)
     s = scale * (np.asarray(q_lat, F64) @ c.T + np.asarray(q_rot, F64) @ kr.T)
     p, lse = softmax_lse(s)
-    o_lat = p @ c if c.shape[0] else np.zeros((s.shape[0], c.shape[1]))
+    empty = np.zeros((s.shape[0], c.shape[1]))
+    o_lat = p @ c if c.shape[0] else empty
+    if with_magnitude:
+        return o_lat, lse, (p @ np.abs(c) if c.shape[0] else empty)
     return o_lat, lse
 
 
@@ -287,11 +292,12 @@ def rows_to_latent_rope(rows, kv_fp8=False, d_c=512):
 # --------------------------------------------------------------------------
 
 
-def reference_decode(inp, b, heads=None):
+def reference_decode(inp, b, heads=None, with_magnitude=False):
     """Decode-only reference for sequence b: the stored cache and query as given.
 
     Q = inp["q_decode"] [B,H,576] (latent query | rotated query), all S_b rows of
-    inp["cache_full"] attended.  Returns (o_lat [h,512], lse [h]).
+    inp["cache_full"] attended.  Returns (o_lat [h,512], lse [h]) and, with
+    with_magnitude, sum_t p_t |c_t| as a third item.
     """
     S = int(inp["seq_lens"][b])
     fp8 = inp["kv_dtype"] == 1
@@ -299,7 +305,7 @@ def reference_decode(inp, b, heads=None):
     c, kr = rows_to_latent_rope(rows, fp8)
     q = bf16_to_f64(inp["q_decode"][b])
     heads = list(range(q.shape[0])) if heads is None else list(heads)
-    return decode_absorbed(q[heads, :512], q[heads, 512:], c, kr, inp["scale"])
+    return decode_absorbed(q[heads, :512], q[heads, 512:], c, kr, inp["scale"], with_magnitude)
 
 
 def reference_step(inp, b, heads=None):

@@ -292,4 +292,20 @@ def workload(cfg: int, seed: int | None = None):
     raise ValueError(f"unknown workload {cfg}")
 
 
+def random_bf16(seed, shape, std=1.0):
+    """Plain N(0, std^2) draw rounded to bf16 bits (stand-alone operands for single-kernel tests)."""
+    return f32_to_bf16_bits(_normal(np.random.default_rng(seed), shape, std))
+
+
+def permute_pages(inp, seed):
+    """Same logical cache, different physical placement: returns (pool, block_table) for key
+    'cache_full' with every page moved to a new random id (plus the unchanged contents)."""
+    rng = np.random.default_rng(seed)
+    pool = inp["cache_full"]
+    perm = rng.permutation(pool.shape[0])
+    new_pool = np.empty_like(pool)
+    new_pool[perm] = pool
+    return new_pool, perm[inp["block_table"]].astype(np.int32)
+
+
 SPLIT_TOKENS = {3: 256}

@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+entry point, reports status strings, sizes workspaces and rejects invalid
+arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_32_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(mla.library_path()),
+                               reason="libmla.so not built (run __graft_entry__.build())")
+
+FAKE = 0x10000          # aligned, never dereferenced: every call below fails validation first
+NULL = None
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*\s*|int\s+|size_t\s+)(mla_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_calls():
+    syms = declared_symbols()
+    for name in ["mla_absorb_q", "mla_rope_append_cache", "mla_decode_paged", "mla_absorb_out"]:
+        assert name in syms
+    assert "mla_decode_workspace_bytes" in syms and "mla_status_string" in syms
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(mla.library_path())
+    for name in declared_symbols():
+        assert hasattr(L, name), f"{name} declared in mla.h but not exported"
+
+
+@needs_lib
+def test_abi_version_and_status_strings():
+    L = mla.lib()
+    assert L.mla_abi_version() == 1
+    assert L.mla_status_string(0) == b"ok"
+    assert L.mla_status_string(-1) == b"invalid argument"
+    assert L.mla_status_string(-2) == b"unsupported size or format"
+    assert L.mla_status_string(-3) == b"workspace too small"
+    assert L.mla_status_string(-4) == b"kernel launch failed"
+    assert L.mla_status_string(7) == b"unknown status"
+
+
+@needs_lib
+def test_workspace_sizing():
+    L = mla.lib()
+    # one chunk per sequence: room for one partial per (b, h)
+    rows1 = 32 * 128
+    assert L.mla_decode_workspace_bytes(32, 128, 4096, 4096) == \
+        ((rows1 * 512 * 4 + 255) // 256) * 256 + ((rows1 * 4 + 255) // 256) * 256
+    assert L.mla_decode_workspace_bytes(32, 128, 0, 0) == 0
+    # 256-token chunks over 4096 tokens: 16 partial (o, lse) rows per (b, h)
+    rows = 32 * 16 * 128
+    want = ((rows * 512 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    assert L.mla_decode_workspace_bytes(32, 128, 4096, 256) == want
+    # invalid sizes report 0
+    assert L.mla_decode_workspace_bytes(0, 128, 4096, 0) == 0
+    assert L.mla_decode_workspace_bytes(32, 128, 4096, 100) == 0
+    # the planner picks a multiple of 64 no smaller than 256 (or the whole sequence)
+    for B, H, S in [(32, 128, 4096), (4, 128, 32768), (8, 16, 1024), (128, 128, 8192), (1, 1, 1)]:
+        sp = L.mla_decode_split_tokens(B, H, S)
+        assert sp % 64 == 0 and sp >= min(256, ((S + 63) // 64) * 64)
+
+
+@needs_lib
+def test_validation_rejects_before_launch():
+    L = mla.lib()
+    # absorb_q: null pointer, misaligned pointer, unsupported widths
+    assert L.mla_absorb_q(NULL, FAKE, FAKE, 1, 1, 128, 512, 64, NULL) == -1
+    assert L.mla_absorb_q(FAKE + 2, FAKE, FAKE, 1, 1, 128, 512, 64, NULL) == -1
+    assert L.mla_absorb_q(FAKE, FAKE, FAKE, 0, 1, 128, 512, 64, NULL) == -1
+    assert L.mla_absorb_q(FAKE, FAKE, FAKE, 1, 1, 64, 512, 64, NULL) == -2
+    assert L.mla_absorb_q(FAKE, FAKE, FAKE, 1, 1, 128, 256, 64, NULL) == -2
+    # absorb_out
+    assert L.mla_absorb_out(FAKE, NULL, FAKE, 1, 1, 512, 128, NULL) == -1
+    assert L.mla_absorb_out(FAKE, FAKE, FAKE, 1, 1, 512, 64, NULL) == -2
+    # rope/append: bad theta, bad dtype, unsupported block size
+    args = [FAKE, FAKE, FAKE, FAKE, 4, FAKE]
+    assert L.mla_rope_append_cache(*args, 0, 8, 64, ctypes.c_float(0.0), FAKE, 1, 1, 512, 64, NULL) == -1
+    assert L.mla_rope_append_cache(*args, 5, 8, 64, ctypes.c_float(1e4), FAKE, 1, 1, 512, 64, NULL) == -1
+    assert L.mla_rope_append_cache(*args, 0, 8, 32, ctypes.c_float(1e4), FAKE, 1, 1, 512, 64, NULL) == -2
+    # decode: bad split, block size, max_seq_len beyond capacity, workspace too small
+    dec = L.mla_decode_paged
+
+    def call(split=0, ws=NULL, ws_bytes=0, max_seq=256, mbps=4, block=64, kv=0, lse=NULL, scale=0.07):
+        return dec(FAKE, FAKE, kv, FAKE, mbps, FAKE, max_seq, 16, block, ctypes.c_float(scale), split,
+                   ws, ws_bytes, FAKE, lse, 2, 128, NULL)
+    assert call(split=100) == -1
+    assert call(split=-64) == -1
+    assert call(block=32) == -2
+    assert call(max_seq=257) == -1
+    assert call(kv=3) == -1
+    assert call(lse=FAKE + 4) == -1
+    assert call(scale=float("inf")) == -1
+    assert call(split=64, ws=NULL) == -3
+    assert call(split=64, ws=FAKE, ws_bytes=1024) == -3
+    assert call(split=262144, max_seq=256) == -2
+    # partial/combine
+    part = L.mla_decode_partial
+    assert part(FAKE, FAKE, 0, FAKE, 4, FAKE, 0, 16, 64, ctypes.c_float(0.07), 64, FAKE, 1 << 20, 2, 128,
+                NULL) == -1   # max_seq_len 0
+    assert part(FAKE, FAKE, 0, FAKE, 4, FAKE, 256, 16, 64, ctypes.c_float(0.07), 64, FAKE, 1024, 2, 128,
+                NULL) == -3
+    comb = L.mla_decode_combine
+    assert comb(NULL, 0, FAKE, 256, 64, FAKE, NULL, 2, 128, NULL) == -1
+    assert comb(FAKE, 16, FAKE, 256, 64, FAKE, NULL, 2, 128, NULL) == -3
+    assert comb(FAKE, 1 << 30, FAKE, 256, 96, FAKE, NULL, 2, 128, NULL) == -1
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mla, "_LIB", None)
+    monkeypatch.setenv("MLA_LIBRARY", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        mla.lib()

@@ -152,6 +152,16 @@ def test_rotary_part_is_not_dropped():
     np.testing.assert_allclose(o_lat[0], c[5], atol=1e-30 + 1e-40)
 
 
+def test_weighted_magnitude_bounds_output():
+    rng = np.random.default_rng(21)
+    c, kr = rng.standard_normal((40, 12)), rng.standard_normal((40, 4))
+    q_lat, q_rot = rng.standard_normal((3, 12)), rng.standard_normal((3, 4))
+    o, _, mag = oracle.decode_absorbed(q_lat, q_rot, c, kr, 0.3, with_magnitude=True)
+    assert (np.abs(o) <= mag + 1e-15).all()
+    o2, _, mag2 = oracle.decode_absorbed(q_lat, q_rot, np.abs(c), kr, 0.3, with_magnitude=True)
+    np.testing.assert_allclose(o2, mag2, rtol=1e-14)
+
+
 # ----------------------------------------------------------- softmax (PIN-4)
 def test_softmax_rows_sum_to_one():
     s = _rand(7, 300) * 20
