@@ -35,7 +35,6 @@ constexpr int ROPE_BYTES = DR * 2;              // 128: rotary part of a row
 constexpr int SLOT_LAT = TB * LAT_BYTES;        // 32768
 constexpr int SLOT_BYTES = SLOT_LAT + TB * ROPE_BYTES;   // 36864
 constexpr int NDMA = TB + TB * ROPE_BYTES / 1024;        // 36 wave-wide copies per block
-constexpr int HPW = 16;                         // heads per wave (MFMA N)
 constexpr int KSTEPS = DROW / 32;               // 18 MFMA k-steps over 576
 constexpr int KLAT = DC / 32;                   // 16 of them over the latent
 constexpr int CBLKS = DC / 16;                  // 32 column blocks of O
@@ -52,74 +51,54 @@ constexpr int MAX_SPLIT_PAGES = MLA_MAX_SPLIT_TOKENS / PAGE;
 // (the transposed value reads) each touch distinct banks.
 __device__ __forceinline__ int fl(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
+// 8-dim group of a 32-dim k-step that the 16-lane group g of a wave reads in
+// the score product.  With lane groups 1 and 2 exchanged, the 16 lanes the LDS
+// serves together in a 128-bit read hit 16 distinct bank quads (measured on
+// gfx950: the identity order costs a 2-way conflict on every score read).
+__device__ __forceinline__ int kgroup(int g) { return ((g & 1) << 1) | (g >> 1); }
+
+// Pairwise reductions across lanes l ^ 16 and l ^ 32 with the gfx950 lane
+// swaps (VALU; no LDS traffic).  Both lanes of a pair get the same result.
+#ifdef MLA_REDUCE_WITH_SHFL
+__device__ __forceinline__ float max_xor16(float v) { return fmaxf(v, __shfl_xor(v, 16)); }
+__device__ __forceinline__ float max_xor32(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+__device__ __forceinline__ float sum_xor16(float v) { return v + __shfl_xor(v, 16); }
+__device__ __forceinline__ float sum_xor32(float v) { return v + __shfl_xor(v, 32); }
+#else
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+#endif
+
+// The copy (DMA) side of a decoder: which rows of a block each wave moves.
 template <int NW>
-struct Decoder {
+struct BlockCopier {
   static constexpr int NI = (NDMA + NW - 1) / NW;       // max DMA copies per wave per block
   static_assert(3 * NI <= 63, "three blocks of copies must fit the vmcnt counter");
 
-  const DecodeArgs &a;
-  const int lane, wave, g, r16;
-  const int b, split, head;
-  const bool head_ok;
-  const int t_begin, t_end;
-  const int32_t *pages;       // LDS copy of the chunk's page ids
-
-  bf16x8 qf[KSTEPS];
-  f32x4 o[CBLKS];
-  // m_run: running max (log2 units); l_run: sum of the bf16-rounded weights
-  // that multiply V (normalises o consistently); e_run: the same sum of the
-  // unrounded weights (gives an lse free of the bf16 rounding of P).
-  float m_run, l_run, e_run;
-  // per-lane LDS byte offsets; every LDS read is one of these plus a constant
-  int k_off[4];               // latent score reads, ks & 3
-  int kr_off[2];              // rotary score reads, ks - 16
-  int v_off[8];               // transposed value reads, cb & 7
-
-  __device__ Decoder(const DecodeArgs &args, const int32_t *pages_, int b_, int split_, int t0, int t1)
-      : a(args), lane(threadIdx.x & 63), wave(threadIdx.x >> 6), g((threadIdx.x & 63) >> 4),
-        r16(threadIdx.x & 15), b(b_), split(split_),
-        head((blockIdx.y * NW + (threadIdx.x >> 6)) * HPW + (threadIdx.x & 15)),
-        head_ok(((blockIdx.y * NW + (threadIdx.x >> 6)) * HPW + (threadIdx.x & 15)) < args.H),
-        t_begin(t0), t_end(t1), pages(pages_) {}
-
-  __device__ __forceinline__ void init_offsets() {
-    // score reads: row r16 (+16), latent chunk 4 ks + g = 16 (ks >> 2) + (4 (ks & 3) + g)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) k_off[e] = r16 * LAT_BYTES + (((4 * e + g) ^ fl(r16)) << 4);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) kr_off[e] = SLOT_LAT + r16 * ROPE_BYTES + (((4 * e + g) ^ (r16 & 7)) << 4);
-    // value reads: row trow (+16), latent chunk 2 cb + csub = 16 (cb >> 3) + (2 (cb & 7) + csub),
-    // byte (r16 & 1) * 8 inside the chunk
-    const int trow = g * 4 + (r16 >> 2);
-    const int csub = (r16 & 3) >> 1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      v_off[e] = trow * LAT_BYTES + (((2 * e + csub) ^ fl(trow)) << 4) + (r16 & 1) * 8;
-  }
-
-  // Query fragments (MFMA B operand): lane (head, g) holds dims [32 ks + 8 g, +8).
-  __device__ __forceinline__ void load_q() {
-    const uint16_t *qp = a.q + (static_cast<size_t>(b) * a.H + (head_ok ? head : 0)) * DROW + g * 8;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4 v = *reinterpret_cast<const u32x4 *>(qp + ks * 32);
-      if (!head_ok) v = u32x4{0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
   // Copies this wave issues per block: copies n = wave, wave + NW, ... < 36.
-  __device__ __forceinline__ int copies() const { return (NDMA - wave + NW - 1) / NW; }
+  __device__ __forceinline__ static int copies(int wave) { return (NDMA - wave + NW - 1) / NW; }
 
-  // Start the DMA of token block `blk` into `slot`.  Copy n < 32 moves latent
-  // row n (one 1 KB row per wave-wide instruction); copies 32..35 move the
-  // rotary keys of 8 rows each.  Rows past the end of the chunk re-read the
-  // last valid row (finite data); their scores are masked.
-  __device__ __forceinline__ void issue(int blk, uint8_t *slot) {
-    const int tok0 = t_begin + blk * TB;
-    const int phys = __builtin_amdgcn_readfirstlane(pages[(tok0 - t_begin) >> 6]);
-    const uint8_t *base = a.cache + (static_cast<size_t>(phys) * PAGE + (tok0 & 32)) * ROW_BYTES;
-    const int last = min(TB, t_end - tok0) - 1;
+  // Start the DMA of the 32-token block starting at tok0 into `slot`.  Copy
+  // n < 32 moves latent row n (one 1 KB row per wave-wide instruction);
+  // copies 32..35 move the rotary keys of 8 rows each.  Rows past `last`
+  // re-read row `last` (finite data); their scores are masked.
+  __device__ __forceinline__ static void issue(const uint8_t *cache, int phys, int tok0, int last,
+                                               int wave, int lane, uint8_t *slot) {
+    const uint8_t *base = cache + (static_cast<size_t>(phys) * PAGE + (tok0 & 32)) * ROW_BYTES;
     const uint32_t slot_lds = lds_addr(slot);
     // Opaque copy of the lane id: keeps the compiler from hoisting the
     // per-copy address arithmetic out of the streaming loop into registers.
@@ -142,6 +121,81 @@ struct Decoder {
       }
     }
   }
+};
+
+// 16 heads per wave: v_mfma_f32_16x16x32_bf16, two waves per SIMD.
+template <int NW_>
+struct DecoderW16 {
+  static constexpr int NW = NW_;
+  static constexpr int HPW = 16;
+  static constexpr int NI = BlockCopier<NW>::NI;
+
+  const DecodeArgs &a;
+  const int lane, wave, g, r16;
+  const int b, split, head;
+  const bool head_ok;
+  const int t_begin, t_end;
+  const int32_t *pages;       // LDS copy of the chunk's page ids
+
+  bf16x8 qf[KSTEPS];
+  f32x4 o[CBLKS];
+  // m_run: running max (log2 units); l_run: sum of the bf16-rounded weights
+  // that multiply V (normalises o consistently); e_run: the same sum of the
+  // unrounded weights (gives an lse free of the bf16 rounding of P).
+  float m_run, l_run, e_run;
+  // per-lane LDS byte offsets; every LDS read is one of these plus a constant
+  int k_off[4];               // latent score reads, ks & 3
+  int kr_off[2];              // rotary score reads, ks - 16
+  int v_off[8];               // transposed value reads, cb & 7
+
+  __device__ DecoderW16(const DecodeArgs &args, const int32_t *pages_, int b_, int split_, int t0, int t1)
+      : a(args), lane(threadIdx.x & 63), wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)),
+        g((threadIdx.x & 63) >> 4),
+        r16(threadIdx.x & 15), b(b_), split(split_),
+        head((blockIdx.y * NW + (threadIdx.x >> 6)) * HPW + (threadIdx.x & 15)),
+        head_ok(((blockIdx.y * NW + (threadIdx.x >> 6)) * HPW + (threadIdx.x & 15)) < args.H),
+        t_begin(t0), t_end(t1), pages(pages_) {}
+
+  __device__ __forceinline__ void begin() {
+    m_run = -INFINITY;
+    l_run = 0.f;
+    e_run = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CBLKS; ++cb) o[cb] = f32x4{};
+    // score reads: row r16 (+16), latent chunk 4 ks + kg = 16 (ks >> 2) + (4 (ks & 3) + kg)
+    const int kg = kgroup(g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k_off[e] = r16 * LAT_BYTES + (((4 * e + kg) ^ fl(r16)) << 4);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) kr_off[e] = SLOT_LAT + r16 * ROPE_BYTES + (((4 * e + kg) ^ (r16 & 7)) << 4);
+    // value reads: row trow (+16), latent chunk 2 cb + csub = 16 (cb >> 3) + (2 (cb & 7) + csub),
+    // byte (r16 & 1) * 8 inside the chunk
+    const int trow = g * 4 + (r16 >> 2);
+    const int csub = (r16 & 3) >> 1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v_off[e] = trow * LAT_BYTES + (((2 * e + csub) ^ fl(trow)) << 4) + (r16 & 1) * 8;
+  }
+
+  // Query fragments (MFMA B operand): lane (head, g) holds dims [32 ks + 8 kgroup(g), +8),
+  // the same 8-dim group its score reads fetch from the cached rows.
+  __device__ __forceinline__ void load_q() {
+    const uint16_t *qp = a.q + (static_cast<size_t>(b) * a.H + (head_ok ? head : 0)) * DROW + kgroup(g) * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4 v = *reinterpret_cast<const u32x4 *>(qp + ks * 32);
+      if (!head_ok) v = u32x4{0, 0, 0, 0};
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  __device__ __forceinline__ int copies() const { return BlockCopier<NW>::copies(wave); }
+
+  __device__ __forceinline__ void issue(int blk, uint8_t *slot) {
+    const int tok0 = t_begin + blk * TB;
+    const int phys = __builtin_amdgcn_readfirstlane(pages[(tok0 - t_begin) >> 6]);
+    BlockCopier<NW>::issue(a.cache, phys, tok0, min(TB, t_end - tok0) - 1, wave, lane, slot);
+  }
 
   __device__ __forceinline__ void compute(const uint8_t *slot, int blk) {
     const int tok0 = t_begin + blk * TB;
@@ -160,20 +214,19 @@ struct Decoder {
 
     // ---- online softmax: lane holds head r16 for tokens 4g+i and 16+4g+i
     float xs[8];
-    float mx = -INFINITY;
-    const bool ragged = tok0 + TB > t_end;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float v = (i < 4 ? s0[i] : s1[i - 4]) * a.scale_log2;
-      if (ragged) {
-        const int t = tok0 + (i >> 2) * 16 + g * 4 + (i & 3);
-        if (t >= t_end) v = -INFINITY;
-      }
-      xs[i] = v;
-      mx = fmaxf(mx, v);
+    for (int i = 0; i < 8; ++i) xs[i] = (i < 4 ? s0[i] : s1[i - 4]) * a.scale_log2;
+    if (tok0 + TB > t_end) [[unlikely]] {
+      // last block of the chunk: tokens at or past t_end do not exist
+      const int lim = t_end - tok0 - g * 4;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if ((i >> 2) * 16 + (i & 3) >= lim) xs[i] = -INFINITY;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float mx = xs[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, xs[i]);
+    mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m_run, mx);
     if (__ballot(m_new > m_run + RESCALE_SLACK)) {
       const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -214,10 +267,8 @@ struct Decoder {
 
   // lane (head r16, g) holds columns 16 cb + 4 g + [0,4) of its head.
   __device__ __forceinline__ void finish() {
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    float e_tot = e_run + __shfl_xor(e_run, 16);
-    e_tot += __shfl_xor(e_tot, 32);
+    const float l_tot = sum_xor32(sum_xor16(l_run));
+    const float e_tot = sum_xor32(sum_xor16(e_run));
     const float inv = 1.0f / l_tot;
     const float lse_v = (m_run + __log2f(e_tot)) * LN2;
     if (!head_ok) return;
@@ -243,9 +294,8 @@ struct Decoder {
 
 // Wait until this wave's copies of block i have landed (copies of the next
 // `ahead` blocks may still be in flight), then synchronise the workgroup.
-template <int NW, int AHEAD>
+template <int NI, int AHEAD>
 __device__ __forceinline__ void wait_block(bool full_share) {
-  constexpr int NI = (NDMA + NW - 1) / NW;
   if (full_share) wait_vmcnt<AHEAD * NI>();
   else wait_vmcnt<AHEAD * (NI - 1)>();
 }
@@ -254,23 +304,24 @@ __device__ __forceinline__ void wait_block(bool full_share) {
   {                                                                    \
     const int i = blk + (K);                                           \
     if (i >= nblk) break;                                              \
-    if (i + 2 < nblk) wait_block<NW, 2>(full_share);                   \
-    else if (i + 1 < nblk) wait_block<NW, 1>(full_share);              \
+    if (i + 2 < nblk) wait_block<D::NI, 2>(full_share);                \
+    else if (i + 1 < nblk) wait_block<D::NI, 1>(full_share);           \
     else wait_vmcnt<0>();                                              \
     barrier_no_fence();                                                \
     if (i + 3 < nblk) dec.issue(i + 3, NXT);                           \
     dec.compute(CUR, i);                                               \
   }
 
-template <int NW>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+template <class D, int WAVES_PER_EU>
+__global__ __attribute__((amdgpu_flat_work_group_size(D::NW * 64, D::NW * 64),
+                          amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void decode_bf16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t slot0[SLOT_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slot1[SLOT_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slot2[SLOT_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slot3[SLOT_BYTES];
   __shared__ int32_t pages[MAX_SPLIT_PAGES];
-  using D = Decoder<NW>;
+  constexpr int NW = D::NW;
 
   const int item = blockIdx.x;
   const int b = item / a.n_splits;
@@ -284,12 +335,14 @@ void decode_bf16_kernel(DecodeArgs a) {
     // (empty sequence: zeros and lse = -inf); split chunks past the end of a
     // sequence are skipped by the combine kernel.
     if (a.direct) {
-      const int lane = threadIdx.x & 63;
-      const int head = (blockIdx.y * NW + (threadIdx.x >> 6)) * HPW + (lane & 15);
+      const int t = threadIdx.x;
+      const int per = NW * 64 / (D::HPW * NW);            // threads per head
+      const int head = blockIdx.y * D::HPW * NW + t / per;
       if (head < a.H) {
-        uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + (lane >> 4) * 128;
-        for (int c = 0; c < 128; c += 8) *reinterpret_cast<u32x4 *>(dst + c) = u32x4{0, 0, 0, 0};
-        if ((lane >> 4) == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = -INFINITY;
+        const int cols = DC / per;
+        uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + (t % per) * cols;
+        for (int c = 0; c < cols; c += 8) *reinterpret_cast<u32x4 *>(dst + c) = u32x4{0, 0, 0, 0};
+        if (t % per == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = -INFINITY;
       }
     }
     return;
@@ -305,12 +358,7 @@ void decode_bf16_kernel(DecodeArgs a) {
   __syncthreads();
 
   D dec(a, pages, b, split, t_begin, t_end);
-  dec.m_run = -INFINITY;
-  dec.l_run = 0.f;
-  dec.e_run = 0.f;
-  dec.init_offsets();
-#pragma unroll
-  for (int cb = 0; cb < CBLKS; ++cb) dec.o[cb] = f32x4{};
+  dec.begin();
   dec.load_q();
   wait_vmcnt<0>();            // query fragments landed before any copy is queued
   const bool full_share = dec.copies() == D::NI;
@@ -376,12 +424,13 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int nw = decode_waves(a.H);
-  const int groups = (a.H + HPW * nw - 1) / (HPW * nw);
+  const int hpw = decode_heads_per_wave(a.H);
+  const int groups = (a.H + hpw * nw - 1) / (hpw * nw);
   dim3 grid(a.B * a.n_splits, groups);
   switch (nw) {
-    case 2: decode_bf16_kernel<2><<<grid, 128, 0, stream>>>(a); break;
-    case 4: decode_bf16_kernel<4><<<grid, 256, 0, stream>>>(a); break;
-    default: decode_bf16_kernel<8><<<grid, 512, 0, stream>>>(a); break;
+    case 2: decode_bf16_kernel<DecoderW16<2>, 1><<<grid, 128, 0, stream>>>(a); break;
+    case 4: decode_bf16_kernel<DecoderW16<4>, 1><<<grid, 256, 0, stream>>>(a); break;
+    default: decode_bf16_kernel<DecoderW16<8>, 2><<<grid, 512, 0, stream>>>(a); break;
   }
   return hipGetLastError();
 }

@@ -31,11 +31,16 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // Log-sum-exp merge of the partials into o_latent/lse.
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);
 
-// Waves per decode workgroup (16 heads each) and heads per workgroup.  At
-// least two waves share a block's copies so that three blocks in flight stay
-// within the 6-bit vector-memory counter (3 x 18 copies per wave).
+// Decode workgroup shape: 16 heads per wave (MFMA 16x16x32) and 2, 4 or 8
+// waves per workgroup.  At least two waves share a block's copies so that
+// three blocks in flight stay within the 6-bit vector-memory counter
+// (3 x 18 copies per wave).
+inline int decode_heads_per_wave(int) { return 16; }
 inline int decode_waves(int H) { return H <= 32 ? 2 : (H <= 64 ? 4 : 8); }
-inline int decode_head_groups(int H) { return (H + 16 * decode_waves(H) - 1) / (16 * decode_waves(H)); }
+inline int decode_head_groups(int H) {
+  const int per = decode_heads_per_wave(H) * decode_waves(H);
+  return (H + per - 1) / per;
+}
 
 // q[b,h,0:512] = q_nope[b,h,:] . W_UK[h]
 hipError_t launch_absorb_q(const uint16_t *q_nope, const uint16_t *w_uk, uint16_t *q, int B, int H,
