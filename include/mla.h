@@ -121,7 +121,7 @@ int mla_rope_append_cache(const void *q_pe, const void *kv_new, const int32_t *s
 
 /*
  * Bytes of the split-KV workspace for these sizes: partial outputs
- * o_part[B][n_chunks][H][512] fp32 followed (at the next 256-byte boundary)
+ * o_part[B][n_chunks][H][512] bf16 followed (at the next 256-byte boundary)
  * by lse_part[B][n_chunks][H] fp32, n_chunks = ceil(max_seq_len / split).
  * split_tokens as passed to the decode calls (0 = library choice).
  * mla_decode_paged needs the workspace only when n_chunks > 1.
@@ -172,8 +172,8 @@ int mla_decode_paged(const void *q, const void *kv_cache, int kv_dtype,
  *
  * mla_decode_partial: attention of every head over each chunk of split_tokens
  * tokens; writes o_part = (sum_t e^{s_t - m} row_t[0:512]) / (sum_t e^{s_t - m})
- * and lse_part = m + log sum_t e^{s_t - m} (natural log) into the workspace
- * layout above.  Chunks that start at or beyond seq_lens[b] are not written.
+ * rounded to bf16 and lse_part = m + log sum_t e^{s_t - m} (natural log, fp32)
+ * into the workspace layout above.  Chunks that start at or beyond seq_lens[b] are not written.
  * Arguments as for mla_decode_paged.
  *
  * mla_decode_combine: o_latent[b,h] = sum_c w_c o_part[b,c,h] / sum_c w_c with

@@ -45,7 +45,7 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 size_t workspace_for(int B, int H, int n_splits) {
   const size_t rows = static_cast<size_t>(B) * n_splits * H;
-  return align256(rows * MLA_D_C * sizeof(float)) + align256(rows * sizeof(float));
+  return align256(rows * MLA_D_C * sizeof(uint16_t)) + align256(rows * sizeof(float));
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
@@ -161,9 +161,9 @@ int prepare_decode(DecodeMode mode, const void *q, const void *kv_cache, int kv_
   a->o_latent = static_cast<uint16_t *>(o_latent);
   a->lse = lse;
   const size_t rows = static_cast<size_t>(B) * n_splits * H;
-  a->o_part = need ? static_cast<float *>(workspace) : nullptr;
+  a->o_part = need ? static_cast<uint16_t *>(workspace) : nullptr;
   a->lse_part = need ? reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
-                                                 align256(rows * MLA_D_C * sizeof(float)))
+                                                 align256(rows * MLA_D_C * sizeof(uint16_t)))
                      : nullptr;
   return MLA_OK;
 }
@@ -220,9 +220,9 @@ int mla_decode_combine(const void *workspace, size_t workspace_bytes, const int3
   a.o_latent = static_cast<uint16_t *>(o_latent);
   a.lse = lse;
   const size_t rows = static_cast<size_t>(B) * n_splits * H;
-  a.o_part = static_cast<float *>(const_cast<void *>(workspace));
+  a.o_part = static_cast<uint16_t *>(const_cast<void *>(workspace));
   a.lse_part = reinterpret_cast<float *>(static_cast<uint8_t *>(const_cast<void *>(workspace)) +
-                                         align256(rows * MLA_D_C * sizeof(float)));
+                                         align256(rows * MLA_D_C * sizeof(uint16_t)));
   return status_of(mla::launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -20,8 +20,8 @@
 // second copy of V exists anywhere.
 //
 // Split-KV: a sequence may be cut into chunks of split_tokens; each chunk
-// writes (o / l, lse) partials in fp32 and a combine kernel merges them with
-// log-sum-exp weights.
+// writes (o / l in bf16, lse in fp32) partials and a combine kernel merges
+// them with log-sum-exp weights in fp32.
 #include "common.h"
 #include "kernels.h"
 
@@ -59,12 +59,6 @@ __device__ __forceinline__ int kgroup(int g) { return ((g & 1) << 1) | (g >> 1);
 
 // Pairwise reductions across lanes l ^ 16 and l ^ 32 with the gfx950 lane
 // swaps (VALU; no LDS traffic).  Both lanes of a pair get the same result.
-#ifdef MLA_REDUCE_WITH_SHFL
-__device__ __forceinline__ float max_xor16(float v) { return fmaxf(v, __shfl_xor(v, 16)); }
-__device__ __forceinline__ float max_xor32(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
-__device__ __forceinline__ float sum_xor16(float v) { return v + __shfl_xor(v, 16); }
-__device__ __forceinline__ float sum_xor32(float v) { return v + __shfl_xor(v, 32); }
-#else
 __device__ __forceinline__ float max_xor16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -81,7 +75,6 @@ __device__ __forceinline__ float sum_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-#endif
 
 // The copy (DMA) side of a decoder: which rows of a block each wave moves.
 template <int NW>
@@ -284,9 +277,14 @@ struct DecoderW16 {
       if (g == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = lse_v;
     } else {
       const size_t row = (static_cast<size_t>(b) * a.n_splits + split) * a.H + head;
-      float *dst = a.o_part + row * DC + g * 4;
+      uint16_t *dst = a.o_part + row * DC + g * 4;
 #pragma unroll
-      for (int cb = 0; cb < CBLKS; ++cb) *reinterpret_cast<f32x4 *>(dst + cb * 16) = o[cb] * inv;
+      for (int cb = 0; cb < CBLKS; ++cb) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[cb][e] * inv);
+        *reinterpret_cast<bf16x4 *>(dst + cb * 16) = v;
+      }
       if (g == 0) a.lse_part[row] = lse_v;
     }
   }
@@ -398,24 +396,23 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const float *lp = a.lse_part + static_cast<size_t>(b) * a.n_splits * stride + head;
   float L = -INFINITY;
   for (int c = 0; c < nv; ++c) L = fmaxf(L, lp[c * stride]);
-  f32x4 acc0 = {}, acc1 = {};
+  float acc[8] = {};
   float z = 0.f;
-  const float *op = a.o_part + (static_cast<size_t>(b) * a.n_splits * stride + head) * DC + t * 8;
+  const uint16_t *op = a.o_part + (static_cast<size_t>(b) * a.n_splits * stride + head) * DC + t * 8;
   for (int c = 0; c < nv; ++c) {
     const float w = expf(lp[c * stride] - L);
     z += w;
-    const f32x4 v0 = *reinterpret_cast<const f32x4 *>(op + c * stride * DC);
-    const f32x4 v1 = *reinterpret_cast<const f32x4 *>(op + c * stride * DC + 4);
-    acc0 += w * v0;
-    acc1 += w * v1;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(op + c * stride * DC);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += w * __uint_as_float(v[e] << 16);
+      acc[2 * e + 1] += w * __uint_as_float(v[e] & 0xFFFF0000u);
+    }
   }
   const float inv = 1.0f / z;
   bf16x8 out;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    out[e] = to_bf16(acc0[e] * inv);
-    out[4 + e] = to_bf16(acc1[e] * inv);
-  }
+  for (int e = 0; e < 8; ++e) out[e] = to_bf16(acc[e] * inv);
   *reinterpret_cast<bf16x8 *>(dst) = out;
   if (t == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = L + logf(z);
 }

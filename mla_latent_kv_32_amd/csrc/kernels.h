@@ -22,7 +22,7 @@ struct DecodeArgs {
   float scale_log2;             // softmax_scale * log2(e)
   uint16_t *o_latent;           // [B, H, 512] bf16
   float *lse;                   // [B, H] or null
-  float *o_part;                // [B, n_splits, H, 512] fp32 (n_splits > 1)
+  uint16_t *o_part;             // [B, n_splits, H, 512] bf16 partial outputs
   float *lse_part;              // [B, n_splits, H] fp32
 };
 

@@ -40,6 +40,10 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float x) {
   return code == 0u ? 0u : (code | sign);
 }
 
+// grid (B, ceil(H / 16)): each workgroup rotates the query pairs of 16 heads
+// of one sequence (2 pairs per thread); workgroup (b, 0) also appends the row.
+constexpr int HEADS_PER_WG = 16;
+
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
   __shared__ float cs[DR / 2], sn[DR / 2];
   const int b = blockIdx.x;
@@ -55,8 +59,10 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
   }
   __syncthreads();
 
-  for (int idx = tid; idx < a.H * (DR / 2); idx += blockDim.x) {
-    const int h = idx / (DR / 2), i = idx % (DR / 2);
+  const int h0 = blockIdx.y * HEADS_PER_WG;
+  for (int idx = tid; idx < HEADS_PER_WG * (DR / 2); idx += blockDim.x) {
+    const int h = h0 + idx / (DR / 2), i = idx % (DR / 2);
+    if (h >= a.H) break;
     const size_t bh = static_cast<size_t>(b) * a.H + h;
     const uint32_t pr = *reinterpret_cast<const uint32_t *>(a.q_pe + bh * DR + 2 * i);
     const float x1 = bf16_to_f32(pr & 0xFFFFu), x2 = bf16_to_f32(pr >> 16);
@@ -65,6 +71,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
     *reinterpret_cast<uint32_t *>(a.q + bh * DROW + DC + 2 * i) =
         static_cast<uint32_t>(bf16_bits(to_bf16(y1))) | (static_cast<uint32_t>(bf16_bits(to_bf16(y2))) << 16);
   }
+  if (blockIdx.y != 0) return;
   if (S <= 0) return;
 
   const int page = a.block_table[static_cast<size_t>(b) * a.max_blocks + (pos / PAGE)];
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
 }  // namespace
 
 hipError_t launch_rope_append(const RopeAppendArgs &a, hipStream_t stream) {
-  rope_append_kernel<<<a.B, 256, 0, stream>>>(a);
+  rope_append_kernel<<<dim3(a.B, (a.H + HEADS_PER_WG - 1) / HEADS_PER_WG), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -56,11 +56,11 @@ def test_workspace_sizing():
     # one chunk per sequence: room for one partial per (b, h)
     rows1 = 32 * 128
     assert L.mla_decode_workspace_bytes(32, 128, 4096, 4096) == \
-        ((rows1 * 512 * 4 + 255) // 256) * 256 + ((rows1 * 4 + 255) // 256) * 256
+        ((rows1 * 512 * 2 + 255) // 256) * 256 + ((rows1 * 4 + 255) // 256) * 256
     assert L.mla_decode_workspace_bytes(32, 128, 0, 0) == 0
     # 256-token chunks over 4096 tokens: 16 partial (o, lse) rows per (b, h)
     rows = 32 * 16 * 128
-    want = ((rows * 512 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    want = ((rows * 512 * 2 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
     assert L.mla_decode_workspace_bytes(32, 128, 4096, 256) == want
     # invalid sizes report 0
     assert L.mla_decode_workspace_bytes(0, 128, 4096, 0) == 0

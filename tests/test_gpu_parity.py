@@ -244,8 +244,8 @@ def test_decode_partial_then_combine_equals_paged():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
     # the partials themselves: chunk c of sequence b against the oracle on that token range
     rows = B * ((max_len + 511) // 512) * H
-    o_part = ws[:rows * 512 * 4].view(torch.float32).view(B, -1, H, 512).cpu().numpy()
-    off = ((rows * 512 * 4 + 255) // 256) * 256
+    o_part = bf(ws[:rows * 512 * 2].view(torch.bfloat16).view(B, -1, H, 512))
+    off = ((rows * 512 * 2 + 255) // 256) * 256
     lse_part = ws[off:off + rows * 4].view(torch.float32).view(B, -1, H).cpu().numpy()
     for b in [0, 3]:
         S = int(w["seq_lens"][b])
