@@ -8,6 +8,7 @@ namespace mla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -16,6 +17,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(1))) const uint8_t gbl_u8;
+// Constant address space: uniform loads through it become scalar (s_load) reads.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Fixed geometry of the latent cache row (DeepSeek-V2/V3: kv_lora_rank 512,
@@ -66,6 +69,18 @@ __device__ __forceinline__ void dma16(const void *gsrc, uint32_t lds_base) {
       : "memory", "m0");
 }
 
+// The same copy with a wave-uniform 64-bit base (SGPR pair) and a 32-bit
+// per-lane byte offset: the per-copy address arithmetic stays scalar.
+__device__ __forceinline__ void dma16_s(uint32_t voff, const void *sbase, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t *)p));
 }
@@ -76,7 +91,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // memory operations across it.
 __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier after this wave's LDS writes have completed (lgkmcnt 0),
+// so that they are visible to every wave past the barrier; outstanding
+// global->LDS copies are not waited for.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
 }
 

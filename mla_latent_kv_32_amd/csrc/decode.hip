@@ -2,26 +2,43 @@
 //
 // Every head scores the same cached row [c_KV | rotated k_R] (576 values), so
 // a workgroup streams each 32-token block of a sequence from HBM into LDS once
-// and all of its heads (up to 128, 16 per wave, 8 waves) consume it there:
-//   S^T[tok, head] = K[tok, 0:576] . Q^T[0:576, head]     MFMA 16x16x32 bf16
-//   online softmax per head (fp32, exp2, lazily rescaled)
-//   O^T[col, head] += V^T[col, tok] . P^T[tok, head]      MFMA, V = K[:, 0:512]
-// The decoding-stage MQA form of MLA (Su, "The Ultimate Tug-of-War Between
-// Cache and Performance", MLA Part 3, eq:mla-mqa); one loaded latent serves
-// every head (Riju, "Multi-Head Latent Attention vs GQA vs MQA", "Arithmetic
-// intensity changes under absorption").
+// and all of its heads (up to 128) consume it there.  The decoding-stage MQA
+// form of MLA (Su, "The Ultimate Tug-of-War Between Cache and Performance",
+// MLA Part 3, eq:mla-mqa); one loaded latent serves every head (Riju,
+// "Multi-Head Latent Attention vs GQA vs MQA", "Arithmetic intensity changes
+// under absorption").
+//
+// Work split: the waves of a workgroup form pairs; a pair owns 32 heads.
+// Both waves of a pair see every token of a block, and each takes half of the
+// contraction and half of the output:
+//   scores   S^T[tok, head] = K[tok, dims] . Q^T[dims, head]   (v_mfma_f32_32x32x16_bf16)
+//            wave h sums the 16-dim k-steps 2 ks + h, ks = 0..17 (latent and rotary)
+//   exchange each wave adds its partner's fp32 partial through LDS; both then hold
+//            the identical full scores and run the same online softmax (fp32, exp2,
+//            lazily rescaled)
+//   values   O^T[col, head] += V^T[col, tok] . P^T[tok, head], V = K[:, 0:512];
+//            wave h owns columns [256 h, 256 h + 256)
+// A 32x32x16 product reads one 1 KB operand tile per 16384 MACs, half of what a
+// 16x16x32 product needs, so the pair layout halves the LDS bytes per MFMA for
+// the same register footprint (72 query + 128 accumulator VGPRs per wave).
+//
+// Schedule: with 8 waves, waves w and w + 4 share a SIMD.  Waves 0..3 (group
+// X) and 4..7 (group Y) run half a block apart, so one group's score MFMAs
+// overlap the other group's softmax (VALU) instead of both groups idling the
+// matrix core at the same time.  Two workgroup barriers per block serve both
+// groups: for X they are "block ready" and "partials exchanged", for Y the
+// other way round.
 //
 // Data movement: 16-byte global->LDS DMA copies (global_load_lds_dwordx4),
-// one 1 KB latent row per wave-wide copy, into a ring of four 36 KB slots:
-// three blocks in flight while one is computed.  Chunks are XOR-swizzled per
-// row so that the row-wise reads of the score product and the transposed
-// reads (ds_read_b64_tr_b16) of the value product spread over the LDS banks.
-// The value operand is read transposed straight out of the same tile: no
-// second copy of V exists anywhere.
+// one 1 KB latent row per wave-wide copy, into a ring of three 36 KB slots.  Chunks are XOR-swizzled per row
+// so that the row-wise score reads (ds_read_b128) and the transposed value
+// reads (ds_read_b64_tr_b16) spread over the LDS banks; the value operand is
+// read transposed straight out of the same tile.
 //
 // Split-KV: a sequence may be cut into chunks of split_tokens; each chunk
 // writes (o / l in bf16, lse in fp32) partials and a combine kernel merges
-// them with log-sum-exp weights in fp32.
+// them with log-sum-exp weights in fp32.  Chunks of one sequence are placed on
+// one XCD so that its L2 serves the query to all of them.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,41 +52,34 @@ constexpr int ROPE_BYTES = DR * 2;              // 128: rotary part of a row
 constexpr int SLOT_LAT = TB * LAT_BYTES;        // 32768
 constexpr int SLOT_BYTES = SLOT_LAT + TB * ROPE_BYTES;   // 36864
 constexpr int NDMA = TB + TB * ROPE_BYTES / 1024;        // 36 wave-wide copies per block
-constexpr int KSTEPS = DROW / 32;               // 18 MFMA k-steps over 576
-constexpr int KLAT = DC / 32;                   // 16 of them over the latent
-constexpr int CBLKS = DC / 16;                  // 32 column blocks of O
+constexpr int KS = DROW / 32;                   // 18 k-steps of 16 dims per wave
+constexpr int KS_LAT = DC / 32;                 // the first 16 of them are latent
+constexpr int CB = DC / 64;                     // 8 column blocks of 32 per wave
+constexpr int XCH_BYTES = 32 * 32 * 4;          // one wave's partial score tile
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float RESCALE_SLACK = 8.0f;           // log2 units a stale max may lag
-constexpr int MAX_SPLIT_PAGES = MLA_MAX_SPLIT_TOKENS / PAGE;
 
 // LDS slot layout for a block of 32 tokens:
 //   [0, 32 KB)      latent rows, 1024 B each; 16-byte chunk c of row r sits at
 //                   chunk position c ^ fl(r) (XOR inside aligned 16-chunk groups)
-//   [32 KB, 36 KB)  rotary keys, 128 B each; chunk c of row r at c ^ (r & 7)
-// fl is a bijection on 0..15 chosen so that (a) 16 consecutive rows reading the
-// same chunk and (b) 4 aligned consecutive rows reading an aligned chunk pair
-// (the transposed value reads) each touch distinct banks.
-__device__ __forceinline__ int fl(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+//   [32 KB, 36 KB)  rotary keys, 128 B each; chunk c of row r at c ^ fr(r)
+// The LDS serves a 128-bit read to 16 consecutive lanes at a time and a
+// transposed 64-bit read to lanes 0..31 and 32..63 (gfx950, measured per
+// access pattern with the bank-conflict counter), so:
+//   - score reads: lanes 16k..16k+15 read rows 16m..16m+15 at one chunk, so
+//     fl must be a bijection on r & 15;
+//   - value reads: 4 aligned rows, each at one aligned 4-chunk group, need
+//     bits 2..3 of fl distinct over 4 aligned rows.
+// fl(r) = 4 (r & 3) + ((r >> 2) & 3) satisfies both.  For the 128-byte rotary
+// rows (two per 256-byte bank period) the 16 rows of a read must cover
+// (r & 1, position) once each: fr(r) = (r >> 1) & 7.
+__device__ __forceinline__ int fl(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int fr(int r) { return (r >> 1) & 7; }
 
-// 8-dim group of a 32-dim k-step that the 16-lane group g of a wave reads in
-// the score product.  With lane groups 1 and 2 exchanged, the 16 lanes the LDS
-// serves together in a 128-bit read hit 16 distinct bank quads (measured on
-// gfx950: the identity order costs a 2-way conflict on every score read).
-__device__ __forceinline__ int kgroup(int g) { return ((g & 1) << 1) | (g >> 1); }
-
-// Pairwise reductions across lanes l ^ 16 and l ^ 32 with the gfx950 lane
-// swaps (VALU; no LDS traffic).  Both lanes of a pair get the same result.
-__device__ __forceinline__ float max_xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
+// Maximum / sum across lanes l and l ^ 32 with the gfx950 lane swap (VALU).
 __device__ __forceinline__ float max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ float sum_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -80,7 +90,7 @@ __device__ __forceinline__ float sum_xor32(float v) {
 template <int NW>
 struct BlockCopier {
   static constexpr int NI = (NDMA + NW - 1) / NW;       // max DMA copies per wave per block
-  static_assert(3 * NI <= 63, "three blocks of copies must fit the vmcnt counter");
+  static_assert(2 * NI <= 63, "two blocks of copies must fit the vmcnt counter");
 
   // Copies this wave issues per block: copies n = wave, wave + NW, ... < 36.
   __device__ __forceinline__ static int copies(int wave) { return (NDMA - wave + NW - 1) / NW; }
@@ -94,7 +104,7 @@ struct BlockCopier {
     const uint8_t *base = cache + (static_cast<size_t>(phys) * PAGE + (tok0 & 32)) * ROW_BYTES;
     const uint32_t slot_lds = lds_addr(slot);
     // Opaque copy of the lane id: keeps the compiler from hoisting the
-    // per-copy address arithmetic out of the streaming loop into registers.
+    // per-copy offsets out of the streaming loop into registers.
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -102,80 +112,110 @@ struct BlockCopier {
       const int n = wave + i * NW;
       if (i * NW + NW <= NDMA || n < NDMA) {
         if (n < TB) {
-          const int r = min(n, last);
-          dma16(base + r * ROW_BYTES + ((ln ^ fl(n)) << 4),
-                __builtin_amdgcn_readfirstlane(slot_lds + n * LAT_BYTES));
+          // row min(n, last) through a scalar base; lane offset (lane ^ fl(n)) * 16
+          dma16_s(static_cast<uint32_t>((ln ^ fl(n)) << 4), base + min(n, last) * ROW_BYTES,
+                  __builtin_amdgcn_readfirstlane(slot_lds + n * LAT_BYTES));
         } else {
           const int rr = (n - TB) * 8 + (ln >> 3);
           const int r = min(rr, last);
-          dma16(base + r * ROW_BYTES + LAT_BYTES + (((ln & 7) ^ (rr & 7)) << 4),
-                __builtin_amdgcn_readfirstlane(slot_lds + SLOT_LAT + (n - TB) * 1024));
+          dma16_s(static_cast<uint32_t>(r * ROW_BYTES + LAT_BYTES + (((ln & 7) ^ fr(rr)) << 4)), base,
+                  __builtin_amdgcn_readfirstlane(slot_lds + SLOT_LAT + (n - TB) * 1024));
         }
       }
     }
   }
 };
 
-// 16 heads per wave: v_mfma_f32_16x16x32_bf16, two waves per SIMD.
+// One wave of a pair: 32 heads, half of the score contraction, half of the
+// output columns.  MFMA 32x32x16 bf16 lane layouts (A/B: row or column l % 32,
+// k = 8 (l / 32) + j; C: column l % 32, row 8 (i / 4) + 4 (l / 32) + i % 4).
 template <int NW_>
-struct DecoderW16 {
+struct DecoderPair {
   static constexpr int NW = NW_;
-  static constexpr int HPW = 16;
+  static constexpr int HEADS = NW * 16;          // heads per workgroup
   static constexpr int NI = BlockCopier<NW>::NI;
 
   const DecodeArgs &a;
-  const int lane, wave, g, r16;
-  const int b, split, head;
-  const bool head_ok;
+  const int wave, half;                          // wave-uniform
+  const int b, split;
   const int t_begin, t_end;
-  const int32_t *pages;       // LDS copy of the chunk's page ids
+  const int32_t *bt_row;                         // block-table row of the sequence
+  uint8_t *xch;                                  // LDS exchange tiles, one per wave
 
-  bf16x8 qf[KSTEPS];
-  f32x4 o[CBLKS];
+  bf16x8 qf[KS];
+  f32x16 o[CB];
+  f32x16 s;                   // this wave's partial, then the full, scores of a block
   // m_run: running max (log2 units); l_run: sum of the bf16-rounded weights
   // that multiply V (normalises o consistently); e_run: the same sum of the
-  // unrounded weights (gives an lse free of the bf16 rounding of P).
+  // unrounded weights (gives an lse free of the bf16 rounding of P).  Each
+  // lane holds the sums over its 16 tokens of a block; lanes l and l ^ 32
+  // together cover the head.
   float m_run, l_run, e_run;
-  // per-lane LDS byte offsets; every LDS read is one of these plus a constant
-  int k_off[4];               // latent score reads, ks & 3
-  int kr_off[2];              // rotary score reads, ks - 16
-  int v_off[8];               // transposed value reads, cb & 7
 
-  __device__ DecoderW16(const DecodeArgs &args, const int32_t *pages_, int b_, int split_, int t0, int t1)
-      : a(args), lane(threadIdx.x & 63), wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)),
-        g((threadIdx.x & 63) >> 4),
-        r16(threadIdx.x & 15), b(b_), split(split_),
-        head((blockIdx.y * NW + (threadIdx.x >> 6)) * HPW + (threadIdx.x & 15)),
-        head_ok(((blockIdx.y * NW + (threadIdx.x >> 6)) * HPW + (threadIdx.x & 15)) < args.H),
-        t_begin(t0), t_end(t1), pages(pages_) {}
+  __device__ DecoderPair(const DecodeArgs &args, uint8_t *xch_, int b_, int split_, int t0, int t1)
+      : a(args), wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)),
+        half(__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 1)),
+        b(b_), split(split_), t_begin(t0), t_end(t1),
+        bt_row(args.block_table + static_cast<size_t>(b_) * args.max_blocks), xch(xch_) {}
+
+  // Per-lane quantities are recomputed where they are used rather than held
+  // in registers across the streaming loop; the opaque lane id keeps the
+  // compiler from hoisting them back out of it.
+  __device__ __forceinline__ static int lane_id() {
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l;
+  }
+  __device__ __forceinline__ int head_of(int l) const { return blockIdx.y * HEADS + (wave >> 1) * 32 + (l & 31); }
+
+  // LDS byte offsets of the first read of each kind.  Every other read is one
+  // of these XOR a compile-time constant plus an immediate: the XOR acts on
+  // address bits that the base's remaining terms leave zero.
+  //   latent score reads, k-step ks < 16: row r = l % 32, latent chunk
+  //   2 (2 ks + half) + hb = 16 (ks >> 2) + (4 (ks & 3) + 2 half + hb), at
+  //   position (4 (ks & 3) ^ (fl & 12)) + ((2 half + hb) ^ (fl & 3)):
+  //   k_base ^ 64 (ks & 3), + 256 (ks >> 2)
+  __device__ __forceinline__ int k_base(int l) const {
+    const int r = l & 31, hb = l >> 5, f = fl(r);
+    return r * LAT_BYTES + (((f & 12) | ((2 * half + hb) ^ (f & 3))) << 4);
+  }
+  //   rotary score reads, k-steps 16, 17: chunk 4 (ks - 16) + 2 half + hb of
+  //   row r, at position (4 (ks - 16) ^ (fr & 4)) + ((2 half + hb) ^ (fr & 3)):
+  //   kr_base ^ 64 (ks - 16)
+  __device__ __forceinline__ int kr_base(int l) const {
+    const int r = l & 31, hb = l >> 5, g = fr(r);
+    return SLOT_LAT + r * ROPE_BYTES + (((g & 4) | ((2 * half + hb) ^ (g & 3))) << 4);
+  }
+  //   value reads (transposed, lane l supplies one address): row
+  //   16 t + 8 hi + 4 (l / 32) + (l & 15) / 4, latent chunk of column block
+  //   cb = 8 half + j: 4 cb + 2 ((l >> 4) & 1) + (l & 3) / 2, byte 8 (l & 1):
+  //   v_base ^ 64 (j & 3), + 256 (j >> 2), + 16 KB t; the hi rows sit 8 rows
+  //   further, where fl(row + 8) = fl(row) ^ 2: ^ 32, + 8 KB
+  __device__ __forceinline__ int v_base(int l) const {
+    const int row0 = 4 * (l >> 5) + ((l & 15) >> 2);
+    const int fv = fl(row0);
+    const int csub = 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
+    return row0 * LAT_BYTES + half * 512 + (((fv & 12) | (csub ^ (fv & 3))) << 4) + 8 * (l & 1);
+  }
+  //   exchange tile: four 1 KB rows of 16 B per lane, lane chunk l ^ 8 (l / 32)
+  __device__ __forceinline__ static int x_off(int l) { return (l ^ ((l >> 5) << 3)) << 4; }
 
   __device__ __forceinline__ void begin() {
     m_run = -INFINITY;
     l_run = 0.f;
     e_run = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < CBLKS; ++cb) o[cb] = f32x4{};
-    // score reads: row r16 (+16), latent chunk 4 ks + kg = 16 (ks >> 2) + (4 (ks & 3) + kg)
-    const int kg = kgroup(g);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) k_off[e] = r16 * LAT_BYTES + (((4 * e + kg) ^ fl(r16)) << 4);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) kr_off[e] = SLOT_LAT + r16 * ROPE_BYTES + (((4 * e + kg) ^ (r16 & 7)) << 4);
-    // value reads: row trow (+16), latent chunk 2 cb + csub = 16 (cb >> 3) + (2 (cb & 7) + csub),
-    // byte (r16 & 1) * 8 inside the chunk
-    const int trow = g * 4 + (r16 >> 2);
-    const int csub = (r16 & 3) >> 1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      v_off[e] = trow * LAT_BYTES + (((2 * e + csub) ^ fl(trow)) << 4) + (r16 & 1) * 8;
+    for (int j = 0; j < CB; ++j) o[j] = f32x16{};
   }
 
-  // Query fragments (MFMA B operand): lane (head, g) holds dims [32 ks + 8 kgroup(g), +8),
-  // the same 8-dim group its score reads fetch from the cached rows.
+  // Query fragments (MFMA B operand): lane (head, hb) holds dims
+  // 16 (2 ks + half) + 8 hb + [0, 8).
   __device__ __forceinline__ void load_q() {
-    const uint16_t *qp = a.q + (static_cast<size_t>(b) * a.H + (head_ok ? head : 0)) * DROW + kgroup(g) * 8;
+    const int l = threadIdx.x & 63, head = head_of(l);
+    const bool head_ok = head < a.H;
+    const uint16_t *qp = a.q + (static_cast<size_t>(b) * a.H + (head_ok ? head : 0)) * DROW + half * 16 + (l >> 5) * 8;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = *reinterpret_cast<const u32x4 *>(qp + ks * 32);
       if (!head_ok) v = u32x4{0, 0, 0, 0};
       qf[ks] = __builtin_bit_cast(bf16x8, v);
@@ -184,108 +224,165 @@ struct DecoderW16 {
 
   __device__ __forceinline__ int copies() const { return BlockCopier<NW>::copies(wave); }
 
-  __device__ __forceinline__ void issue(int blk, uint8_t *slot) {
-    const int tok0 = t_begin + blk * TB;
-    const int phys = __builtin_amdgcn_readfirstlane(pages[(tok0 - t_begin) >> 6]);
-    BlockCopier<NW>::issue(a.cache, phys, tok0, min(TB, t_end - tok0) - 1, wave, lane, slot);
+  // Physical page of block blk: a scalar load from the block table, issued a
+  // step before the copy that needs it so its latency stays off the LDS path.
+  __device__ __forceinline__ int page_of(int blk) const {
+    return ((const_i32 *)bt_row)[(t_begin + blk * TB) >> 6];
   }
 
-  __device__ __forceinline__ void compute(const uint8_t *slot, int blk) {
+  __device__ __forceinline__ void issue(int blk, int phys, uint8_t *slot) {
     const int tok0 = t_begin + blk * TB;
+    BlockCopier<NW>::issue(a.cache, phys, tok0, min(TB, t_end - tok0) - 1, wave, threadIdx.x & 63, slot);
+  }
 
-    // ---- scores S^T[token, head] for the two 16-token halves of the block
-    f32x4 s0 = {}, s1 = {};
+  // Partial scores of the block in `slot` over this wave's 18 k-steps, then
+  // published to the partner wave through this wave's exchange tile.
+  __device__ __forceinline__ void scores(const uint8_t *slot) {
+    const int l = lane_id();
+    const int kb = k_base(l), krb = kr_base(l);
+
+    // ---- partial scores over this wave's 18 k-steps.  Operands stream
+    // through a ring PF k-steps deep so LDS latency overlaps earlier MFMAs;
+    // the empty asm ties each MFMA operand to its place in the ring (without
+    // it the scheduler sinks every read to just before its use).
+    auto kread = [&](int ks) -> bf16x8 {
+      const uint8_t *kp = ks < KS_LAT ? slot + (kb ^ ((ks & 3) * 64)) + (ks >> 2) * 256
+                                      : slot + (krb ^ ((ks - KS_LAT) * 64));
+      return *reinterpret_cast<const bf16x8 *>(kp);
+    };
+    constexpr int PF = 3;
+    bf16x8 kf[KS];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const uint8_t *kp = ks < KLAT ? slot + k_off[ks & 3] + (ks >> 2) * 256 : slot + kr_off[ks - KLAT];
-      const int second = ks < KLAT ? 16 * LAT_BYTES : 16 * ROPE_BYTES;
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8 *>(kp);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8 *>(kp + second);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
+    for (int ks = 0; ks < PF; ++ks) kf[ks] = kread(ks);
+    s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + PF < KS) kf[ks + PF] = kread(ks + PF);
+      asm volatile("" : "+v"(kf[ks]) : : "memory");
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
     }
 
-    // ---- online softmax: lane holds head r16 for tokens 4g+i and 16+4g+i
-    float xs[8];
+    uint8_t *mine = xch + wave * XCH_BYTES + x_off(l);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xs[i] = (i < 4 ? s0[i] : s1[i - 4]) * a.scale_log2;
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<f32x4 *>(mine + i * 1024) = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
+  }
+
+  // After the partner's partial is visible: full scores, online softmax and
+  // the value product for the block in `slot` (block index blk).
+  __device__ __forceinline__ void softmax_values(const uint8_t *slot, int blk) {
+    const int tok0 = t_begin + blk * TB;
+    const int l = lane_id(), hb = l >> 5;
+    const int vb = v_base(l);
+    // Both waves of the pair hold S_own + S_partner: the same fp32 sums, as
+    // addition commutes.
+    const uint8_t *theirs = xch + (wave ^ 1) * XCH_BYTES + x_off(l);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 t = *reinterpret_cast<const f32x4 *>(theirs + i * 1024);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[4 * i + e] += t[e];
+    }
+
+    // ---- online softmax: lane holds head l % 32 for tokens 8 (i / 4) + 4 hb + i % 4.
+    // Scores stay unscaled; the scale c = softmax_scale * log2(e) > 0 enters
+    // the running max (max(c s) = c max(s)) and the exponent as one fma.
+    const float c = a.scale_log2;
     if (tok0 + TB > t_end) [[unlikely]] {
       // last block of the chunk: tokens at or past t_end do not exist
-      const int lim = t_end - tok0 - g * 4;
+      const int lim = t_end - tok0 - 4 * hb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if ((i >> 2) * 16 + (i & 3) >= lim) xs[i] = -INFINITY;
+      for (int i = 0; i < 16; ++i)
+        if ((i >> 2) * 8 + (i & 3) >= lim) s[i] = -INFINITY;
     }
-    float mx = xs[0];
+    float mx = s[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, xs[i]);
-    mx = max_xor32(max_xor16(mx));
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = max_xor32(mx) * c;
     const float m_new = fmaxf(m_run, mx);
     if (__ballot(m_new > m_run + RESCALE_SLACK)) {
       const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-      for (int cb = 0; cb < CBLKS; ++cb) o[cb] *= alpha;
+      for (int j = 0; j < CB; ++j) o[j] *= alpha;
       l_run *= alpha;
       e_run *= alpha;
       m_run = m_new;
     }
-    bf16x8 p;
-    float ps = 0.f, pe = 0.f;
+    // P as the MFMA B operand of token step t: k index 8 hb + j stands for
+    // token 16 t + 8 (j / 4) + 4 hb + j % 4, i.e. score register 8 t + j.
+    bf16x8 p[2];
+    float pe = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m_run));
+      pe += pf;
+      p[i >> 3][i & 7] = to_bf16(pf);
+    }
+    // sum of the rounded weights: bf16 pairs dotted with (1, 1)
+    float ps = l_run;
+    const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float pf = __builtin_amdgcn_exp2f(xs[i] - m_run);
-      const __bf16 pb = to_bf16(pf);
-      pe += pf;
-      ps += static_cast<float>(pb);
-      p[i] = pb;
+      const bf16x2 pr = {p[i >> 2][2 * (i & 3)], p[i >> 2][2 * (i & 3) + 1]};
+      ps = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps, false);
     }
-    l_run += ps;
+    l_run = ps;
     e_run += pe;
 
-    // ---- O^T[col, head] += V^T[col, token] P^T[token, head]
-    // The MFMA k index 8g + j stands for token 4g + j (j < 4) and 16 + 4g + j - 4
-    // (j >= 4): the order in which the score accumulators hold P.  Each
-    // transposed read returns 4 tokens of one column per lane; lane
-    // (16g + 4r + q) supplies the address of token row r, columns [4q, 4q+4)
-    // of the 16-column block.
-#pragma unroll
-    for (int cb = 0; cb < CBLKS; ++cb) {
-      const uint8_t *r0 = slot + v_off[cb & 7] + (cb >> 3) * 256;
+    // ---- O^T[col, head] += V^T[col, token] P^T[token, head] over this wave's
+    // 8 column blocks and the block's two 16-token steps.  A transposed read
+    // returns 4 consecutive tokens of one column per lane: "lo" covers tokens
+    // 16 t + 4 hb + [0, 4), "hi" the same 8 rows further.
+    auto vread = [&](int n) -> bf16x8 {
+      const int j = n >> 1, t = n & 1;
+      const int x = vb ^ ((j & 3) * 64);
+      const uint8_t *r0 = slot + x + (j >> 2) * 256 + t * 16 * LAT_BYTES;
+      const uint8_t *r1 = slot + (x ^ 32) + (j >> 2) * 256 + t * 16 * LAT_BYTES + 8 * LAT_BYTES;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)r0);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(r0 + 16 * LAT_BYTES));
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, p, o[cb], 0, 0, 0);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)r1);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int PV = 2;
+    constexpr int NV = 2 * CB;
+    bf16x8 vf[NV];
+#pragma unroll
+    for (int n = 0; n < PV; ++n) vf[n] = vread(n);
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      if (n + PV < NV) vf[n + PV] = vread(n + PV);
+      asm volatile("" : "+v"(vf[n]) : : "memory");
+      o[n >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[n], p[n & 1], o[n >> 1], 0, 0, 0);
     }
   }
 
-  // lane (head r16, g) holds columns 16 cb + 4 g + [0,4) of its head.
+  // Lane (head l % 32, hb) holds columns 32 (8 half + j) + 8 q + 4 hb + [0, 4)
+  // in registers 4 q .. 4 q + 3 of o[j].
   __device__ __forceinline__ void finish() {
-    const float l_tot = sum_xor32(sum_xor16(l_run));
-    const float e_tot = sum_xor32(sum_xor16(e_run));
+    const float l_tot = sum_xor32(l_run);
+    const float e_tot = sum_xor32(e_run);
     const float inv = 1.0f / l_tot;
     const float lse_v = (m_run + __log2f(e_tot)) * LN2;
-    if (!head_ok) return;
+    const int l = threadIdx.x & 63, hb = l >> 5, head = head_of(l);
+    if (head >= a.H) return;
+    uint16_t *dst;
     if (a.direct) {
-      uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + g * 4;
-#pragma unroll
-      for (int cb = 0; cb < CBLKS; ++cb) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[cb][e] * inv);
-        *reinterpret_cast<bf16x4 *>(dst + cb * 16) = v;
-      }
-      if (g == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = lse_v;
+      dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC;
+      if (half == 0 && hb == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = lse_v;
     } else {
       const size_t row = (static_cast<size_t>(b) * a.n_splits + split) * a.H + head;
-      uint16_t *dst = a.o_part + row * DC + g * 4;
+      dst = a.o_part + row * DC;
+      if (half == 0 && hb == 0) a.lse_part[row] = lse_v;
+    }
+    dst += half * 256 + hb * 4;
 #pragma unroll
-      for (int cb = 0; cb < CBLKS; ++cb) {
+    for (int j = 0; j < CB; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[cb][e] * inv);
-        *reinterpret_cast<bf16x4 *>(dst + cb * 16) = v;
+        for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[j][4 * q + e] * inv);
+        *reinterpret_cast<bf16x4 *>(dst + j * 32 + q * 8) = v;
       }
-      if (g == 0) a.lse_part[row] = lse_v;
     }
   }
 };
@@ -298,16 +395,38 @@ __device__ __forceinline__ void wait_block(bool full_share) {
   else wait_vmcnt<AHEAD * (NI - 1)>();
 }
 
-#define MLA_DECODE_STEP(K, CUR, NXT)                                   \
+// Group X, block i in slot CUR: [wait copies of i] Ba [scores i] Bb [copy i + 2
+// into NXT] [softmax + values i].
+#define MLA_STEP_X(K, CUR, NXT)                                        \
   {                                                                    \
     const int i = blk + (K);                                           \
     if (i >= nblk) break;                                              \
-    if (i + 2 < nblk) wait_block<D::NI, 2>(full_share);                \
-    else if (i + 1 < nblk) wait_block<D::NI, 1>(full_share);           \
+    const int phys = i + 2 < nblk ? dec.page_of(i + 2) : 0;            \
+    if (i + 1 < nblk) wait_block<D::NI, 1>(full_share);                \
     else wait_vmcnt<0>();                                              \
     barrier_no_fence();                                                \
-    if (i + 3 < nblk) dec.issue(i + 3, NXT);                           \
-    dec.compute(CUR, i);                                               \
+    dec.scores(CUR);                                                   \
+    barrier_lds();                                                     \
+    if (i + 2 < nblk) dec.issue(i + 2, phys, NXT);                     \
+    dec.softmax_values(CUR, i);                                        \
+  }
+
+// Group Y, block i >= 1 in slot CUR (block i - 1 in PRV, which is also the
+// slot block i + 2 is copied into): [wait copies of i] Ba [softmax + values
+// i - 1] Bb [copy i + 2 into PRV] [scores i].  Ba publishes Y's partials of
+// i - 1.
+#define MLA_STEP_Y(K, CUR, PRV)                                        \
+  {                                                                    \
+    const int i = blk + (K);                                           \
+    if (i >= nblk) break;                                              \
+    const int phys = i + 2 < nblk ? dec.page_of(i + 2) : 0;            \
+    if (i + 1 < nblk) wait_block<D::NI, 1>(full_share);                \
+    else wait_vmcnt<0>();                                              \
+    barrier_lds();                                                     \
+    dec.softmax_values(PRV, i - 1);                                    \
+    barrier_no_fence();                                                \
+    if (i + 2 < nblk) dec.issue(i + 2, phys, PRV);                     \
+    dec.scores(CUR);                                                   \
   }
 
 template <class D, int WAVES_PER_EU>
@@ -317,11 +436,14 @@ void decode_bf16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t slot0[SLOT_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slot1[SLOT_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slot2[SLOT_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t slot3[SLOT_BYTES];
-  __shared__ int32_t pages[MAX_SPLIT_PAGES];
+  __shared__ __attribute__((aligned(16))) uint8_t xch[D::NW * XCH_BYTES];
   constexpr int NW = D::NW;
 
-  const int item = blockIdx.x;
+  // Chunk placement: workgroups are dealt to the 8 XCDs round-robin by id, so
+  // id -> (XCD id % 8, position id / 8) is remapped to consecutive chunk
+  // indices per XCD; the chunks of a sequence then share one L2.
+  int item = blockIdx.x;
+  if ((gridDim.x & 7) == 0) item = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int b = item / a.n_splits;
   const int split = item - b * a.n_splits;
   const int S = a.seq_lens[b];
@@ -334,48 +456,61 @@ void decode_bf16_kernel(DecodeArgs a) {
     // sequence are skipped by the combine kernel.
     if (a.direct) {
       const int t = threadIdx.x;
-      const int per = NW * 64 / (D::HPW * NW);            // threads per head
-      const int head = blockIdx.y * D::HPW * NW + t / per;
+      const int head = blockIdx.y * D::HEADS + t / 4;       // 4 threads per head
       if (head < a.H) {
-        const int cols = DC / per;
-        uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + (t % per) * cols;
-        for (int c = 0; c < cols; c += 8) *reinterpret_cast<u32x4 *>(dst + c) = u32x4{0, 0, 0, 0};
-        if (t % per == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = -INFINITY;
+        uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + (t % 4) * (DC / 4);
+        for (int c = 0; c < DC / 4; c += 8) *reinterpret_cast<u32x4 *>(dst + c) = u32x4{0, 0, 0, 0};
+        if (t % 4 == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = -INFINITY;
       }
     }
     return;
   }
 
-  // Page ids of this chunk -> LDS, so the streaming loop issues no vector
-  // loads besides its DMA copies (vmcnt then counts exactly those).
-  {
-    const int32_t *bt = a.block_table + static_cast<size_t>(b) * a.max_blocks + (t_begin >> 6);
-    const int np = (t_end - t_begin + PAGE - 1) / PAGE;
-    for (int i = threadIdx.x; i < np; i += NW * 64) pages[i] = bt[i];
-  }
-  __syncthreads();
-
-  D dec(a, pages, b, split, t_begin, t_end);
+  // Page ids are read with scalar loads (the streaming loop's only vector
+  // memory operations are its DMA copies, so vmcnt counts exactly those).
+  D dec(a, xch, b, split, t_begin, t_end);
   dec.begin();
   dec.load_q();
   wait_vmcnt<0>();            // query fragments landed before any copy is queued
   const bool full_share = dec.copies() == D::NI;
 
   const int nblk = (t_end - t_begin + TB - 1) / TB;
-  dec.issue(0, slot0);
-  if (nblk > 1) dec.issue(1, slot1);
-  if (nblk > 2) dec.issue(2, slot2);
+  dec.issue(0, dec.page_of(0), slot0);
+  if (nblk > 1) dec.issue(1, dec.page_of(1), slot1);
 
-  for (int blk = 0; blk < nblk; blk += 4) {
-    MLA_DECODE_STEP(0, slot0, slot3)
-    MLA_DECODE_STEP(1, slot1, slot0)
-    MLA_DECODE_STEP(2, slot2, slot1)
-    MLA_DECODE_STEP(3, slot3, slot2)
+  // Slot of block i: i % 3.  A slot is rewritten (block i + 3) only after the
+  // second barrier of block i + 1, when both groups are done with block i.
+  const bool group_y = NW == 8 && (threadIdx.x >> 8) != 0;
+  if (!group_y) {
+    for (int blk = 0; blk < nblk; blk += 3) {
+      MLA_STEP_X(0, slot0, slot2)
+      MLA_STEP_X(1, slot1, slot0)
+      MLA_STEP_X(2, slot2, slot1)
+    }
+    barrier_no_fence();       // Y publishes its partials of the last block
+  } else {
+    // block 0: nothing of Y's to finish yet
+    if (nblk > 1) wait_block<D::NI, 1>(full_share);
+    else wait_vmcnt<0>();
+    const int phys = nblk > 2 ? dec.page_of(2) : 0;
+    barrier_lds();
+    barrier_no_fence();
+    if (nblk > 2) dec.issue(2, phys, slot2);
+    dec.scores(slot0);
+    for (int blk = 1; blk < nblk; blk += 3) {
+      MLA_STEP_Y(0, slot1, slot0)
+      MLA_STEP_Y(1, slot2, slot1)
+      MLA_STEP_Y(2, slot0, slot2)
+    }
+    barrier_lds();
+    const int last = nblk - 1;
+    dec.softmax_values(last % 3 == 0 ? slot0 : (last % 3 == 1 ? slot1 : slot2), last);
   }
   dec.finish();
 }
 
-#undef MLA_DECODE_STEP
+#undef MLA_STEP_X
+#undef MLA_STEP_Y
 
 // Merge split-KV partials: o = sum_c w_c o_c / sum_c w_c, w_c = exp(lse_c - L).
 // One 64-lane group per (sequence, head), 8 columns per lane.
@@ -425,9 +560,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int groups = (a.H + hpw * nw - 1) / (hpw * nw);
   dim3 grid(a.B * a.n_splits, groups);
   switch (nw) {
-    case 2: decode_bf16_kernel<DecoderW16<2>, 1><<<grid, 128, 0, stream>>>(a); break;
-    case 4: decode_bf16_kernel<DecoderW16<4>, 1><<<grid, 256, 0, stream>>>(a); break;
-    default: decode_bf16_kernel<DecoderW16<8>, 2><<<grid, 512, 0, stream>>>(a); break;
+    case 2: decode_bf16_kernel<DecoderPair<2>, 1><<<grid, 128, 0, stream>>>(a); break;
+    case 4: decode_bf16_kernel<DecoderPair<4>, 1><<<grid, 256, 0, stream>>>(a); break;
+    default: decode_bf16_kernel<DecoderPair<8>, 2><<<grid, 512, 0, stream>>>(a); break;
   }
   return hipGetLastError();
 }
