@@ -8,32 +8,32 @@
 // "Multi-Head Latent Attention vs GQA vs MQA", "Arithmetic intensity changes
 // under absorption").
 //
-// Work split: the waves of a workgroup form pairs; a pair owns 32 heads.
-// Both waves of a pair see every token of a block, and each takes half of the
-// contraction and half of the output:
-//   scores   S^T[tok, head] = K[tok, dims] . Q^T[dims, head]   (v_mfma_f32_32x32x16_bf16)
-//            wave h sums the 16-dim k-steps 2 ks + h, ks = 0..17 (latent and rotary)
-//   exchange each wave adds its partner's fp32 partial through LDS; both then hold
-//            the identical full scores and run the same online softmax (fp32, exp2,
-//            lazily rescaled)
-//   values   O^T[col, head] += V^T[col, tok] . P^T[tok, head], V = K[:, 0:512];
-//            wave h owns columns [256 h, 256 h + 256)
-// A 32x32x16 product reads one 1 KB operand tile per 16384 MACs, half of what a
-// 16x16x32 product needs, so the pair layout halves the LDS bytes per MFMA for
-// the same register footprint (72 query + 128 accumulator VGPRs per wave).
+// Work split (8 waves, 128 heads): waves pair up on 32 heads.
+//   scores   each wave owns 16 heads: S^T[tok, head] = K[tok, 0:576] . Q^T
+//            (v_mfma_f32_16x16x32_bf16), then the online softmax of its heads
+//            (fp32, exp2, lazily rescaled) and P rounded to bf16
+//   exchange both waves of a pair publish P (bf16, 1 KB per wave) and the
+//            per-head rescale factors through LDS
+//   values   O^T[col, head] += V^T[col, tok] . P^T[tok, head] for the pair's 32
+//            heads (v_mfma_f32_32x32x16_bf16), V = K[:, 0:512]; wave h of the
+//            pair owns columns [256 h, 256 h + 256)
+// The 32x32x16 value product reads one 1 KB operand tile per 16384 MACs, half
+// of what 16-head value products need, at the same register footprint (72
+// query + 128 accumulator VGPRs per wave), and no score or softmax work is
+// duplicated.
 //
-// Schedule: with 8 waves, waves w and w + 4 share a SIMD.  Waves 0..3 (group
-// X) and 4..7 (group Y) run half a block apart, so one group's score MFMAs
-// overlap the other group's softmax (VALU) instead of both groups idling the
-// matrix core at the same time.  Two workgroup barriers per block serve both
-// groups: for X they are "block ready" and "partials exchanged", for Y the
+// Schedule: waves w and w + 4 share a SIMD.  Waves 0..3 (group X) and 4..7
+// (group Y) run half a block apart, so one group's score MFMAs and softmax
+// overlap the other group's value MFMAs.  Two workgroup barriers per block
+// serve both groups: for X they are "block ready" and "P exchanged", for Y the
 // other way round.
 //
 // Data movement: 16-byte global->LDS DMA copies (global_load_lds_dwordx4),
-// one 1 KB latent row per wave-wide copy, into a ring of three 36 KB slots.  Chunks are XOR-swizzled per row
-// so that the row-wise score reads (ds_read_b128) and the transposed value
-// reads (ds_read_b64_tr_b16) spread over the LDS banks; the value operand is
-// read transposed straight out of the same tile.
+// one 1 KB latent row per wave-wide copy, into a ring of four 36 KB slots;
+// copies of a block are issued 2.5 blocks ahead of their first use.  Chunks
+// are XOR-swizzled per row so that the row-wise score reads (ds_read_b128) and
+// the transposed value reads (ds_read_b64_tr_b16) spread over the LDS banks;
+// the value operand is read transposed straight out of the same tile.
 //
 // Split-KV: a sequence may be cut into chunks of split_tokens; each chunk
 // writes (o / l in bf16, lse in fp32) partials and a combine kernel merges
@@ -51,11 +51,13 @@ constexpr int LAT_BYTES = DC * 2;               // 1024: latent part of a row
 constexpr int ROPE_BYTES = DR * 2;              // 128: rotary part of a row
 constexpr int SLOT_LAT = TB * LAT_BYTES;        // 32768
 constexpr int SLOT_BYTES = SLOT_LAT + TB * ROPE_BYTES;   // 36864
+constexpr int NSLOT = 4;
 constexpr int NDMA = TB + TB * ROPE_BYTES / 1024;        // 36 wave-wide copies per block
-constexpr int KS = DROW / 32;                   // 18 k-steps of 16 dims per wave
-constexpr int KS_LAT = DC / 32;                 // the first 16 of them are latent
-constexpr int CB = DC / 64;                     // 8 column blocks of 32 per wave
-constexpr int XCH_BYTES = 32 * 32 * 4;          // one wave's partial score tile
+constexpr int KSTEPS = DROW / 32;               // 18 score k-steps of 32 dims
+constexpr int KLAT = DC / 32;                   // the first 16 of them are latent
+constexpr int CB = DC / 64;                     // 8 value column blocks of 32 per wave
+constexpr int PX_BYTES = 8 * 32 * 8;            // P of a pair: [token quartet][head][4 tokens] bf16
+constexpr int AX_BYTES = 32 * 4;                // per-head fp32 factors of a pair
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float RESCALE_SLACK = 8.0f;           // log2 units a stale max may lag
 
@@ -63,23 +65,37 @@ constexpr float RESCALE_SLACK = 8.0f;           // log2 units a stale max may la
 //   [0, 32 KB)      latent rows, 1024 B each; 16-byte chunk c of row r sits at
 //                   chunk position c ^ fl(r) (XOR inside aligned 16-chunk groups)
 //   [32 KB, 36 KB)  rotary keys, 128 B each; chunk c of row r at c ^ fr(r)
-// The LDS serves a 128-bit read to 16 consecutive lanes at a time and a
-// transposed 64-bit read to lanes 0..31 and 32..63 (gfx950, measured per
-// access pattern with the bank-conflict counter), so:
-//   - score reads: lanes 16k..16k+15 read rows 16m..16m+15 at one chunk, so
-//     fl must be a bijection on r & 15;
+// LDS bank groups on gfx950 (measured lane pair by lane pair with the
+// bank-conflict counter): a 128-bit read is served 16 lanes at a time, the
+// groups being the 4-lane clusters q = l / 4 in {0, 3, 5, 6}, {1, 2, 4, 7},
+// {8, 11, 13, 14}, {9, 10, 12, 15}; a 64-bit write 16 consecutive lanes at a
+// time.  A 16-byte chunk's bank quad is its position mod 16 (rows are 1 KB).
+//   - score reads (lane l: row l % 16, chunk 4 ks + l / 16): group {0,3,5,6}
+//     holds rows {0-3, 12-15} at chunk c and rows {4-11} at chunk c + 1, so
+//     fl must be a bijection on r & 15 whose values on rows 4..11 are closed
+//     under ^ 1;
 //   - value reads: 4 aligned rows, each at one aligned 4-chunk group, need
 //     bits 2..3 of fl distinct over 4 aligned rows.
-// fl(r) = 4 (r & 3) + ((r >> 2) & 3) satisfies both.  For the 128-byte rotary
-// rows (two per 256-byte bank period) the 16 rows of a read must cover
-// (r & 1, position) once each: fr(r) = (r >> 1) & 7.
-__device__ __forceinline__ int fl(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// fl(r) = 4 (r & 3) + h[(r >> 2) & 3] with h = (2, 0, 1, 3) satisfies both
+// (and fl(r + 4) = fl(r) ^ 2 for r % 8 < 4).  For the 128-byte rotary rows
+// (two per 256-byte bank period) fr(r) = (r >> 1) & 7 spreads every read group
+// over distinct (r & 1, position) pairs.
+__device__ __forceinline__ int fl(int r) { return ((r & 3) << 2) | ((0xD2 >> (2 * ((r >> 2) & 3))) & 3); }
 __device__ __forceinline__ int fr(int r) { return (r >> 1) & 7; }
 
-// Maximum / sum across lanes l and l ^ 32 with the gfx950 lane swap (VALU).
+// Pairwise reductions across lanes l ^ 16 and l ^ 32 with the gfx950 lane
+// swaps (VALU; no LDS traffic).  Both lanes of a pair get the same result.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ float sum_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -90,7 +106,7 @@ __device__ __forceinline__ float sum_xor32(float v) {
 template <int NW>
 struct BlockCopier {
   static constexpr int NI = (NDMA + NW - 1) / NW;       // max DMA copies per wave per block
-  static_assert(2 * NI <= 63, "two blocks of copies must fit the vmcnt counter");
+  static_assert((NSLOT - 1) * NI <= 63, "three blocks of copies must fit the vmcnt counter");
 
   // Copies this wave issues per block: copies n = wave, wave + NW, ... < 36.
   __device__ __forceinline__ static int copies(int wave) { return (NDMA - wave + NW - 1) / NW; }
@@ -126,9 +142,12 @@ struct BlockCopier {
   }
 };
 
-// One wave of a pair: 32 heads, half of the score contraction, half of the
-// output columns.  MFMA 32x32x16 bf16 lane layouts (A/B: row or column l % 32,
-// k = 8 (l / 32) + j; C: column l % 32, row 8 (i / 4) + 4 (l / 32) + i % 4).
+// One wave: scores and softmax for 16 heads, values for its pair's 32 heads
+// over half of the columns.
+//   MFMA 16x16x32 bf16: A/B lane l: row/column l % 16, k = 8 (l / 16) + j;
+//                       C register i: row 4 (l / 16) + i, column l % 16.
+//   MFMA 32x32x16 bf16: A/B lane l: row/column l % 32, k = 8 (l / 32) + j;
+//                       C register i: row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32.
 template <int NW_>
 struct DecoderPair {
   static constexpr int NW = NW_;
@@ -140,23 +159,27 @@ struct DecoderPair {
   const int b, split;
   const int t_begin, t_end;
   const int32_t *bt_row;                         // block-table row of the sequence
-  uint8_t *xch;                                  // LDS exchange tiles, one per wave
+  uint8_t *px;                                   // LDS: this pair's P tile
+  float *ax;                                     // LDS: this pair's per-head rescale factors
+  float *fx;                                     // LDS: this pair's per-head 1 / l
 
-  bf16x8 qf[KS];
+  bf16x8 qf[KSTEPS];
   f32x16 o[CB];
-  f32x16 s;                   // this wave's partial, then the full, scores of a block
-  // m_run: running max (log2 units); l_run: sum of the bf16-rounded weights
-  // that multiply V (normalises o consistently); e_run: the same sum of the
-  // unrounded weights (gives an lse free of the bf16 rounding of P).  Each
-  // lane holds the sums over its 16 tokens of a block; lanes l and l ^ 32
-  // together cover the head.
+  f32x4 s0, s1;               // scores of the block's two 16-token halves
+  // Per scoring lane (head l % 16, tokens 4 (l / 16) + i and 16 + 4 (l / 16) + i):
+  // m_run: running max of the head (log2 units); l_run: its share of the sum
+  // of the bf16-rounded weights that multiply V; e_run: the same sum of the
+  // unrounded weights (gives an lse free of the bf16 rounding of P).
   float m_run, l_run, e_run;
 
-  __device__ DecoderPair(const DecodeArgs &args, uint8_t *xch_, int b_, int split_, int t0, int t1)
+  __device__ DecoderPair(const DecodeArgs &args, uint8_t *px_, float *ax_, float *fx_, int b_, int split_, int t0,
+                         int t1)
       : a(args), wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)),
         half(__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 1)),
         b(b_), split(split_), t_begin(t0), t_end(t1),
-        bt_row(args.block_table + static_cast<size_t>(b_) * args.max_blocks), xch(xch_) {}
+        bt_row(args.block_table + static_cast<size_t>(b_) * args.max_blocks),
+        px(px_ + (threadIdx.x >> 7) * PX_BYTES), ax(ax_ + (threadIdx.x >> 7) * 32),
+        fx(fx_ + (threadIdx.x >> 7) * 32) {}
 
   // Per-lane quantities are recomputed where they are used rather than held
   // in registers across the streaming loop; the opaque lane id keeps the
@@ -166,39 +189,38 @@ struct DecoderPair {
     asm volatile("" : "+v"(l));
     return l;
   }
-  __device__ __forceinline__ int head_of(int l) const { return blockIdx.y * HEADS + (wave >> 1) * 32 + (l & 31); }
+  // head scored by lane l, and the pair head a 32-wide lane layout maps to lane l
+  __device__ __forceinline__ int score_head(int l) const { return blockIdx.y * HEADS + wave * 16 + (l & 15); }
+  __device__ __forceinline__ int pair_head(int l) const { return blockIdx.y * HEADS + (wave >> 1) * 32 + (l & 31); }
 
   // LDS byte offsets of the first read of each kind.  Every other read is one
   // of these XOR a compile-time constant plus an immediate: the XOR acts on
   // address bits that the base's remaining terms leave zero.
-  //   latent score reads, k-step ks < 16: row r = l % 32, latent chunk
-  //   2 (2 ks + half) + hb = 16 (ks >> 2) + (4 (ks & 3) + 2 half + hb), at
-  //   position (4 (ks & 3) ^ (fl & 12)) + ((2 half + hb) ^ (fl & 3)):
-  //   k_base ^ 64 (ks & 3), + 256 (ks >> 2)
-  __device__ __forceinline__ int k_base(int l) const {
-    const int r = l & 31, hb = l >> 5, f = fl(r);
-    return r * LAT_BYTES + (((f & 12) | ((2 * half + hb) ^ (f & 3))) << 4);
+  //   latent score reads, k-step ks < 16: row r = l % 16 (+16), chunk 4 ks + g
+  //   (g = l / 16) at position (4 (ks & 3) ^ (fl & 12)) + (g ^ (fl & 3)):
+  //   k_base ^ 64 (ks & 3), + 256 (ks >> 2), + 16 KB for rows 16..31
+  __device__ __forceinline__ static int k_base(int l) {
+    const int r = l & 15, g = l >> 4, f = fl(r);
+    return r * LAT_BYTES + (((f & 12) | (g ^ (f & 3))) << 4);
   }
-  //   rotary score reads, k-steps 16, 17: chunk 4 (ks - 16) + 2 half + hb of
-  //   row r, at position (4 (ks - 16) ^ (fr & 4)) + ((2 half + hb) ^ (fr & 3)):
-  //   kr_base ^ 64 (ks - 16)
-  __device__ __forceinline__ int kr_base(int l) const {
-    const int r = l & 31, hb = l >> 5, g = fr(r);
-    return SLOT_LAT + r * ROPE_BYTES + (((g & 4) | ((2 * half + hb) ^ (g & 3))) << 4);
+  //   rotary score reads, k-steps 16, 17: chunk 4 (ks - 16) + g of row r, at
+  //   position (4 (ks - 16) ^ (fr & 4)) + (g ^ (fr & 3)): kr_base ^ 64 (ks - 16),
+  //   + 2 KB for rows 16..31
+  __device__ __forceinline__ static int kr_base(int l) {
+    const int r = l & 15, g = l >> 4, f = fr(r);
+    return SLOT_LAT + r * ROPE_BYTES + (((f & 4) | (g ^ (f & 3))) << 4);
   }
   //   value reads (transposed, lane l supplies one address): row
-  //   16 t + 8 hi + 4 (l / 32) + (l & 15) / 4, latent chunk of column block
+  //   16 t + 8 (l / 32) + 4 hi + (l & 15) / 4, latent chunk of column block
   //   cb = 8 half + j: 4 cb + 2 ((l >> 4) & 1) + (l & 3) / 2, byte 8 (l & 1):
-  //   v_base ^ 64 (j & 3), + 256 (j >> 2), + 16 KB t; the hi rows sit 8 rows
-  //   further, where fl(row + 8) = fl(row) ^ 2: ^ 32, + 8 KB
+  //   v_base ^ 64 (j & 3), + 256 (j >> 2), + 16 KB t; the hi rows sit 4 rows
+  //   further, where fl(row + 4) = fl(row) ^ 2: ^ 32, + 4 KB
   __device__ __forceinline__ int v_base(int l) const {
-    const int row0 = 4 * (l >> 5) + ((l & 15) >> 2);
+    const int row0 = 8 * (l >> 5) + ((l & 15) >> 2);
     const int fv = fl(row0);
     const int csub = 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
     return row0 * LAT_BYTES + half * 512 + (((fv & 12) | (csub ^ (fv & 3))) << 4) + 8 * (l & 1);
   }
-  //   exchange tile: four 1 KB rows of 16 B per lane, lane chunk l ^ 8 (l / 32)
-  __device__ __forceinline__ static int x_off(int l) { return (l ^ ((l >> 5) << 3)) << 4; }
 
   __device__ __forceinline__ void begin() {
     m_run = -INFINITY;
@@ -208,14 +230,14 @@ struct DecoderPair {
     for (int j = 0; j < CB; ++j) o[j] = f32x16{};
   }
 
-  // Query fragments (MFMA B operand): lane (head, hb) holds dims
-  // 16 (2 ks + half) + 8 hb + [0, 8).
+  // Query fragments (16x16x32 B operand): lane (head l % 16, g = l / 16) holds
+  // dims 32 ks + 8 g + [0, 8).
   __device__ __forceinline__ void load_q() {
-    const int l = threadIdx.x & 63, head = head_of(l);
+    const int l = threadIdx.x & 63, head = score_head(l);
     const bool head_ok = head < a.H;
-    const uint16_t *qp = a.q + (static_cast<size_t>(b) * a.H + (head_ok ? head : 0)) * DROW + half * 16 + (l >> 5) * 8;
+    const uint16_t *qp = a.q + (static_cast<size_t>(b) * a.H + (head_ok ? head : 0)) * DROW + (l >> 4) * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KSTEPS; ++ks) {
       u32x4 v = *reinterpret_cast<const u32x4 *>(qp + ks * 32);
       if (!head_ok) v = u32x4{0, 0, 0, 0};
       qf[ks] = __builtin_bit_cast(bf16x8, v);
@@ -235,114 +257,127 @@ struct DecoderPair {
     BlockCopier<NW>::issue(a.cache, phys, tok0, min(TB, t_end - tok0) - 1, wave, threadIdx.x & 63, slot);
   }
 
-  // Partial scores of the block in `slot` over this wave's 18 k-steps, then
-  // published to the partner wave through this wave's exchange tile.
-  __device__ __forceinline__ void scores(const uint8_t *slot) {
-    const int l = lane_id();
+  // Scores of this wave's 16 heads for the block in `slot`, online softmax,
+  // then P and the rescale factors published to the pair's exchange tiles.
+  __device__ __forceinline__ void scores_softmax(const uint8_t *slot, int blk) {
+    const int l = lane_id(), g = l >> 4;
     const int kb = k_base(l), krb = kr_base(l);
-
-    // ---- partial scores over this wave's 18 k-steps.  Operands stream
-    // through a ring PF k-steps deep so LDS latency overlaps earlier MFMAs;
-    // the empty asm ties each MFMA operand to its place in the ring (without
-    // it the scheduler sinks every read to just before its use).
-    auto kread = [&](int ks) -> bf16x8 {
-      const uint8_t *kp = ks < KS_LAT ? slot + (kb ^ ((ks & 3) * 64)) + (ks >> 2) * 256
-                                      : slot + (krb ^ ((ks - KS_LAT) * 64));
+    // Operands stream through a ring PF k-steps deep so LDS latency overlaps
+    // earlier MFMAs; the empty asm ties each MFMA operand to its place in the
+    // ring (without it the scheduler sinks every read to just before its use).
+    auto kread = [&](int ks, int hi) -> bf16x8 {
+      const uint8_t *kp = ks < KLAT ? slot + (kb ^ ((ks & 3) * 64)) + (ks >> 2) * 256 + hi * 16 * LAT_BYTES
+                                    : slot + (krb ^ ((ks - KLAT) * 64)) + hi * 16 * ROPE_BYTES;
       return *reinterpret_cast<const bf16x8 *>(kp);
     };
-    constexpr int PF = 3;
-    bf16x8 kf[KS];
+    constexpr int PF = 1;
+    bf16x8 k0[KSTEPS], k1[KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < PF; ++ks) kf[ks] = kread(ks);
-    s = f32x16{};
+    for (int ks = 0; ks < PF; ++ks) {
+      k0[ks] = kread(ks, 0);
+      k1[ks] = kread(ks, 1);
+    }
+    s0 = f32x4{};
+    s1 = f32x4{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + PF < KS) kf[ks + PF] = kread(ks + PF);
-      asm volatile("" : "+v"(kf[ks]) : : "memory");
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (ks + PF < KSTEPS) {
+        k0[ks + PF] = kread(ks + PF, 0);
+        k1[ks + PF] = kread(ks + PF, 1);
+      }
+      asm volatile("" : "+v"(k0[ks]), "+v"(k1[ks]) : : "memory");
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[ks], qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[ks], qf[ks], s1, 0, 0, 0);
     }
 
-    uint8_t *mine = xch + wave * XCH_BYTES + x_off(l);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<f32x4 *>(mine + i * 1024) = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
-  }
-
-  // After the partner's partial is visible: full scores, online softmax and
-  // the value product for the block in `slot` (block index blk).
-  __device__ __forceinline__ void softmax_values(const uint8_t *slot, int blk) {
+    // ---- online softmax.  Scores stay unscaled: the scale c = softmax_scale *
+    // log2(e) > 0 enters the running max (max(c s) = c max(s)) and the exponent
+    // as one fma.
     const int tok0 = t_begin + blk * TB;
-    const int l = lane_id(), hb = l >> 5;
-    const int vb = v_base(l);
-    // Both waves of the pair hold S_own + S_partner: the same fp32 sums, as
-    // addition commutes.
-    const uint8_t *theirs = xch + (wave ^ 1) * XCH_BYTES + x_off(l);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 t = *reinterpret_cast<const f32x4 *>(theirs + i * 1024);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s[4 * i + e] += t[e];
-    }
-
-    // ---- online softmax: lane holds head l % 32 for tokens 8 (i / 4) + 4 hb + i % 4.
-    // Scores stay unscaled; the scale c = softmax_scale * log2(e) > 0 enters
-    // the running max (max(c s) = c max(s)) and the exponent as one fma.
     const float c = a.scale_log2;
     if (tok0 + TB > t_end) [[unlikely]] {
       // last block of the chunk: tokens at or past t_end do not exist
-      const int lim = t_end - tok0 - 4 * hb;
+      const int lim = t_end - tok0 - 4 * g;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if ((i >> 2) * 8 + (i & 3) >= lim) s[i] = -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        if (i >= lim) s0[i] = -INFINITY;
+        if (16 + i >= lim) s1[i] = -INFINITY;
+      }
     }
-    float mx = s[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = max_xor32(mx) * c;
+    float mx = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3]));
+    mx = fmaxf(mx, fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    mx = max_xor32(max_xor16(mx)) * c;
     const float m_new = fmaxf(m_run, mx);
-    if (__ballot(m_new > m_run + RESCALE_SLACK)) {
-      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int j = 0; j < CB; ++j) o[j] *= alpha;
+    float alpha = 1.0f;
+    if (m_new > m_run + RESCALE_SLACK) {
+      alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
       e_run *= alpha;
       m_run = m_new;
     }
-    // P as the MFMA B operand of token step t: k index 8 hb + j stands for
-    // token 16 t + 8 (j / 4) + 4 hb + j % 4, i.e. score register 8 t + j.
-    bf16x8 p[2];
+    bf16x4 p0, p1;
     float pe = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m_run));
-      pe += pf;
-      p[i >> 3][i & 7] = to_bf16(pf);
+    for (int i = 0; i < 4; ++i) {
+      const float f0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -m_run));
+      const float f1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -m_run));
+      pe += f0 + f1;
+      p0[i] = to_bf16(f0);
+      p1[i] = to_bf16(f1);
     }
     // sum of the rounded weights: bf16 pairs dotted with (1, 1)
-    float ps = l_run;
     const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16x2 pr = {p[i >> 2][2 * (i & 3)], p[i >> 2][2 * (i & 3) + 1]};
-      ps = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps, false);
-    }
+    float ps = l_run;
+    ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[0], p0[1]}, one2, ps, false);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2], p0[3]}, one2, ps, false);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[0], p1[1]}, one2, ps, false);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[2], p1[3]}, one2, ps, false);
     l_run = ps;
     e_run += pe;
 
-    // ---- O^T[col, head] += V^T[col, token] P^T[token, head] over this wave's
-    // 8 column blocks and the block's two 16-token steps.  A transposed read
-    // returns 4 consecutive tokens of one column per lane: "lo" covers tokens
-    // 16 t + 4 hb + [0, 4), "hi" the same 8 rows further.
+    // ---- publish.  P tile of the pair: quartet k = token / 4, 8 bytes per
+    // (quartet, pair head), P[token][head] at ((k * 32 + head) * 8 + 2 (token % 4)):
+    // 16 consecutive lanes write 16 consecutive 8-byte slots.  This lane holds
+    // quartets g (tokens 4 g + i) and 4 + g (tokens 16 + 4 g + i).
+    const int ph = half * 16 + (l & 15);
+    uint8_t *pw = px + (g * 32 + ph) * 8;
+    *reinterpret_cast<bf16x4 *>(pw) = p0;
+    *reinterpret_cast<bf16x4 *>(pw + 4 * 32 * 8) = p1;
+    if (g == 0) ax[ph] = alpha;
+  }
+
+  // After the pair's P is visible: rescale if any of the pair's heads moved
+  // its max, then the value product of the block in `slot`.
+  __device__ __forceinline__ void values(const uint8_t *slot) {
+    const int l = lane_id();
+    const int vb = v_base(l);
+    // B operand of token step t: lane (pair head l % 32, hb = l / 32) holds
+    // tokens 16 t + 8 hb + [0, 8): quartets 4 t + 2 hb and 4 t + 2 hb + 1.
+    auto pread = [&](int k) -> bf16x4 {
+      return *reinterpret_cast<const bf16x4 *>(px + (k * 32 + (l & 31)) * 8);
+    };
+    const int q0 = 2 * (l >> 5);
+    const bf16x4 p00 = pread(q0), p01 = pread(q0 + 1), p10 = pread(q0 + 4), p11 = pread(q0 + 5);
+    const bf16x8 pb0 = __builtin_shufflevector(p00, p01, 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x8 pb1 = __builtin_shufflevector(p10, p11, 0, 1, 2, 3, 4, 5, 6, 7);
+    const float alpha = ax[l & 31];
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int j = 0; j < CB; ++j) o[j] *= alpha;
+    }
+    // A operand: a transposed read returns 4 consecutive tokens of one column
+    // per lane: "lo" covers tokens 16 t + 8 hb + [0, 4), "hi" the next 4.
     auto vread = [&](int n) -> bf16x8 {
-      const int j = n >> 1, t = n & 1;
+      const int j = n & 7, t = n >> 3;
       const int x = vb ^ ((j & 3) * 64);
       const uint8_t *r0 = slot + x + (j >> 2) * 256 + t * 16 * LAT_BYTES;
-      const uint8_t *r1 = slot + (x ^ 32) + (j >> 2) * 256 + t * 16 * LAT_BYTES + 8 * LAT_BYTES;
+      const uint8_t *r1 = slot + (x ^ 32) + (j >> 2) * 256 + t * 16 * LAT_BYTES + 4 * LAT_BYTES;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)r0);
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)r1);
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    constexpr int PV = 2;
+    // n = 8 t + j: consecutive MFMAs go to different accumulators.
+    constexpr int PV = 3;
     constexpr int NV = 2 * CB;
     bf16x8 vf[NV];
 #pragma unroll
@@ -351,36 +386,46 @@ struct DecoderPair {
     for (int n = 0; n < NV; ++n) {
       if (n + PV < NV) vf[n + PV] = vread(n + PV);
       asm volatile("" : "+v"(vf[n]) : : "memory");
-      o[n >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[n], p[n & 1], o[n >> 1], 0, 0, 0);
+      o[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[n], n < 8 ? pb0 : pb1, o[n & 7], 0, 0, 0);
     }
   }
 
-  // Lane (head l % 32, hb) holds columns 32 (8 half + j) + 8 q + 4 hb + [0, 4)
-  // in registers 4 q .. 4 q + 3 of o[j].
+  // Normalise and store.  The scoring lanes publish 1 / l of their heads
+  // (to tiles of their own, as the partner wave may still be reading the
+  // rescale factors) and write lse; lane (pair head l % 32, hb) holds columns 32 (8 half + j) + 8 q +
+  // 4 hb + [0, 4) in registers 4 q .. 4 q + 3 of o[j].  Every wave of the
+  // workgroup calls this once (it contains a barrier).
   __device__ __forceinline__ void finish() {
-    const float l_tot = sum_xor32(l_run);
-    const float e_tot = sum_xor32(e_run);
+    const int l = threadIdx.x & 63;
+    const float l_tot = sum_xor32(sum_xor16(l_run));
+    const float e_tot = sum_xor32(sum_xor16(e_run));
     const float inv = 1.0f / l_tot;
     const float lse_v = (m_run + __log2f(e_tot)) * LN2;
-    const int l = threadIdx.x & 63, hb = l >> 5, head = head_of(l);
-    if (head >= a.H) return;
-    uint16_t *dst;
-    if (a.direct) {
-      dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC;
-      if (half == 0 && hb == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = lse_v;
-    } else {
-      const size_t row = (static_cast<size_t>(b) * a.n_splits + split) * a.H + head;
-      dst = a.o_part + row * DC;
-      if (half == 0 && hb == 0) a.lse_part[row] = lse_v;
+    const int sh = score_head(l);
+    if (l < 16) {
+      fx[half * 16 + l] = inv;
+      if (sh < a.H) {
+        if (a.direct) {
+          if (a.lse) a.lse[static_cast<size_t>(b) * a.H + sh] = lse_v;
+        } else {
+          a.lse_part[(static_cast<size_t>(b) * a.n_splits + split) * a.H + sh] = lse_v;
+        }
+      }
     }
-    dst += half * 256 + hb * 4;
+    barrier_lds();
+    const float scale = fx[l & 31];
+    const int head = pair_head(l);
+    if (head >= a.H) return;
+    uint16_t *dst = a.direct ? a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC
+                             : a.o_part + ((static_cast<size_t>(b) * a.n_splits + split) * a.H + head) * DC;
+    dst += half * 256 + (l >> 5) * 4;
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[j][4 * q + e] * inv);
+        for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[j][4 * q + e] * scale);
         *reinterpret_cast<bf16x4 *>(dst + j * 32 + q * 8) = v;
       }
     }
@@ -388,45 +433,48 @@ struct DecoderPair {
 };
 
 // Wait until this wave's copies of block i have landed (copies of the next
-// `ahead` blocks may still be in flight), then synchronise the workgroup.
+// `ahead` blocks may still be in flight).
 template <int NI, int AHEAD>
 __device__ __forceinline__ void wait_block(bool full_share) {
   if (full_share) wait_vmcnt<AHEAD * NI>();
   else wait_vmcnt<AHEAD * (NI - 1)>();
 }
 
-// Group X, block i in slot CUR: [wait copies of i] Ba [scores i] Bb [copy i + 2
-// into NXT] [softmax + values i].
+#define MLA_WAIT_BLOCK(i)                                              \
+  if ((i) + 2 < nblk) wait_block<D::NI, 2>(full_share);                \
+  else if ((i) + 1 < nblk) wait_block<D::NI, 1>(full_share);           \
+  else wait_vmcnt<0>();
+
+// Group X, block i in slot CUR (block i + 3 goes into NXT, the slot of block
+// i - 1): [wait copies of i] Ba [scores + softmax i] Bb [copy i + 3]
+// [values i].
 #define MLA_STEP_X(K, CUR, NXT)                                        \
   {                                                                    \
     const int i = blk + (K);                                           \
     if (i >= nblk) break;                                              \
-    const int phys = i + 2 < nblk ? dec.page_of(i + 2) : 0;            \
-    if (i + 1 < nblk) wait_block<D::NI, 1>(full_share);                \
-    else wait_vmcnt<0>();                                              \
+    const int phys = i + 3 < nblk ? dec.page_of(i + 3) : 0;            \
+    MLA_WAIT_BLOCK(i)                                                  \
     barrier_no_fence();                                                \
-    dec.scores(CUR);                                                   \
+    dec.scores_softmax(CUR, i);                                        \
     barrier_lds();                                                     \
-    if (i + 2 < nblk) dec.issue(i + 2, phys, NXT);                     \
-    dec.softmax_values(CUR, i);                                        \
+    if (i + 3 < nblk) dec.issue(i + 3, phys, NXT);                     \
+    dec.values(CUR);                                                   \
   }
 
 // Group Y, block i >= 1 in slot CUR (block i - 1 in PRV, which is also the
-// slot block i + 2 is copied into): [wait copies of i] Ba [softmax + values
-// i - 1] Bb [copy i + 2 into PRV] [scores i].  Ba publishes Y's partials of
-// i - 1.
+// slot block i + 3 is copied into): [wait copies of i] Ba [values i - 1] Bb
+// [copy i + 3 into PRV] [scores + softmax i].  Ba publishes Y's P of i - 1.
 #define MLA_STEP_Y(K, CUR, PRV)                                        \
   {                                                                    \
     const int i = blk + (K);                                           \
     if (i >= nblk) break;                                              \
-    const int phys = i + 2 < nblk ? dec.page_of(i + 2) : 0;            \
-    if (i + 1 < nblk) wait_block<D::NI, 1>(full_share);                \
-    else wait_vmcnt<0>();                                              \
+    const int phys = i + 3 < nblk ? dec.page_of(i + 3) : 0;            \
+    MLA_WAIT_BLOCK(i)                                                  \
     barrier_lds();                                                     \
-    dec.softmax_values(PRV, i - 1);                                    \
+    dec.values(PRV);                                                   \
     barrier_no_fence();                                                \
-    if (i + 2 < nblk) dec.issue(i + 2, phys, PRV);                     \
-    dec.scores(CUR);                                                   \
+    if (i + 3 < nblk) dec.issue(i + 3, phys, PRV);                     \
+    dec.scores_softmax(CUR, i);                                        \
   }
 
 template <class D, int WAVES_PER_EU>
@@ -436,7 +484,10 @@ void decode_bf16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t slot0[SLOT_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slot1[SLOT_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t slot2[SLOT_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t xch[D::NW * XCH_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t slot3[SLOT_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t px[D::NW / 2 * PX_BYTES];
+  __shared__ __attribute__((aligned(16))) float ax[D::NW / 2 * 32];
+  __shared__ __attribute__((aligned(16))) float fx[D::NW / 2 * 32];
   constexpr int NW = D::NW;
 
   // Chunk placement: workgroups are dealt to the 8 XCDs round-robin by id, so
@@ -468,49 +519,54 @@ void decode_bf16_kernel(DecodeArgs a) {
 
   // Page ids are read with scalar loads (the streaming loop's only vector
   // memory operations are its DMA copies, so vmcnt counts exactly those).
-  D dec(a, xch, b, split, t_begin, t_end);
+  D dec(a, px, ax, fx, b, split, t_begin, t_end);
   dec.begin();
-  dec.load_q();
-  wait_vmcnt<0>();            // query fragments landed before any copy is queued
-  const bool full_share = dec.copies() == D::NI;
-
   const int nblk = (t_end - t_begin + TB - 1) / TB;
+  // First copies go out before the query loads so the two latencies overlap.
   dec.issue(0, dec.page_of(0), slot0);
   if (nblk > 1) dec.issue(1, dec.page_of(1), slot1);
+  if (nblk > 2) dec.issue(2, dec.page_of(2), slot2);
+  dec.load_q();
+  wait_vmcnt<0>();            // query fragments (and the first copies) landed
+  const bool full_share = dec.copies() == D::NI;
 
-  // Slot of block i: i % 3.  A slot is rewritten (block i + 3) only after the
-  // second barrier of block i + 1, when both groups are done with block i.
+  // Slot of block i: i % 4.  The slot of block i - 1 is rewritten (block
+  // i + 3) only after the second barrier of block i, when both groups are
+  // done with block i - 1.
   const bool group_y = NW == 8 && (threadIdx.x >> 8) != 0;
   if (!group_y) {
-    for (int blk = 0; blk < nblk; blk += 3) {
-      MLA_STEP_X(0, slot0, slot2)
+    for (int blk = 0; blk < nblk; blk += 4) {
+      MLA_STEP_X(0, slot0, slot3)
       MLA_STEP_X(1, slot1, slot0)
       MLA_STEP_X(2, slot2, slot1)
+      MLA_STEP_X(3, slot3, slot2)
     }
-    barrier_no_fence();       // Y publishes its partials of the last block
+    barrier_no_fence();       // Y publishes its P of the last block
   } else {
     // block 0: nothing of Y's to finish yet
-    if (nblk > 1) wait_block<D::NI, 1>(full_share);
-    else wait_vmcnt<0>();
-    const int phys = nblk > 2 ? dec.page_of(2) : 0;
-    barrier_lds();
-    barrier_no_fence();
-    if (nblk > 2) dec.issue(2, phys, slot2);
-    dec.scores(slot0);
-    for (int blk = 1; blk < nblk; blk += 3) {
+    {
+      const int phys = nblk > 3 ? dec.page_of(3) : 0;
+      barrier_lds();
+      barrier_no_fence();
+      if (nblk > 3) dec.issue(3, phys, slot3);
+      dec.scores_softmax(slot0, 0);
+    }
+    for (int blk = 1; blk < nblk; blk += 4) {
       MLA_STEP_Y(0, slot1, slot0)
       MLA_STEP_Y(1, slot2, slot1)
-      MLA_STEP_Y(2, slot0, slot2)
+      MLA_STEP_Y(2, slot3, slot2)
+      MLA_STEP_Y(3, slot0, slot3)
     }
     barrier_lds();
-    const int last = nblk - 1;
-    dec.softmax_values(last % 3 == 0 ? slot0 : (last % 3 == 1 ? slot1 : slot2), last);
+    const int last = (nblk - 1) & 3;
+    dec.values(last == 0 ? slot0 : (last == 1 ? slot1 : (last == 2 ? slot2 : slot3)));
   }
   dec.finish();
 }
 
 #undef MLA_STEP_X
 #undef MLA_STEP_Y
+#undef MLA_WAIT_BLOCK
 
 // Merge split-KV partials: o = sum_c w_c o_c / sum_c w_c, w_c = exp(lse_c - L).
 // One 64-lane group per (sequence, head), 8 columns per lane.
