@@ -102,7 +102,8 @@ __device__ __forceinline__ float sum_xor32(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The copy (DMA) side of a decoder: which rows of a block each wave moves.
+// The copy (DMA) side of a decoder: which rows of a block each of the NW
+// copying waves moves.
 template <int NW>
 struct BlockCopier {
   static constexpr int NI = (NDMA + NW - 1) / NW;       // max DMA copies per wave per block
@@ -152,7 +153,11 @@ template <int NW_>
 struct DecoderPair {
   static constexpr int NW = NW_;
   static constexpr int HEADS = NW * 16;          // heads per workgroup
-  static constexpr int NI = BlockCopier<NW>::NI;
+  // Copying waves.  A global->LDS copy stalls at issue while the memory pipe
+  // is full, and a stalled wave issues no MFMAs; with 8 waves only group X
+  // (which otherwise waits for group Y at the first barrier) copies.
+  static constexpr int NC = NW == 8 ? 4 : NW;
+  static constexpr int NI = BlockCopier<NC>::NI;
 
   const DecodeArgs &a;
   const int wave, half;                          // wave-uniform
@@ -244,7 +249,7 @@ struct DecoderPair {
     }
   }
 
-  __device__ __forceinline__ int copies() const { return BlockCopier<NW>::copies(wave); }
+  __device__ __forceinline__ int copies() const { return wave < NC ? BlockCopier<NC>::copies(wave) : 0; }
 
   // Physical page of block blk: a scalar load from the block table, issued a
   // step before the copy that needs it so its latency stays off the LDS path.
@@ -254,7 +259,7 @@ struct DecoderPair {
 
   __device__ __forceinline__ void issue(int blk, int phys, uint8_t *slot) {
     const int tok0 = t_begin + blk * TB;
-    BlockCopier<NW>::issue(a.cache, phys, tok0, min(TB, t_end - tok0) - 1, wave, threadIdx.x & 63, slot);
+    if (wave < NC) BlockCopier<NC>::issue(a.cache, phys, tok0, min(TB, t_end - tok0) - 1, wave, threadIdx.x & 63, slot);
   }
 
   // Scores of this wave's 16 heads for the block in `slot`, online softmax,
@@ -392,10 +397,14 @@ struct DecoderPair {
 
   // Normalise and store.  The scoring lanes publish 1 / l of their heads
   // (to tiles of their own, as the partner wave may still be reading the
-  // rescale factors) and write lse; lane (pair head l % 32, hb) holds columns 32 (8 half + j) + 8 q +
-  // 4 hb + [0, 4) in registers 4 q .. 4 q + 3 of o[j].  Every wave of the
-  // workgroup calls this once (it contains a barrier).
-  __device__ __forceinline__ void finish() {
+  // rescale factors) and write lse.  Lane (pair head l % 32, hb) holds
+  // columns 32 (8 half + j) + 8 q + 4 hb + [0, 4) in registers 4 q .. 4 q + 3
+  // of o[j]: stored directly, every instruction would scatter 16-byte pieces
+  // over 32 rows.  The tile goes through LDS instead (`stage`, the free slot
+  // ring: row = head of the workgroup, 1 KB, chunk c at position c ^ (row &
+  // 15)), and each wave then writes 16 whole rows, 1 KB per instruction.
+  // Every wave of the workgroup calls this once (it contains barriers).
+  __device__ __forceinline__ void finish(uint8_t *stage) {
     const int l = threadIdx.x & 63;
     const float l_tot = sum_xor32(sum_xor16(l_run));
     const float e_tot = sum_xor32(sum_xor16(e_run));
@@ -412,13 +421,10 @@ struct DecoderPair {
         }
       }
     }
-    barrier_lds();
+    barrier_lds();            // 1 / l visible; every wave is done with the slots
     const float scale = fx[l & 31];
-    const int head = pair_head(l);
-    if (head >= a.H) return;
-    uint16_t *dst = a.direct ? a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC
-                             : a.o_part + ((static_cast<size_t>(b) * a.n_splits + split) * a.H + head) * DC;
-    dst += half * 256 + (l >> 5) * 4;
+    const int row = (wave >> 1) * 32 + (l & 31);
+    uint8_t *srow = stage + row * LAT_BYTES + (l >> 5) * 8;
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
 #pragma unroll
@@ -426,7 +432,20 @@ struct DecoderPair {
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[j][4 * q + e] * scale);
-        *reinterpret_cast<bf16x4 *>(dst + j * 32 + q * 8) = v;
+        const int c = half * 32 + j * 4 + q;                  // 16-byte chunk of the row
+        *reinterpret_cast<bf16x4 *>(srow + ((c ^ (row & 15)) << 4)) = v;
+      }
+    }
+    barrier_lds();
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+      const int r = wave * 16 + k;
+      const int head = blockIdx.y * HEADS + r;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * LAT_BYTES + ((l ^ (r & 15)) << 4));
+      if (head < a.H) {
+        uint16_t *dst = a.direct ? a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC
+                                 : a.o_part + ((static_cast<size_t>(b) * a.n_splits + split) * a.H + head) * DC;
+        *reinterpret_cast<u32x4 *>(dst + l * 8) = v;
       }
     }
   }
@@ -481,10 +500,10 @@ template <class D, int WAVES_PER_EU>
 __global__ __attribute__((amdgpu_flat_work_group_size(D::NW * 64, D::NW * 64),
                           amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void decode_bf16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t slot0[SLOT_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t slot1[SLOT_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t slot2[SLOT_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t slot3[SLOT_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT * SLOT_BYTES];
+  uint8_t *const slot0 = ring, *const slot1 = ring + SLOT_BYTES, *const slot2 = ring + 2 * SLOT_BYTES,
+                 *const slot3 = ring + 3 * SLOT_BYTES;
+  static_assert(D::HEADS * LAT_BYTES <= NSLOT * SLOT_BYTES, "the output tile is staged in the slot ring");
   __shared__ __attribute__((aligned(16))) uint8_t px[D::NW / 2 * PX_BYTES];
   __shared__ __attribute__((aligned(16))) float ax[D::NW / 2 * 32];
   __shared__ __attribute__((aligned(16))) float fx[D::NW / 2 * 32];
@@ -561,7 +580,7 @@ void decode_bf16_kernel(DecodeArgs a) {
     const int last = (nblk - 1) & 3;
     dec.values(last == 0 ? slot0 : (last == 1 ? slot1 : (last == 2 ? slot2 : slot3)));
   }
-  dec.finish();
+  dec.finish(ring);
 }
 
 #undef MLA_STEP_X
