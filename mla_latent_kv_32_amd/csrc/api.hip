@@ -5,6 +5,8 @@
 #include <stdint.h>
 
 #include "mla.h"
+
+#include <cmath>
 #include "common.h"
 #include "kernels.h"
 
@@ -96,7 +98,8 @@ int mla_rope_append_cache(const void *q_pe, const void *kv_new, const int32_t *s
   a.max_blocks = max_blocks_per_seq;
   a.cache = static_cast<uint8_t *>(kv_cache);
   a.kv_fp8 = kv_dtype == MLA_KV_FP8_E4M3;
-  a.theta = static_cast<double>(rope_theta);
+  for (int i = 0; i < MLA_D_R / 2; ++i)
+    a.inv_freq[i] = std::pow(static_cast<double>(rope_theta), -(2.0 * i) / static_cast<double>(MLA_D_R));
   a.q = static_cast<uint16_t *>(q);
   a.B = B;
   a.H = H;

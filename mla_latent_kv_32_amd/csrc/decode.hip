@@ -587,8 +587,10 @@ void decode_bf16_kernel(DecodeArgs a) {
 #undef MLA_STEP_Y
 #undef MLA_WAIT_BLOCK
 
-// Merge split-KV partials: o = sum_c w_c o_c / sum_c w_c, w_c = exp(lse_c - L).
-// One 64-lane group per (sequence, head), 8 columns per lane.
+// Merge split-KV partials: o = sum_c w_c o_c / sum_c w_c, w_c = exp(lse_c - L),
+// L = max_c lse_c.  One 64-lane group per (sequence, head), 8 columns per
+// lane; the chunks' lse are reduced across the lanes first, then the partial
+// rows stream in groups of 8 so that 8 loads per lane are in flight.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int b = blockIdx.x;
   const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -605,18 +607,34 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const size_t stride = static_cast<size_t>(a.H);
   const float *lp = a.lse_part + static_cast<size_t>(b) * a.n_splits * stride + head;
   float L = -INFINITY;
-  for (int c = 0; c < nv; ++c) L = fmaxf(L, lp[c * stride]);
+  for (int c = t; c < nv; c += 64) L = fmaxf(L, lp[c * stride]);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) L = fmaxf(L, __shfl_xor(L, m));
   float acc[8] = {};
   float z = 0.f;
   const uint16_t *op = a.o_part + (static_cast<size_t>(b) * a.n_splits * stride + head) * DC + t * 8;
-  for (int c = 0; c < nv; ++c) {
-    const float w = expf(lp[c * stride] - L);
-    z += w;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(op + c * stride * DC);
+  for (int c0 = 0; c0 < nv; c0 += 8) {
+    u32x4 v[8];
+    float w[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += w * __uint_as_float(v[e] << 16);
-      acc[2 * e + 1] += w * __uint_as_float(v[e] & 0xFFFF0000u);
+    for (int k = 0; k < 8; ++k) {
+      const int c = c0 + k;
+      if (c < nv) {
+        v[k] = *reinterpret_cast<const u32x4 *>(op + c * stride * DC);
+        w[k] = expf(lp[c * stride] - L);
+      } else {
+        v[k] = u32x4{0, 0, 0, 0};
+        w[k] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      z += w[k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += w[k] * __uint_as_float(v[k][e] << 16);
+        acc[2 * e + 1] += w[k] * __uint_as_float(v[k][e] & 0xFFFF0000u);
+      }
     }
   }
   const float inv = 1.0f / z;

@@ -57,7 +57,7 @@ struct RopeAppendArgs {
   int max_blocks;
   uint8_t *cache;
   int kv_fp8;
-  double theta;
+  double inv_freq[32];          // theta^(-2i/64), i = 0..31, formed on the host in float64
   uint16_t *q;                  // [B, H, 576]
   int B, H;
 };

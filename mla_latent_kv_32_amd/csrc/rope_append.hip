@@ -7,8 +7,8 @@
 // decoupled RoPE paragraph).  Pairs are interleaved (v[2i], v[2i+1]) with
 // frequency theta^(-2i/64) (Riju, "Multi-Head Latent Attention vs GQA vs MQA",
 // rope function in "A latent KV projection in PyTorch").  Angles are formed
-// and reduced in float64 (positions reach 32K and beyond), the rotation runs
-// in float32, results round to bf16.
+// and reduced in float64 (positions reach 32K and beyond; the 32 frequencies
+// come from the host), the rotation runs in float32, results round to bf16.
 //
 // fp8 caches store the latent as OCP E4M3 codes with one fp32 scale per group
 // of 128: scale = amax/448 (IEEE float32 division), code = round-to-nearest-
@@ -51,9 +51,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendArgs a) {
   const int S = a.seq_lens[b];
   const int pos = S > 0 ? S - 1 : 0;
   if (tid < DR / 2) {
-    const double inv = pow(a.theta, -(2.0 * tid) / static_cast<double>(DR));
     double sv, cv;
-    sincos(static_cast<double>(pos) * inv, &sv, &cv);
+    sincos(static_cast<double>(pos) * a.inv_freq[tid], &sv, &cv);
     cs[tid] = static_cast<float>(cv);
     sn[tid] = static_cast<float>(sv);
   }
