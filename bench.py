@@ -40,6 +40,25 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROW_BYTES = 576 * 2
 COPIES = 3
 
+# HBM bytes the decode kernel moves per launch on this workload, from two
+# rocprofv3 --pmc passes over this benchmark (FETCH_SIZE, then WRITE_SIZE, KiB
+# per dispatch, averaged over the decode dispatches), each scaled by what the
+# same counter reads for a plain 512 MiB device copy (`--copy-calibration`):
+# FETCH_SIZE reports half of the bytes read (x2.0), WRITE_SIZE all of them
+# (x1.0).  The figure belongs to the decode source it was measured on and is
+# reported only while that source is unchanged.
+DECODE_TRAFFIC = {
+    "sources_sha256": {
+        "mla_latent_kv_32_amd/csrc/decode.hip": "62d48bc9b2ccaebce8212e41194253a396337a3baac698e3c816201eaf557724",
+        "mla_latent_kv_32_amd/csrc/common.h": "ab381b81c10ae7b628a24624be42a9c4c2714b9b2e3b82c2038876b6e1f6e82d",
+    },
+    "fetch_kib": 76362.9,
+    "write_kib": 32896.0,
+    "fetch_scale": 2.0,
+    "write_scale": 1.0,
+    "profile": "profiles/decode_bf16_B32_H128_ctx4096_hbm_counters.md",
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -65,6 +84,17 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
+
+
+def decode_traffic_bytes():
+    """HBM bytes per decode launch from the recorded counters, or None if the source changed."""
+    import hashlib
+    for rel, digest in DECODE_TRAFFIC["sources_sha256"].items():
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    t = DECODE_TRAFFIC
+    return round((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024)
 
 
 def cpu_baseline(w, budget_s):
@@ -270,7 +300,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": decode_traffic_bytes(),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes": cache_bytes,
         },
         "parity": parity,
     }
