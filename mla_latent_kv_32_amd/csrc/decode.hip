@@ -541,12 +541,15 @@ void decode_bf16_kernel(DecodeArgs a) {
   D dec(a, px, ax, fx, b, split, t_begin, t_end);
   dec.begin();
   const int nblk = (t_end - t_begin + TB - 1) / TB;
-  // First copies go out before the query loads so the two latencies overlap.
+  // Block 0's copies go out before the query loads so the two latencies
+  // overlap; both are waited for here (the compiler, which does not see the
+  // copies, would otherwise wait for everything at the first use of the
+  // query), and blocks 1 and 2 follow, to land while block 0 is computed.
   dec.issue(0, dec.page_of(0), slot0);
+  dec.load_q();
+  wait_vmcnt<0>();
   if (nblk > 1) dec.issue(1, dec.page_of(1), slot1);
   if (nblk > 2) dec.issue(2, dec.page_of(2), slot2);
-  dec.load_q();
-  wait_vmcnt<0>();            // query fragments (and the first copies) landed
   const bool full_share = dec.copies() == D::NI;
 
   // Slot of block i: i % 4.  The slot of block i - 1 is rewritten (block
