@@ -6,10 +6,12 @@ Workload: one decode step of a DeepSeek-V3-shaped MLA layer, B = 32 sequences
 of 4096 cached tokens, H = 128 heads, bf16 paged latent cache (64-token pages
 in a random permutation), inputs from the seeded generator (synth.workload(2)).
 A step is the whole hot path through the C ABI:
-  mla_absorb_q -> mla_rope_append_cache -> mla_decode_partial -> mla_decode_combine
-  -> mla_absorb_out
-(partial + combine are exactly mla_decode_paged split in two, so the decode
-kernel can be timed on its own with HIP events on the launch stream).
+  mla_absorb_q -> mla_rope_append_cache -> mla_decode_partial
+  -> mla_decode_combine_absorb_out
+(partial + combine are mla_decode_paged split in two, so the decode kernel can
+be timed on its own with HIP events on the launch stream; the combine is fused
+with the value absorption, whose results equal mla_decode_combine followed by
+mla_absorb_out).
 
 Keeping reads honest: three copies of the latent cache (3 x 151 MB) and of the
 absorption weights rotate from step to step, so each step streams a cache that
@@ -161,8 +163,6 @@ def main():
     split = args.split_tokens or mla.mla_decode_split_tokens(B, H, S)
     ws = torch.empty(mla.mla_decode_workspace_bytes(B, H, S, split), dtype=torch.uint8, device=dev)
     q = torch.empty((B, H, 576), dtype=torch.bfloat16, device=dev)
-    o_lat = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     o = torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -179,12 +179,9 @@ def main():
         mla.mla_decode_partial(q, caches[c], mla.KV_BF16, bt, sl, S, w["scale"], ws, split_tokens=split)
         if ev is not None:
             ev[3].record(stream)
-        mla.mla_decode_combine(ws, sl, S, o_lat, lse, split_tokens=split)
+        mla.mla_decode_combine_absorb_out(ws, sl, S, w_uvs[c], o, split_tokens=split)
         if ev is not None:
             ev[4].record(stream)
-        mla.mla_absorb_out(o_lat, w_uvs[c], o)
-        if ev is not None:
-            ev[5].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -226,19 +223,19 @@ def main():
     # ---- per-kernel durations: the same steps launched eagerly behind a GPU
     # sleep, so every launch is queued before the GPU reaches it and the HIP
     # events on the launch stream bracket kernel time only.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     torch.cuda._sleep(200_000_000)      # long enough for every launch below to be queued first
     for i in range(args.steps):
         step(i, events[i])
     torch.cuda.synchronize()
-    names = ["absorb_q", "rope_append", "decode", "combine", "absorb_out"]
+    names = ["absorb_q", "rope_append", "decode", "combine_absorb_out"]
     per = {n: [] for n in names}
     for ev in events:
         for k, n in enumerate(names):
             per[n].append(ev[k].elapsed_time(ev[k + 1]) * 1e3)     # us
     avg_us = {n: float(np.mean(v)) for n, v in per.items()}
-    eager_step_us = float(np.mean([ev[0].elapsed_time(ev[5]) * 1e3 for ev in events]))
+    eager_step_us = float(np.mean([ev[0].elapsed_time(ev[4]) * 1e3 for ev in events]))
 
     cache_bytes = B * S * ROW_BYTES                    # algorithmic: every cached row read once
     flops = 2.0 * B * H * S * (576 + 512)
@@ -247,7 +244,7 @@ def main():
     dec_s = avg_us["decode"] * 1e-6
     achieved = cache_bytes / dec_s / 1e9
 
-    # parity of the benchmarked buffers (last step wrote o, o_lat, lse; q holds this step's query)
+    # parity of the benchmarked output (the last step wrote o)
     parity = None
     try:
         import oracle

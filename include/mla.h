@@ -203,6 +203,26 @@ int mla_decode_combine(const void *workspace, size_t workspace_bytes, const int3
 int mla_absorb_out(const void *o_latent, const void *w_uv, void *o,
                    int B, int H, int d_c, int d_v, void *stream);
 
+/*
+ * mla_decode_combine followed by mla_absorb_out in one launch: the chunk
+ * merge of the log-sum-exp combine feeds the value up-projection directly,
+ * so the merged latent output need not go through memory (Su, eq:mla-mqa
+ * first line; Riju, "Inside MLA: Absorption").  Results are those of the two
+ * separate calls.
+ *   workspace, workspace_bytes, seq_lens, max_seq_len, split_tokens
+ *            as for mla_decode_combine (split_tokens = the partial call's)
+ *   w_uv     [H, 512, 128] bf16
+ *   o        [B, H, 128] bf16 output
+ *   o_latent [B, H, 512] bf16 merged latent output, or NULL to skip it
+ *   lse      [B, H] fp32 output, or NULL
+ * Requires d_c == 512, d_v == 128, H <= 65535.  An empty sequence gives
+ * o = 0 (and o_latent = 0, lse = -inf).
+ */
+int mla_decode_combine_absorb_out(const void *workspace, size_t workspace_bytes,
+                                  const int32_t *seq_lens, int max_seq_len, int split_tokens,
+                                  const void *w_uv, void *o, void *o_latent, float *lse,
+                                  int B, int H, int d_c, int d_v, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,7 @@ __all__ = [
     "FP8_ROW_BYTES", "library_path", "lib", "abi_version",
     "mla_absorb_q", "mla_rope_append_cache", "mla_decode_paged", "mla_absorb_out",
     "mla_decode_workspace_bytes", "mla_decode_split_tokens", "mla_decode_partial", "mla_decode_combine",
+    "mla_decode_combine_absorb_out",
 ]
 
 KV_BF16 = 0
@@ -80,6 +81,9 @@ def lib():
     L.mla_decode_combine.restype = c_int
     L.mla_absorb_out.argtypes = [vp, vp, vp, c_int, c_int, c_int, c_int, vp]
     L.mla_absorb_out.restype = c_int
+    L.mla_decode_combine_absorb_out.argtypes = [vp, c_size, i32p, c_int, c_int, vp, vp, vp, vp, c_int, c_int,
+                                                c_int, c_int, vp]
+    L.mla_decode_combine_absorb_out.restype = c_int
     _LIB = L
     return L
 
@@ -206,3 +210,22 @@ def mla_absorb_out(o_latent, w_uv, o, stream=None):
         _dense(t, n, torch.bfloat16)
     _check("mla_absorb_out", lib().mla_absorb_out(_ptr(o_latent), _ptr(w_uv), _ptr(o), B, H, dc,
                                                   w_uv.shape[2], _stream(stream)))
+
+
+def mla_decode_combine_absorb_out(workspace, seq_lens, max_seq_len, w_uv, o, o_latent=None, lse=None,
+                                  split_tokens=0, stream=None):
+    """Merge the workspace partials and apply W_UV in one launch: o [B,H,128] bf16
+    (optionally also o_latent [B,H,512] bf16 and lse [B,H] fp32)."""
+    B, H, dv = o.shape
+    _dense(workspace, "workspace")
+    _dense(seq_lens, "seq_lens", torch.int32)
+    _dense(w_uv, "w_uv", torch.bfloat16)
+    _dense(o, "o", torch.bfloat16)
+    if o_latent is not None:
+        _dense(o_latent, "o_latent", torch.bfloat16)
+    if lse is not None:
+        _dense(lse, "lse", torch.float32)
+    _check("mla_decode_combine_absorb_out", lib().mla_decode_combine_absorb_out(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(seq_lens), int(max_seq_len),
+        int(split_tokens), _ptr(w_uv), _ptr(o), _ptr(o_latent), _ptr(lse), B, H, w_uv.shape[1], dv,
+        _stream(stream)))

@@ -17,6 +17,8 @@
 // v_mfma_f32_32x32x16_bf16, taking the activations (A, K-contiguous) straight
 // from global memory and the weight operand (B, K-strided) from LDS with the
 // transposed read ds_read_b64_tr_b16.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -100,7 +102,190 @@ __global__ __launch_bounds__(NT * 2) void absorb_kernel(const uint16_t *act, con
   }
 }
 
+// Split-KV merge fused with the value up-projection.  Each workgroup owns one
+// head h and keeps W_UV[h] (512 x 128 bf16, 128 KB) in LDS; the batch is cut
+// into tiles of 16 sequences, and the tiles of a head are dealt out to
+// COMBINE_TILE_SLOTS(B) workgroups (two for 17..32 sequences, so a 32-sequence
+// batch fills 256 compute units).  Workgroups that share a head are numbered
+// so that they run on the same XCD and the second W_UV read can hit its L2.
+//
+// Merge: wave w builds tile rows w and w + 8.  Lanes 32 j .. 32 j + 31 hold
+// row j's chunk log-sum-exps (one pass for up to 32 chunks, loaded together
+// with the sequence lengths), the row maximum is a 32-lane shuffle reduction,
+// and the weights reach the accumulation as wave-uniform values; all partial
+// rows of a batch of 16 chunks are loaded together.  Each row sums its chunks
+// in chunk order with the arithmetic of combine_kernel, so o_latent and lse
+// equal the separate merge bit for bit.  The merged bf16 rows go to an LDS
+// tile (16-byte chunk c of row r at position c ^ (r & 15)) whose rows 16..31
+// stay zero, and waves 0-3 multiply it by W_UV[h] with 32x32x16 MFMAs, 32
+// output columns each (rows 16..31 of the product are discarded).
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void combine_absorb_out_kernel(CombineOutArgs a) {
+  constexpr int K = DC, N = DV, NT = 128;
+  constexpr int NWAVE = 8, ROWS = 16, RPW = ROWS / NWAVE;   // 2 tile rows per wave
+  constexpr int LPR = 64 / RPW;                             // 32 lanes per row in the lse phase
+  constexpr int VB = 16;                                    // chunks per load batch
+  constexpr int CPR = NT * 2 / 16;                          // 16-byte chunks per W row
+  constexpr int PER_WAVE = K * CPR / (64 * NWAVE);          // 16 DMA copies per wave
+  __shared__ __attribute__((aligned(16))) uint8_t wt[K * NT * 2];     // 128 KB
+  __shared__ __attribute__((aligned(16))) uint8_t at[32 * DC * 2];    //  32 KB
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slots = a.tile_slots;
+  const int G = gridDim.x;
+  const int L = blockIdx.x;
+  const int item = (G & 7) == 0 ? (L & 7) * (G >> 3) + (L >> 3) : L;
+  const int h = item / slots, slot = item % slots;
+
+  // ---- W_UV[h] -> LDS (row k, position p <- chunk p ^ wsw(k) of the row)
+  const uint8_t *wg = reinterpret_cast<const uint8_t *>(a.w_uv + static_cast<size_t>(h) * K * N);
+  const uint32_t wt_lds = lds_addr(wt);
+#pragma unroll 4
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int base = (wave * PER_WAVE + i) * 64;
+    const int p = base + lane;
+    const int k = p / CPR;
+    const int c = (p % CPR) ^ wsw<NT>(k);
+    dma16(wg + static_cast<size_t>(k) * N * 2 + c * 16, __builtin_amdgcn_readfirstlane(wt_lds + base * 16));
+  }
+  // rows 16..31 of the A tile: zero for the whole kernel
+  reinterpret_cast<u32x4 *>(at + ROWS * DC * 2)[threadIdx.x] = u32x4{0, 0, 0, 0};
+  reinterpret_cast<u32x4 *>(at + ROWS * DC * 2)[threadIdx.x + 512] = u32x4{0, 0, 0, 0};
+
+  // transposed B reads (waves 0-3), as in absorb_kernel
+  const int g = lane >> 4, q = lane & 15;
+  const int krow = 8 * (g >> 1) + (q >> 2);
+  const int chunk = 4 * (wave & 3) + 2 * (g & 1) + ((q & 3) >> 1);
+  const int boff0 = krow * (NT * 2) + ((chunk ^ wsw<NT>(krow)) << 4) + (q & 1) * 8;
+  const int boff1 = (krow + 4) * (NT * 2) + ((chunk ^ wsw<NT>(krow + 4)) << 4) + (q & 1) * 8;
+  const int r = lane & 31, hl = lane >> 5;
+  const size_t stride = static_cast<size_t>(a.H);
+  const int jl = lane / LPR, kl = lane % LPR;   // lse phase: row jl of this wave, chunk slot kl
+  bool first = true;
+
+  for (int b0 = slot * ROWS; b0 < a.B; b0 += slots * ROWS) {
+    // ---- chunk counts and row maxima, lane-parallel.  The first LPR chunk
+    // lse values are loaded alongside the sequence lengths (every chunk slot
+    // below n_splits lies inside the workspace) and masked afterwards.
+    const int bl = b0 + wave + NWAVE * jl;
+    const float *lp_l = a.lse_part + static_cast<size_t>(bl < a.B ? bl : 0) * a.n_splits * stride + h;
+    const float l0 = kl < a.n_splits ? lp_l[kl * stride] : -INFINITY;
+    int nv_l = 0;
+    if (bl < a.B) nv_l = max(0, (a.seq_lens[bl] + a.split_tokens - 1) / a.split_tokens);
+    float mx = kl < nv_l ? l0 : -INFINITY;
+    for (int c = kl + LPR; c < nv_l; c += LPR) mx = fmaxf(mx, lp_l[c * stride]);
+#pragma unroll
+    for (int sh = 1; sh < LPR; sh <<= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+    int nv[RPW];
+    float Lm[RPW];
+    const uint16_t *op[RPW];
+    int ncmax = 0;
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      nv[j] = __builtin_amdgcn_readlane(nv_l, LPR * j);
+      Lm[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), LPR * j));
+      ncmax = max(ncmax, nv[j]);
+      const int b = b0 + wave + NWAVE * j;
+      op[j] = a.o_part + (static_cast<size_t>(b < a.B ? b : 0) * a.n_splits * stride + h) * DC + lane * 8;
+    }
+
+    // ---- weighted sums, VB chunks of every row per batch
+    float acc[RPW][8] = {};
+    float z[RPW] = {};
+    for (int cb = 0; cb < ncmax; cb += LPR) {
+      // lane LPR j + k: weight of chunk cb + k of row j
+      float w_l = 0.f;
+      if (cb + kl < nv_l) w_l = expf((cb == 0 ? l0 : lp_l[(cb + kl) * stride]) - mx);
+#pragma unroll
+      for (int part = 0; part < LPR; part += VB) {
+        const int c0 = cb + part;
+        if (c0 >= ncmax) break;
+        u32x4 v[RPW][VB];
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+#pragma unroll
+          for (int k = 0; k < VB; ++k) {
+            if (c0 + k < nv[j]) v[j][k] = *reinterpret_cast<const u32x4 *>(op[j] + (c0 + k) * stride * DC);
+            else v[j][k] = u32x4{0, 0, 0, 0};
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+#pragma unroll
+          for (int k = 0; k < VB; ++k) {
+            const float wk = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), LPR * j + part + k));
+            z[j] += wk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[j][2 * e] += wk * __uint_as_float(v[j][k][e] << 16);
+              acc[j][2 * e + 1] += wk * __uint_as_float(v[j][k][e] & 0xFFFF0000u);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int row = wave + NWAVE * j;
+      const int b = b0 + row;
+      bf16x8 out = {};
+      if (nv[j] > 0) {
+        const float inv = 1.0f / z[j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = to_bf16(acc[j][e] * inv);
+      }
+      if (b < a.B) {
+        if (lane == 0 && a.lse)
+          a.lse[static_cast<size_t>(b) * a.H + h] = nv[j] > 0 ? Lm[j] + logf(z[j]) : -INFINITY;
+        if (a.o_latent)
+          *reinterpret_cast<bf16x8 *>(a.o_latent + (static_cast<size_t>(b) * a.H + h) * DC + lane * 8) = out;
+      }
+      *reinterpret_cast<bf16x8 *>(at + row * DC * 2 + ((lane ^ (row & 15)) << 4)) = out;
+    }
+    if (first) wait_vmcnt<0>();         // this wave's W tile copies landed
+    first = false;
+    __syncthreads();
+
+    // ---- o[b0 + row, h, 32 wave + r] = tile[row, :] . W_UV[h][:, 32 wave + r]
+    if (wave < 4) {
+      f32x16 d = {};
+#pragma unroll 8
+      for (int kb = 0; kb < K / 16; ++kb) {
+        const int ck = 2 * kb + hl;                         // 16-byte chunk of tile row r
+        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(at + r * DC * 2 + ((ck ^ (r & 15)) << 4));
+        const uint8_t *t0 = wt + kb * 16 * (NT * 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t0 + boff0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t0 + boff1));
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, d, 0, 0, 0);
+      }
+      const int rows = min(ROWS, a.B - b0);
+      const size_t ld_out = static_cast<size_t>(a.H) * DV;
+      uint16_t *opo = a.o + static_cast<size_t>(b0) * ld_out + static_cast<size_t>(h) * DV + wave * 32 + r;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = (i >> 2) * 8 + hl * 4 + (i & 3);
+        if (row < rows) opo[row * ld_out] = bf16_bits(to_bf16(d[i]));
+      }
+    }
+    __syncthreads();                    // the tile is rebuilt for the next rows
+  }
+  if (first) wait_vmcnt<0>();           // no tile: still drain the W copies before exit
+}
+
 }  // namespace
+
+hipError_t launch_combine_absorb_out(const CombineOutArgs &args, hipStream_t stream) {
+  // 16-sequence tiles dealt to enough workgroups per head to reach 256
+  // workgroups, but never more than there are tiles
+  CombineOutArgs a = args;
+  const int tiles = (a.B + 15) / 16;
+  a.tile_slots = std::max(1, std::min(tiles, (256 + a.H - 1) / a.H));
+  combine_absorb_out_kernel<<<dim3(a.H * a.tile_slots), 512, 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_absorb_q(const uint16_t *q_nope, const uint16_t *w_uk, uint16_t *q, int B, int H,
                            hipStream_t stream) {

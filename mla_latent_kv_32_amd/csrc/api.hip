@@ -229,6 +229,36 @@ int mla_decode_combine(const void *workspace, size_t workspace_bytes, const int3
   return status_of(mla::launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 
+int mla_decode_combine_absorb_out(const void *workspace, size_t workspace_bytes, const int32_t *seq_lens,
+                                  int max_seq_len, int split_tokens, const void *w_uv, void *o, void *o_latent,
+                                  float *lse, int B, int H, int d_c, int d_v, void *stream) {
+  if (!aligned16(workspace) || !aligned16(seq_lens) || !aligned16(w_uv) || !aligned16(o) ||
+      (o_latent != nullptr && !aligned16(o_latent)) || (lse != nullptr && !aligned16(lse)) || B < 1 || H < 1 ||
+      max_seq_len <= 0 || split_tokens < 0 || split_tokens % MLA_BLOCK_SIZE != 0)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (split_tokens > MLA_MAX_SPLIT_TOKENS || H > 65535) return MLA_ERR_UNSUPPORTED;
+  if (d_c != MLA_D_C || d_v != MLA_D_V) return MLA_ERR_UNSUPPORTED;
+  const int split = split_tokens ? split_tokens : plan_split(B, H, max_seq_len);
+  const int n_splits = (max_seq_len + split - 1) / split;
+  const size_t need = workspace_for(B, H, n_splits);
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  mla::CombineOutArgs a = {};
+  const size_t rows = static_cast<size_t>(B) * n_splits * H;
+  a.o_part = static_cast<const uint16_t *>(workspace);
+  a.lse_part = reinterpret_cast<const float *>(static_cast<const uint8_t *>(workspace) +
+                                               align256(rows * MLA_D_C * sizeof(uint16_t)));
+  a.seq_lens = seq_lens;
+  a.split_tokens = split;
+  a.n_splits = n_splits;
+  a.w_uv = static_cast<const uint16_t *>(w_uv);
+  a.o = static_cast<uint16_t *>(o);
+  a.o_latent = static_cast<uint16_t *>(o_latent);
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  return status_of(mla::launch_combine_absorb_out(a, static_cast<hipStream_t>(stream)));
+}
+
 int mla_absorb_out(const void *o_latent, const void *w_uv, void *o, int B, int H, int d_c, int d_v,
                    void *stream) {
   if (!aligned16(o_latent) || !aligned16(w_uv) || !aligned16(o) || B < 1 || H < 1)

@@ -49,6 +49,21 @@ hipError_t launch_absorb_q(const uint16_t *q_nope, const uint16_t *w_uk, uint16_
 hipError_t launch_absorb_out(const uint16_t *o_latent, const uint16_t *w_uv, uint16_t *o, int B, int H,
                              hipStream_t stream);
 
+// Split-KV combine fused with the value absorption (one workgroup per head).
+struct CombineOutArgs {
+  const uint16_t *o_part;       // [B, n_splits, H, 512] bf16
+  const float *lse_part;        // [B, n_splits, H]
+  const int32_t *seq_lens;
+  int split_tokens, n_splits;
+  const uint16_t *w_uv;         // [H, 512, 128]
+  uint16_t *o;                  // [B, H, 128]
+  uint16_t *o_latent;           // [B, H, 512] or null
+  float *lse;                   // [B, H] or null
+  int B, H;
+  int tile_slots;               // workgroups per head (set by the launcher)
+};
+hipError_t launch_combine_absorb_out(const CombineOutArgs &a, hipStream_t stream);
+
 struct RopeAppendArgs {
   const uint16_t *q_pe;         // [B, H, 64]
   const uint16_t *kv_new;       // [B, 576]

@@ -114,6 +114,12 @@ def test_validation_rejects_before_launch():
     assert comb(NULL, 0, FAKE, 256, 64, FAKE, NULL, 2, 128, NULL) == -1
     assert comb(FAKE, 16, FAKE, 256, 64, FAKE, NULL, 2, 128, NULL) == -3
     assert comb(FAKE, 1 << 30, FAKE, 256, 96, FAKE, NULL, 2, 128, NULL) == -1
+    fused = L.mla_decode_combine_absorb_out
+    assert fused(NULL, 0, FAKE, 256, 64, FAKE, FAKE, NULL, NULL, 2, 128, 512, 128, NULL) == -1
+    assert fused(FAKE, 1 << 30, FAKE, 256, 64, FAKE, FAKE + 2, NULL, NULL, 2, 128, 512, 128, NULL) == -1
+    assert fused(FAKE, 16, FAKE, 256, 64, FAKE, FAKE, NULL, NULL, 2, 128, 512, 128, NULL) == -3
+    assert fused(FAKE, 1 << 30, FAKE, 256, 64, FAKE, FAKE, NULL, NULL, 2, 128, 256, 128, NULL) == -2
+    assert fused(FAKE, 1 << 30, FAKE, 256, 64, FAKE, FAKE, NULL, NULL, 2, 70000, 512, 128, NULL) == -2
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

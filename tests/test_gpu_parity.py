@@ -259,6 +259,57 @@ def test_decode_partial_then_combine_equals_paged():
             assert_close(lse_part[b, ch], rl, LSE_ATOL, LSE_RTOL, what=f"lse_part b={b} c={ch}")
 
 
+@pytest.mark.parametrize("H,lens,split", [
+    (128, [4096] * 32, 512),                                   # one 32-row tile, every chunk full
+    (16, [0, 1, 63, 64, 65, 700, 1500, 2048, 3000] * 4 + [17], 256),   # two tiles, ragged tail, empties
+    (20, [5, 129, 4000], 64),                                  # many chunks, heads not a multiple of 16
+    (128, [(37 * i) % 2600 for i in range(70)], 128),          # 5 tiles over 2 workgroups per head, 21 chunks
+])
+def test_combine_absorb_out_fused(H, lens, split):
+    """One launch for merge + value absorption: bit-identical to mla_decode_combine
+    followed by mla_absorb_out, and o within the bf16 bound of the oracle applied to
+    the same partials (merged latent rounded to bf16, then W_UV)."""
+    B = len(lens)
+    w = synth.gaussian_workload(60 + H, B=B, H=H, seq_lens=lens)
+    max_len = int(max(lens))
+    q = to_dev_bf16(w["q_decode"])
+    kv, bt, sl = to_dev_bf16(w["cache_full"]), to_dev(w["block_table"]), to_dev(w["seq_lens"])
+    w_uv = to_dev_bf16(w["w_uv"])
+    ws = torch.full((mla.mla_decode_workspace_bytes(B, H, max_len, split),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    mla.mla_decode_partial(q, kv, w["kv_dtype"], bt, sl, max_len, w["scale"], ws, split_tokens=split)
+    o_lat1, l1, o1 = nan_bf16(B, H, 512), torch.empty((B, H), dtype=torch.float32, device="cuda"), nan_bf16(B, H, 128)
+    mla.mla_decode_combine(ws, sl, max_len, o_lat1, l1, split_tokens=split)
+    mla.mla_absorb_out(o_lat1, w_uv, o1)
+    o_lat2, l2, o2 = nan_bf16(B, H, 512), torch.empty((B, H), dtype=torch.float32, device="cuda"), nan_bf16(B, H, 128)
+    mla.mla_decode_combine_absorb_out(ws, sl, max_len, w_uv, o2, o_lat2, l2, split_tokens=split)
+    o3 = nan_bf16(B, H, 128)
+    mla.mla_decode_combine_absorb_out(ws, sl, max_len, w_uv, o3, split_tokens=split)
+    torch.cuda.synchronize()
+    assert torch.equal(o_lat1.view(torch.int16), o_lat2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o2.view(torch.int16), o3.view(torch.int16))
+    # oracle on the partials the GPU wrote
+    n_splits = (max_len + split - 1) // split
+    rows = B * n_splits * H
+    o_part = bf(ws[:rows * 512 * 2].view(torch.bfloat16).view(B, n_splits, H, 512))
+    off = ((rows * 512 * 2 + 255) // 256) * 256
+    lse_part = ws[off:off + rows * 4].view(torch.float32).view(B, n_splits, H).cpu().numpy().astype(np.float64)
+    w_uv64 = oracle.bf16_to_f64(w["w_uv"])
+    got = bf(o2)
+    for b in range(B):
+        nv = (lens[b] + split - 1) // split
+        if nv == 0:
+            assert (got[b] == 0).all() and torch.isneginf(l2[b]).all().item()
+            continue
+        ref_lat, ref_l = oracle.combine_partials(o_part[b, :nv], lse_part[b, :nv])
+        assert_close(bf(o_lat2[b]), ref_lat, what=f"merged o_latent b={b}")
+        assert_close(l2[b].cpu().numpy(), ref_l, LSE_ATOL, LSE_RTOL, what=f"lse b={b}")
+        ref_o = oracle.absorb_out(bf(o_lat2[b]), w_uv64)
+        assert_close(got[b], ref_o, what=f"o b={b}")
+
+
 def test_decode_repeatable():
     w = synth.workload(1)
     o1, l1 = run_decode(w)
