@@ -142,7 +142,11 @@ int mla_decode_split_tokens(int B, int H, int max_seq_len);
  * streamed once per head group of up to 128 heads; MFMA with the heads as the
  * matrix dimension, online softmax in fp32, P rounded to bf16 for P.V.
  *   q           [B, H, 576] bf16
- *   kv_cache    as in mla_rope_append_cache
+ *   kv_cache    as in mla_rope_append_cache, format kv_dtype.  For
+ *               MLA_KV_FP8_E4M3 each latent value is expanded in the kernel as
+ *               code * scale of its 128-wide group (fp32, then rounded to
+ *               bf16) before the same bf16 products; rows of a page past
+ *               seq_lens[b] are never used, whatever bytes they hold.
  *   seq_lens    [B] int32, each in [0, max_seq_len]
  *   max_seq_len host-side upper bound on seq_lens (sizes the grid), >= 0,
  *               <= max_blocks_per_seq * block_size

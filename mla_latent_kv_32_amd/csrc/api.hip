@@ -141,7 +141,6 @@ int prepare_decode(DecodeMode mode, const void *q, const void *kv_cache, int kv_
   if (block_size != MLA_BLOCK_SIZE) return MLA_ERR_UNSUPPORTED;
   if (static_cast<long>(max_seq_len) > static_cast<long>(max_blocks_per_seq) * block_size)
     return MLA_ERR_INVALID_ARGUMENT;
-  if (kv_dtype != MLA_KV_BF16) return MLA_ERR_UNSUPPORTED;
   if (split_tokens > MLA_MAX_SPLIT_TOKENS) return MLA_ERR_UNSUPPORTED;
   const int split = split_tokens ? split_tokens : plan_split(B, H, max_seq_len);
   const int n_splits = max_seq_len > 0 ? (max_seq_len + split - 1) / split : 1;
@@ -160,6 +159,7 @@ int prepare_decode(DecodeMode mode, const void *q, const void *kv_cache, int kv_
   a->split_tokens = split;
   a->n_splits = n_splits;
   a->direct = direct ? 1 : 0;
+  a->kv_fp8 = kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 0;
   a->scale_log2 = softmax_scale * 1.44269504088896340736f;
   a->o_latent = static_cast<uint16_t *>(o_latent);
   a->lse = lse;

@@ -60,6 +60,8 @@ constexpr int PX_BYTES = 8 * 32 * 8;            // P of a pair: [token quartet][
 constexpr int AX_BYTES = 32 * 4;                // per-head fp32 factors of a pair
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float RESCALE_SLACK = 8.0f;           // log2 units a stale max may lag
+constexpr int STAGE_BYTES = TB * FP8_ROW_BYTES;  // 20992: a block of packed fp8 rows
+constexpr int FP8_SCALE_OFF = DC + ROPE_BYTES;   // 640: the four group scales of a packed row
 
 // LDS slot layout for a block of 32 tokens:
 //   [0, 32 KB)      latent rows, 1024 B each; 16-byte chunk c of row r sits at
@@ -143,6 +145,36 @@ struct BlockCopier {
   }
 };
 
+// The copy side of the fp8 cache.  A packed row is [512 E4M3 codes | 64 bf16
+// rotary values | 4 fp32 group scales] (656 bytes) and the 32 rows of a block
+// are contiguous in the page, so each of the NC copying waves moves its own
+// TB / NC rows as one contiguous byte range into a staging buffer, unchanged.
+// The same wave later expands exactly those rows (convert8), so the copy and
+// the expansion need no workgroup barrier between them.
+template <int NC>
+struct Fp8Copier {
+  static constexpr int ROWS = TB / NC;                          // rows per copying wave
+  static constexpr int CHUNKS = ROWS * FP8_ROW_BYTES / 16;      // 16-byte pieces per wave
+  static constexpr int NI = (CHUNKS + 63) / 64;                 // wave-wide copies per block
+  static constexpr int TAIL = CHUNKS - (NI - 1) * 64;           // active lanes of the last copy
+  static_assert(ROWS * FP8_ROW_BYTES % 16 == 0 && 2 * NI <= 63, "copy ranges");
+
+  // Rows past the end of the sequence are copied too (they lie inside the
+  // page) and discarded by the expansion.
+  __device__ __forceinline__ static void issue(const uint8_t *cache, int phys, int tok0, int wave, int lane,
+                                               uint8_t *stage) {
+    const uint8_t *src = cache + (static_cast<size_t>(phys) * PAGE + (tok0 & 32) + wave * ROWS) * FP8_ROW_BYTES;
+    const uint32_t dst = lds_addr(stage + wave * ROWS * FP8_ROW_BYTES);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (i + 1 < NI || ln < TAIL)
+        dma16_s(static_cast<uint32_t>((i * 64 + ln) * 16), src, __builtin_amdgcn_readfirstlane(dst + i * 1024));
+    }
+  }
+};
+
 // One wave: scores and softmax for 16 heads, values for its pair's 32 heads
 // over half of the columns.
 //   MFMA 16x16x32 bf16: A/B lane l: row/column l % 16, k = 8 (l / 16) + j;
@@ -158,6 +190,7 @@ struct DecoderPair {
   // (which otherwise waits for group Y at the first barrier) copies.
   static constexpr int NC = NW == 8 ? 4 : NW;
   static constexpr int NI = BlockCopier<NC>::NI;
+  static constexpr int NI8 = Fp8Copier<NC>::NI;
 
   const DecodeArgs &a;
   const int wave, half;                          // wave-uniform
@@ -260,6 +293,55 @@ struct DecoderPair {
   __device__ __forceinline__ void issue(int blk, int phys, uint8_t *slot) {
     const int tok0 = t_begin + blk * TB;
     if (wave < NC) BlockCopier<NC>::issue(a.cache, phys, tok0, min(TB, t_end - tok0) - 1, wave, threadIdx.x & 63, slot);
+  }
+
+  // fp8 cache: start the copy of block blk's packed rows into `stage`.
+  __device__ __forceinline__ void issue8(int blk, int phys, uint8_t *stage) {
+    if (wave < NC) Fp8Copier<NC>::issue(a.cache, phys, t_begin + blk * TB, wave, threadIdx.x & 63, stage);
+  }
+
+  // fp8 cache: expand this wave's rows of block blk from `stage` into the
+  // bf16 slot layout the score and value reads expect.  Latent value j of a
+  // row is code_j * scale[j / 128] formed in fp32 and rounded to bf16 (the
+  // E4M3 code converts to fp32 exactly); the rotary part is copied.  Rows
+  // past the end of the chunk become zeros, so their masked scores meet
+  // finite values.  Lane l handles 16-byte output chunk l of each latent row.
+  __device__ __forceinline__ void convert8(int blk, const uint8_t *stage, uint8_t *slot) {
+    if (wave >= NC) return;
+    constexpr int ROWS = Fp8Copier<NC>::ROWS;
+    const int tok0 = t_begin + blk * TB;
+    const int last = min(TB, t_end - tok0) - 1;
+    const int l = lane_id();
+#pragma unroll
+    for (int k = 0; k < ROWS; ++k) {
+      const int r = wave * ROWS + k;
+      u32x4 out = u32x4{0, 0, 0, 0};
+      if (r <= last) {
+        const uint8_t *src = stage + r * FP8_ROW_BYTES;
+        const u32x2 codes = *reinterpret_cast<const u32x2 *>(src + l * 8);
+        const float sc = *reinterpret_cast<const float *>(src + FP8_SCALE_OFF + (l >> 4) * 4);
+        bf16x8 v;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes[h]), false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes[h]), true);
+          v[4 * h + 0] = to_bf16(lo[0] * sc);
+          v[4 * h + 1] = to_bf16(lo[1] * sc);
+          v[4 * h + 2] = to_bf16(hi[0] * sc);
+          v[4 * h + 3] = to_bf16(hi[1] * sc);
+        }
+        out = __builtin_bit_cast(u32x4, v);
+      }
+      *reinterpret_cast<u32x4 *>(slot + r * LAT_BYTES + ((l ^ fl(r)) << 4)) = out;
+    }
+#pragma unroll
+    for (int n0 = 0; n0 < ROWS * 8; n0 += 64) {
+      const int n = n0 + l;
+      const int r = wave * ROWS + (n >> 3), c = n & 7;
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (r <= last) v = *reinterpret_cast<const u32x4 *>(stage + r * FP8_ROW_BYTES + DC + c * 16);
+      *reinterpret_cast<u32x4 *>(slot + SLOT_LAT + r * ROPE_BYTES + ((c ^ fr(r)) << 4)) = v;
+    }
   }
 
   // Scores of this wave's 16 heads for the block in `slot`, online softmax,
@@ -590,6 +672,117 @@ void decode_bf16_kernel(DecodeArgs a) {
 #undef MLA_STEP_Y
 #undef MLA_WAIT_BLOCK
 
+// fp8 cache.  Packed rows are copied into a staging buffer one step ahead
+// and expanded to bf16 into a ring of three slots one block before use; the
+// score, softmax and value phases are those of the bf16 kernel.
+//
+// Group X, block i in slot CUR (block i + 1 goes into NXT, the slot of block
+// i - 2): Ba [scores + softmax i] Bb [copy i + 2 into staging i % 2]
+// [values i] [wait copy i + 1, expand i + 1].  Ba also publishes X's
+// expansion of block i.
+#define MLA_STEP_X8(K, CUR, NXT)                                       \
+  {                                                                    \
+    const int i = blk + (K);                                           \
+    if (i >= nblk) break;                                              \
+    const int phys = i + 2 < nblk ? dec.page_of(i + 2) : 0;            \
+    barrier_lds();                                                     \
+    dec.scores_softmax(CUR, i);                                        \
+    barrier_lds();                                                     \
+    if (i + 2 < nblk) dec.issue8(i + 2, phys, stage + (i & 1) * STAGE_BYTES); \
+    dec.values(CUR);                                                   \
+    if (i + 1 < nblk) {                                                \
+      if (i + 2 < nblk) wait_vmcnt<D::NI8>();                          \
+      else wait_vmcnt<0>();                                            \
+      dec.convert8(i + 1, stage + ((i + 1) & 1) * STAGE_BYTES, NXT);   \
+    }                                                                  \
+  }
+
+// Group Y, block i >= 1 in slot CUR, block i - 1 in PRV: Ba [values i - 1]
+// Bb [scores + softmax i].
+#define MLA_STEP_Y8(K, CUR, PRV)                                       \
+  {                                                                    \
+    const int i = blk + (K);                                           \
+    if (i >= nblk) break;                                              \
+    barrier_lds();                                                     \
+    dec.values(PRV);                                                   \
+    barrier_no_fence();                                                \
+    dec.scores_softmax(CUR, i);                                        \
+  }
+
+template <class D, int WAVES_PER_EU>
+__global__ __attribute__((amdgpu_flat_work_group_size(D::NW * 64, D::NW * 64),
+                          amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
+void decode_fp8_kernel(DecodeArgs a) {
+  constexpr int RING = 3 * SLOT_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[RING + 2 * STAGE_BYTES];
+  uint8_t *const slot0 = lds, *const slot1 = lds + SLOT_BYTES, *const slot2 = lds + 2 * SLOT_BYTES;
+  uint8_t *const stage = lds + RING;
+  static_assert(D::HEADS * LAT_BYTES <= RING + 2 * STAGE_BYTES, "the output tile is staged in LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t px[D::NW / 2 * PX_BYTES];
+  __shared__ __attribute__((aligned(16))) float ax[D::NW / 2 * 32];
+  __shared__ __attribute__((aligned(16))) float fx[D::NW / 2 * 32];
+  constexpr int NW = D::NW;
+
+  int item = blockIdx.x;
+  if ((gridDim.x & 7) == 0) item = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int b = item / a.n_splits;
+  const int split = item - b * a.n_splits;
+  const int S = a.seq_lens[b];
+  const int t_begin = split * a.split_tokens;
+  const int t_end = min(S, t_begin + a.split_tokens);
+
+  if (t_begin >= t_end) {
+    if (a.direct) {
+      const int t = threadIdx.x;
+      const int head = blockIdx.y * D::HEADS + t / 4;
+      if (head < a.H) {
+        uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + (t % 4) * (DC / 4);
+        for (int c = 0; c < DC / 4; c += 8) *reinterpret_cast<u32x4 *>(dst + c) = u32x4{0, 0, 0, 0};
+        if (t % 4 == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = -INFINITY;
+      }
+    }
+    return;
+  }
+
+  D dec(a, px, ax, fx, b, split, t_begin, t_end);
+  dec.begin();
+  const int nblk = (t_end - t_begin + TB - 1) / TB;
+  dec.issue8(0, dec.page_of(0), stage);
+  dec.load_q();
+  wait_vmcnt<0>();
+  if (nblk > 1) dec.issue8(1, dec.page_of(1), stage + STAGE_BYTES);
+  dec.convert8(0, stage, slot0);
+
+  // Slot of block i: i % 3.  Block i + 1 is expanded into the slot of block
+  // i - 2 after the second barrier of block i, when both groups are done
+  // with block i - 2.
+  const bool group_y = NW == 8 && (threadIdx.x >> 8) != 0;
+  if (!group_y) {
+    for (int blk = 0; blk < nblk; blk += 3) {
+      MLA_STEP_X8(0, slot0, slot1)
+      MLA_STEP_X8(1, slot1, slot2)
+      MLA_STEP_X8(2, slot2, slot0)
+    }
+    barrier_no_fence();       // Y publishes its P of the last block
+  } else {
+    barrier_lds();
+    barrier_no_fence();
+    dec.scores_softmax(slot0, 0);
+    for (int blk = 1; blk < nblk; blk += 3) {
+      MLA_STEP_Y8(0, slot1, slot0)
+      MLA_STEP_Y8(1, slot2, slot1)
+      MLA_STEP_Y8(2, slot0, slot2)
+    }
+    barrier_lds();
+    const int last = (nblk - 1) % 3;
+    dec.values(last == 0 ? slot0 : (last == 1 ? slot1 : slot2));
+  }
+  dec.finish(lds);
+}
+
+#undef MLA_STEP_X8
+#undef MLA_STEP_Y8
+
 // Merge split-KV partials: o = sum_c w_c o_c / sum_c w_c, w_c = exp(lse_c - L),
 // L = max_c lse_c.  One 64-lane group per (sequence, head), 8 columns per
 // lane; the chunks' lse are reduced across the lanes first, then the partial
@@ -655,6 +848,14 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int hpw = decode_heads_per_wave(a.H);
   const int groups = (a.H + hpw * nw - 1) / (hpw * nw);
   dim3 grid(a.B * a.n_splits, groups);
+  if (a.kv_fp8) {
+    switch (nw) {
+      case 2: decode_fp8_kernel<DecoderPair<2>, 1><<<grid, 128, 0, stream>>>(a); break;
+      case 4: decode_fp8_kernel<DecoderPair<4>, 1><<<grid, 256, 0, stream>>>(a); break;
+      default: decode_fp8_kernel<DecoderPair<8>, 2><<<grid, 512, 0, stream>>>(a); break;
+    }
+    return hipGetLastError();
+  }
   switch (nw) {
     case 2: decode_bf16_kernel<DecoderPair<2>, 1><<<grid, 128, 0, stream>>>(a); break;
     case 4: decode_bf16_kernel<DecoderPair<4>, 1><<<grid, 256, 0, stream>>>(a); break;

@@ -19,6 +19,7 @@ struct DecodeArgs {
   int split_tokens;             // multiple of 64
   int n_splits;                 // chunks per sequence in the grid
   int direct;                   // 1: one chunk, write o_latent / lse directly
+  int kv_fp8;                   // 1: packed fp8 rows (656 bytes), else bf16 rows (1152 bytes)
   float scale_log2;             // softmax_scale * log2(e)
   uint16_t *o_latent;           // [B, H, 512] bf16
   float *lse;                   // [B, H] or null
