@@ -51,10 +51,10 @@ COPIES = 3
 # reported only while that source is unchanged.
 DECODE_TRAFFIC = {
     "sources_sha256": {
-        "mla_latent_kv_32_amd/csrc/decode.hip": "62d48bc9b2ccaebce8212e41194253a396337a3baac698e3c816201eaf557724",
-        "mla_latent_kv_32_amd/csrc/common.h": "ab381b81c10ae7b628a24624be42a9c4c2714b9b2e3b82c2038876b6e1f6e82d",
+        "mla_latent_kv_32_amd/csrc/decode.hip": "8ed0a26dc51d2b4ee4ea106521cc4fba9089f835c03880ed835abbf89324ceb8",
+        "mla_latent_kv_32_amd/csrc/common.h": "9119e84c6a1340e11077a316e161bf93b3bc7e62a88e7300f6ef510da895fad9",
     },
-    "fetch_kib": 76362.9,
+    "fetch_kib": 76356.8,
     "write_kib": 32896.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,

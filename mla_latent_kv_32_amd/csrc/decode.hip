@@ -357,7 +357,7 @@ struct DecoderPair {
                                     : slot + (krb ^ ((ks - KLAT) * 64)) + hi * 16 * ROPE_BYTES;
       return *reinterpret_cast<const bf16x8 *>(kp);
     };
-    constexpr int PF = 1;
+    constexpr int PF = 2;
     bf16x8 k0[KSTEPS], k1[KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < PF; ++ks) {
