@@ -533,6 +533,417 @@ struct DecoderPair {
   }
 };
 
+// One wave per SIMD: 4 waves of 32 heads each (128 heads per workgroup), 512
+// registers per lane.  Both products use v_mfma_f32_32x32x16_bf16 with the
+// heads as the 32-wide N dimension, so every 1 KB operand tile read from LDS
+// feeds 32 heads, and no wave exchanges anything with another.
+//   scores   S^T[row, head] = K[row, 0:576] . Q^T over 36 k-steps of 16 dims;
+//            the query fragments (144 VGPRs) stay in registers
+//   softmax  on the score accumulator: lane (head l % 32, hb = l / 32) holds
+//            K-rows 8 (i / 4) + 4 hb + i % 4 of register i
+//   values   O^T[col, head] += V^T[col, row] . P^T[row, head]; registers
+//            8 t .. 8 t + 7 of the score accumulator, rounded to bf16, are the
+//            B operand of token step t as they stand
+//   16 column tiles x 16 registers of accumulators per lane (256 AGPRs).
+// A single wave per SIMD issues at most one instruction per four cycles, and
+// a 32x32x16 MFMA lasts eight of those issue slots, so the operand reads are
+// laid out to need no address arithmetic: every read is a per-lane base
+// register plus an immediate offset.
+//
+// Slot layout (one 32-token block): latent rows at a padded stride of
+// 1040 bytes (the 16-byte pad puts row r's chunk c on bank quad (r + c) % 16),
+// then the rotary keys, 128 bytes per row, chunk c of row r at c ^ fr(r).
+// Token n of the block is stored in row n.  The MFMA's K-row m is token
+// pi(m): with m = 16 t + 8 h + 4 b + d, pi(m) = 16 b + 4 d + 2 t + h.
+//   - score reads: lane l reads row pi(l % 32), chunk 2 ks + l / 32; each
+//     16-lane read group covers the residues of its 16 rows mod 16 once, so
+//     no two lanes share a bank quad;
+//   - value reads (transposed): the lo/hi reads of token step t cover rows
+//     16 hb + 4 d + 2 t (+ 1 for hi), d = 0..3 -- four rows 4 apart, so the
+//     4 x 4 chunks of 32 lanes fall on 16 distinct bank quads, and the rows
+//     are exactly the K-rows of score registers 8 t .. 8 t + 7 in the order
+//     the B operand expects.
+// A stale running max may lag the true one by up to 32 (log2 units) before
+// the value accumulators are rescaled: weights stay below 2^32 and sums of
+// them below 2^51 times the largest latent value, far inside fp32, and the
+// rescale (which touches all 256 accumulator registers) becomes rare.
+constexpr float SOLO_SLACK = 32.0f;
+constexpr int S_LROW = LAT_BYTES + 16;               // 1040
+constexpr int S_LAT = TB * S_LROW;                   // 33280
+constexpr int S_SLOT = S_LAT + TB * ROPE_BYTES;      // 37376
+__device__ __forceinline__ int solo_pi(int m) {
+  return 16 * ((m >> 2) & 1) + 4 * (m & 3) + 2 * ((m >> 4) & 1) + ((m >> 3) & 1);
+}
+
+struct DecoderSolo {
+  static constexpr int NW = 4;
+  static constexpr int HEADS = 128;
+  static constexpr int NI = TB / NW + 1;           // copies per wave per block
+  static constexpr int KS = DROW / 16;             // 36 score k-steps
+  static constexpr int KSL = DC / 16;              // the first 32 are latent
+  static constexpr int NT = DC / 32;               // 16 value column tiles
+  static_assert(NI * NW == NDMA && 3 * NI <= 63, "every wave copies the same share of a block");
+
+  const DecodeArgs &a;
+  const int wave;
+  const int b, split;
+  const int t_begin, t_end;
+  const int32_t *bt_row;
+
+  bf16x8 qf[KS];
+  f32x16 o[NT];
+  // Per lane (head l % 32; lanes l and l + 32 share a head and hold the same
+  // m_run): running max (log2 units), this lane's share of the sum of the
+  // bf16-rounded weights and of the unrounded weights.
+  float m_run, l_run, e_run;
+
+  __device__ DecoderSolo(const DecodeArgs &args, int b_, int split_, int t0, int t1)
+      : a(args), wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)), b(b_), split(split_),
+        t_begin(t0), t_end(t1), bt_row(args.block_table + static_cast<size_t>(b_) * args.max_blocks) {}
+
+  __device__ __forceinline__ static int lane_id() {
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l;
+  }
+  __device__ __forceinline__ static int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+  }
+  __device__ __forceinline__ int head_of(int l) const { return blockIdx.y * HEADS + wave * 32 + (l & 31); }
+
+  __device__ __forceinline__ void begin() {
+    m_run = -INFINITY;
+    l_run = 0.f;
+    e_run = 0.f;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) o[j] = f32x16{};
+  }
+
+  // Query fragments (32x32x16 B operand): lane (head l % 32, hb = l / 32)
+  // holds dims 16 ks + 8 hb + [0, 8).
+  __device__ __forceinline__ void load_q() {
+    const int l = threadIdx.x & 63, head = head_of(l);
+    const bool ok = head < a.H;
+    const uint16_t *qp = a.q + (static_cast<size_t>(b) * a.H + (ok ? head : 0)) * DROW + (l >> 5) * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = *reinterpret_cast<const u32x4 *>(qp + ks * 16);
+      if (!ok) v = u32x4{0, 0, 0, 0};
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  __device__ __forceinline__ int page_of(int blk) const {
+    return ((const_i32 *)bt_row)[(t_begin + blk * TB) >> 6];
+  }
+
+  // Copies of a block into its slot: wave w moves latent rows w + 4 k
+  // (k = 0..7, one 1 KB row per wave-wide copy, to row w + 4 k of the slot)
+  // and the rotary keys of rows 8 w .. 8 w + 7 (copy k = 8).  Rows past the
+  // end of the chunk re-read its last row (finite data, masked scores).
+  struct Copy {
+    const uint8_t *base;       // first row of the block in its page
+    uint32_t slot_lds;
+    int last;                  // last valid row of the block
+  };
+  __device__ __forceinline__ Copy copy_of(int blk, int phys, uint8_t *slot) const {
+    const int tok0 = t_begin + blk * TB;
+    return Copy{a.cache + (static_cast<size_t>(phys) * PAGE + (tok0 & 32)) * ROW_BYTES, lds_addr(slot),
+                min(TB, t_end - tok0) - 1};
+  }
+  // voff: this lane's byte offset in a latent row (16 * lane); roff: its
+  // offset for the rotary copy (row min(8 w + l / 8, last), chunk l % 8 of
+  // the rotary part, stored at chunk (l % 8) ^ fr(row)).
+  __device__ __forceinline__ uint32_t rope_voff(const Copy &c, int l) const {
+    const int rr = wave * 8 + (l >> 3);
+    return static_cast<uint32_t>(min(rr, c.last) * ROW_BYTES + LAT_BYTES + (((l & 7) ^ fr(rr)) << 4));
+  }
+  __device__ __forceinline__ void copy(const Copy &c, int k, uint32_t voff, uint32_t roff) const {
+    if (k < TB / NW) {
+      const int n = wave + NW * k;
+      dma16_s(voff, c.base + min(n, c.last) * ROW_BYTES, __builtin_amdgcn_readfirstlane(c.slot_lds + n * S_LROW));
+    } else {
+      dma16_s(roff, c.base, __builtin_amdgcn_readfirstlane(c.slot_lds + S_LAT + wave * 1024));
+    }
+  }
+  __device__ __forceinline__ void issue(int blk, int phys, uint8_t *slot) const {
+    const Copy c = copy_of(blk, phys, slot);
+    const int l = lane_id();
+    const uint32_t voff = static_cast<uint32_t>(l << 4), roff = rope_voff(c, l);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) copy(c, k, voff, roff);
+  }
+
+  // MFMAs are written out so that their order is the program order (the
+  // loads between them are pinned by the memory clobber) and so that the
+  // score accumulator stays in VGPRs (the builtin would take the accumulator
+  // form, and the 256 value accumulators fill the AGPR file).  The score
+  // accumulator lives in fixed registers (v[16:31]) so that the compiler
+  // never copies it between two MFMAs of its chain.  The last MFMA of a chain
+  // whose result compiler-generated code reads carries the result wait states
+  // in the same asm statement: the compiler cannot see that an asm MFMA is
+  // still writing its output.  "nop" adds the wait states a VALU write of an
+  // operand needs right before an MFMA (the first MFMA after the softmax).
+#define MLA_MFMA_WAIT "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+  __device__ __forceinline__ static void mfma_s(f32x16 &s, bf16x8 k, bf16x8 q, bool first, bool last) {
+    if (first)
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                   : "=&{v[16:31]}"(s) : "v"(k), "v"(q) : "memory");
+    else if (!last)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                   : "+{v[16:31]}"(s) : "v"(k), "v"(q) : "memory");
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" MLA_MFMA_WAIT
+                   : "+{v[16:31]}"(s) : "v"(k), "v"(q) : "memory");
+  }
+  __device__ __forceinline__ static void mfma_o(f32x16 &acc, bf16x8 v, bf16x8 p, bool nop, bool last) {
+    if (nop)
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p) : "memory");
+    else if (!last)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p) : "memory");
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" MLA_MFMA_WAIT
+                   : "+a"(acc) : "v"(v), "v"(p) : "memory");
+  }
+#undef MLA_MFMA_WAIT
+  // Orders every later read of the value accumulators after the asm MFMAs
+  // issued before it.
+  __device__ __forceinline__ void fence_o() {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) asm volatile("" : "+a"(o[j]) : : "memory");
+  }
+
+  // Score operand of k-step ks (A of S^T = K Q^T): lane l, K-row m = l % 32,
+  // reads row pi(m), 16-byte chunk 2 ks + l / 32: k_base + 32 ks.  Rotary
+  // k-steps (ks >= 32): chunk c = 2 (ks - 32) + l / 32 at c ^ fr(row):
+  // kr_base ^ 32 (ks - 32).
+  __device__ __forceinline__ static int k_base(int l) {
+    return solo_pi(l & 31) * S_LROW + 16 * (l >> 5);
+  }
+  __device__ __forceinline__ static int kr_base(int l) {
+    const int r = solo_pi(l & 31);
+    return S_LAT + r * ROPE_BYTES + (((l >> 5) ^ fr(r)) << 4);
+  }
+  __device__ __forceinline__ static bf16x8 kread(const uint8_t *slot, int kb, int krb, int ks) {
+    const uint8_t *p = ks < KSL ? slot + kb + 32 * ks : slot + (opaque(krb) ^ ((ks - KSL) * 32));
+    return *reinterpret_cast<const bf16x8 *>(p);
+  }
+  // Value operand n = 16 t + j (column tile j, token step t; A of
+  // O^T += V^T P^T): a transposed read returns column 32 j + l % 32 of the
+  // 4 rows supplied by the lane quads of its 16-lane group.  Lane l supplies
+  // row 16 hb + 4 d + 2 t (d = (l & 15) / 4; + 1 for the hi read), chunk
+  // 4 j + csub, csub = 2 ((l >> 4) & 1) + (l & 3) / 2, byte 8 (l & 1):
+  // v_base + 2080 t + 64 j, hi + 1040.
+  __device__ __forceinline__ static int v_base(int l) {
+    const int row = 16 * (l >> 5) + 4 * ((l & 15) >> 2);
+    const int csub = 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
+    return row * S_LROW + 16 * csub + 8 * (l & 1);
+  }
+  __device__ __forceinline__ static bf16x8 vread(const uint8_t *slot, int vb, int n) {
+    const int j = n & 15, t = n >> 4;
+    const uint8_t *r0 = slot + vb + 2 * t * S_LROW + 64 * j;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)r0);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(r0 + S_LROW));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  // Online-softmax state of the block whose scores are in the score
+  // accumulator.  Register i of lane (head, hb) holds the score of token
+  // pi(8 (i / 4) + 4 hb + i % 4) = 16 hb + 4 (i % 4) + 2 (i / 8) + (i / 4) % 2.
+  // The max update is branch-free (the lazy rescale of the value
+  // accumulators by alpha happens before the next value product).
+  struct Soft {
+    float mx, alpha, pe;
+    bf16x8 p[2];
+  };
+  // Step k (0..13) of the softmax of scores s; the steps are spread over the
+  // value MFMAs of the previous block.
+  __device__ __forceinline__ void soft_step(int k, f32x16 &s, Soft &st, bool mask, int lim) {
+    const float c = a.scale_log2;
+    if (k == 0) {
+      if (mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (4 * (i & 3) + 2 * (i >> 3) + ((i >> 2) & 1) >= lim) s[i] = -INFINITY;
+      }
+      st.mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    } else if (k == 1) {
+      st.mx = fmaxf(st.mx, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
+                                 fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+    } else if (k == 2) {
+      const float m_new = fmaxf(m_run, max_xor32(st.mx) * c);
+      const bool up = m_new > m_run + SOLO_SLACK;
+      const float e = __builtin_amdgcn_exp2f(m_run - m_new);       // 0 while m_run = -inf
+      st.alpha = up ? e : 1.0f;
+      m_run = up ? m_new : m_run;
+      l_run *= st.alpha;
+      e_run *= st.alpha;
+      st.pe = 0.f;
+    } else if (k < 11) {
+      // two registers per step: 2 (k - 3), 2 (k - 3) + 1
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = 2 * (k - 3) + h;
+        const float f = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m_run));
+        st.pe += f;
+        st.p[i >> 3][i & 7] = to_bf16(f);
+      }
+    } else if (k < 13) {
+      // sum of the rounded weights (bf16 pairs dotted with (1, 1))
+      const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+      const bf16x8 q = st.p[k - 11];
+      float ps = l_run;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{q[2 * i], q[2 * i + 1]}, one2, ps, false);
+      l_run = ps;
+      if (k == 12) e_run += st.pe;
+    }
+  }
+  __device__ __forceinline__ void softmax_all(f32x16 &s, Soft &st, bool mask, int lim) {
+#pragma unroll
+    for (int k = 0; k < 13; ++k) soft_step(k, s, st, mask, lim);
+  }
+  // Rescale the value accumulators if any head of the wave moved its max.
+  __device__ __forceinline__ void rescale(float alpha) {
+    if (__ballot(alpha != 1.0f)) {
+      // In place on the accumulator registers, one at a time (a vector
+      // multiply of o would copy all 256 of them out of the AGPR file),
+      // after the wait states of the value MFMAs that wrote them last.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          float t;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\ts_nop 1\n\tv_mul_f32 %1, %1, %2\n\ts_nop 1\n\t"
+                       "v_accvgpr_write_b32 %0, %1"
+                       : "+a"(o[j][k]), "=&v"(t) : "v"(alpha));
+        }
+      asm volatile("s_nop 7" ::: "memory");
+    }
+  }
+
+  // Scores of the block in `slot_s` (36 dependent MFMAs, with the copies of
+  // `cp` spread over them when COPY), then the value product of the block in
+  // `slot_v` (P = pv) with the softmax of the new scores spread over its 32
+  // MFMAs (mask: the new block is the last, partial one; lim = its valid
+  // tokens, less 16 on the lanes of the second half).  Returns the new block's P in pn and its rescale factor.
+  template <bool COPY>
+  __device__ __forceinline__ void phase(const uint8_t *slot_s, const uint8_t *slot_v, const bf16x8 (&pv)[2],
+                                        bf16x8 (&pn)[2], float &alpha, const Copy &cp, bool mask, int lim) {
+    const int l = lane_id();
+    const int kb = k_base(l), krb = kr_base(l), vb = v_base(l);
+    uint32_t voff = 0, roff = 0;
+    if (COPY) {
+      voff = static_cast<uint32_t>(opaque(l) << 4);
+      roff = rope_voff(cp, l);
+    }
+    constexpr int RK = 4, RV = 4, NV = 2 * NT;
+    bf16x8 kr[KS], vf[NV];
+    f32x16 s;
+#pragma unroll
+    for (int ks = 0; ks < RK; ++ks) kr[ks] = kread(slot_s, kb, krb, ks);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + RK < KS) kr[ks + RK] = kread(slot_s, kb, krb, ks + RK);
+      mfma_s(s, kr[ks], qf[ks], ks == 0, ks == KS - 1);
+      if (COPY && (ks & 3) == 1 && (ks >> 2) < NI) copy(cp, ks >> 2, voff, roff);
+    }
+#pragma unroll
+    for (int n = 0; n < RV; ++n) vf[n] = vread(slot_v, vb, n);
+    Soft st;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      if (n + RV < NV) vf[n + RV] = vread(slot_v, vb, n + RV);
+      mfma_o(o[n & 15], vf[n], pv[n >> 4], n == 0, false);
+      if (n >= 1 && n <= 13) soft_step(n - 1, s, st, mask, lim);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pn[0] = st.p[0];
+    pn[1] = st.p[1];
+    alpha = st.alpha;
+  }
+
+  // Scores of the first block (no value product yet).
+  __device__ __forceinline__ f32x16 scores(const uint8_t *slot) const {
+    const int l = lane_id();
+    const int kb = k_base(l), krb = kr_base(l);
+    constexpr int RK = 4;
+    bf16x8 kr[KS];
+#pragma unroll
+    for (int ks = 0; ks < RK; ++ks) kr[ks] = kread(slot, kb, krb, ks);
+    f32x16 s;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + RK < KS) kr[ks + RK] = kread(slot, kb, krb, ks + RK);
+      mfma_s(s, kr[ks], qf[ks], ks == 0, ks == KS - 1);
+    }
+    return s;
+  }
+
+  // Value product of the last block alone.
+  __device__ __forceinline__ void values(const uint8_t *slot, const bf16x8 (&pv)[2]) {
+    const int l = lane_id();
+    const int vb = v_base(l);
+    constexpr int RV = 4, NV = 2 * NT;
+    bf16x8 vf[NV];
+#pragma unroll
+    for (int n = 0; n < RV; ++n) vf[n] = vread(slot, vb, n);
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      if (n + RV < NV) vf[n + RV] = vread(slot, vb, n + RV);
+      mfma_o(o[n & 15], vf[n], pv[n >> 4], n == 0, n == NV - 1);
+    }
+  }
+
+  // Normalise and store: lse by the lanes of the first half; the tile goes
+  // through LDS (row = head of the workgroup, 16-byte chunk c at position
+  // c ^ (row & 15)) so that each global store writes one whole 1 KB row.
+  // Each wave reads back only the rows it wrote.
+  __device__ __forceinline__ void finish(uint8_t *stage) {
+    const int l = threadIdx.x & 63;
+    const float l_tot = sum_xor32(l_run);
+    const float e_tot = sum_xor32(e_run);
+    const float inv = 1.0f / l_tot;
+    const float lse_v = (m_run + __log2f(e_tot)) * LN2;
+    const int head = head_of(l);
+    if (l < 32 && head < a.H) {
+      if (a.direct) {
+        if (a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = lse_v;
+      } else {
+        a.lse_part[(static_cast<size_t>(b) * a.n_splits + split) * a.H + head] = lse_v;
+      }
+    }
+    barrier_lds();            // every wave is done with the slots
+    const int row = wave * 32 + (l & 31);
+    uint8_t *srow = stage + row * LAT_BYTES + (l >> 5) * 8;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[j][4 * q + e] * inv);
+        const int c = j * 4 + q;                            // 16-byte chunk of the row
+        *reinterpret_cast<bf16x4 *>(srow + ((c ^ (row & 15)) << 4)) = v;
+      }
+    }
+    asm volatile("" ::: "memory");   // a wave's LDS accesses complete in order
+#pragma unroll 4
+    for (int k = 0; k < 32; ++k) {
+      const int r = wave * 32 + k;
+      const int h = blockIdx.y * HEADS + r;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * LAT_BYTES + ((l ^ (r & 15)) << 4));
+      if (h < a.H) {
+        uint16_t *dst = a.direct ? a.o_latent + (static_cast<size_t>(b) * a.H + h) * DC
+                                 : a.o_part + ((static_cast<size_t>(b) * a.n_splits + split) * a.H + h) * DC;
+        *reinterpret_cast<u32x4 *>(dst + l * 8) = v;
+      }
+    }
+  }
+};
+
 // Wait until this wave's copies of block i have landed (copies of the next
 // `ahead` blocks may still be in flight).
 template <int NI, int AHEAD>
@@ -671,6 +1082,93 @@ void decode_bf16_kernel(DecodeArgs a) {
 #undef MLA_STEP_X
 #undef MLA_STEP_Y
 #undef MLA_WAIT_BLOCK
+
+// One-wave-per-SIMD decoder.  Iteration i (scores of block i already in s):
+// [wait own copies of i + 1] barrier [copy i + 3 into the slot of i - 1]
+// [softmax i] [scores i + 1] [values i]; the last block is peeled off the
+// loop.  The barrier makes block i + 1 visible and certifies that every wave
+// is done with block i - 1.  Slot of block i: i % 4.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void decode_solo_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT * S_SLOT];
+  static_assert(DecoderSolo::HEADS * LAT_BYTES <= NSLOT * S_SLOT, "the output tile is staged in the slot ring");
+
+  int item = blockIdx.x;
+  if ((gridDim.x & 7) == 0) item = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int b = item / a.n_splits;
+  const int split = item - b * a.n_splits;
+  const int S = a.seq_lens[b];
+  const int t_begin = split * a.split_tokens;
+  const int t_end = min(S, t_begin + a.split_tokens);
+
+  if (t_begin >= t_end) {
+    if (a.direct) {
+      const int t = threadIdx.x;
+      const int head = blockIdx.y * DecoderSolo::HEADS + t / 2;      // 2 threads per head
+      if (head < a.H) {
+        uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + (t % 2) * (DC / 2);
+        for (int c = 0; c < DC / 2; c += 8) *reinterpret_cast<u32x4 *>(dst + c) = u32x4{0, 0, 0, 0};
+        if (t % 2 == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = -INFINITY;
+      }
+    }
+    return;
+  }
+
+  DecoderSolo dec(a, b, split, t_begin, t_end);
+  dec.begin();
+  const int nblk = (t_end - t_begin + TB - 1) / TB;
+  const int lim_last = t_end - t_begin - (nblk - 1) * TB - 16 * (threadIdx.x >> 5 & 1);
+  const bool ragged = (t_end - t_begin) % TB != 0;
+  auto slot = [&](int i) { return ring + (i & (NSLOT - 1)) * S_SLOT; };
+  // Block 0's copies, the query and blocks 1 and 2 all go out at once; the
+  // first wait covers block 0 and the query only.
+  dec.issue(0, dec.page_of(0), slot(0));
+  dec.load_q();
+  if (nblk > 1) dec.issue(1, dec.page_of(1), slot(1));
+  if (nblk > 2) dec.issue(2, dec.page_of(2), slot(2));
+  if (nblk > 2) wait_vmcnt<2 * DecoderSolo::NI>();
+  else if (nblk > 1) wait_vmcnt<DecoderSolo::NI>();
+  else wait_vmcnt<0>();
+  barrier_no_fence();         // block 0 visible
+  bf16x8 pb[2], pn[2];
+  float alpha;
+  {
+    f32x16 s0 = dec.scores(slot(0));
+    DecoderSolo::Soft st;
+    dec.softmax_all(s0, st, nblk == 1 && ragged, lim_last);
+    pb[0] = st.p[0];
+    pb[1] = st.p[1];
+    alpha = 1.0f;             // the value accumulators are still zero
+  }
+  // Iteration i: [wait own copies of i + 1] barrier [rescale for block i]
+  // [scores i + 1 (+ copies of i + 3 into the slot of i - 1)]
+  // [values i + softmax i + 1].  The barrier makes block i + 1 visible and
+  // certifies that every wave is done with block i - 1.
+  int i = 0;
+  for (; i + 3 < nblk; ++i) {
+    const int phys = dec.page_of(i + 3);
+    wait_vmcnt<DecoderSolo::NI>();
+    barrier_no_fence();
+    const DecoderSolo::Copy cp = dec.copy_of(i + 3, phys, slot(i + 3));
+    dec.rescale(alpha);
+    dec.phase<true>(slot(i + 1), slot(i), pb, pn, alpha, cp, false, 0);
+    pb[0] = pn[0];
+    pb[1] = pn[1];
+  }
+  for (; i + 1 < nblk; ++i) {
+    if (i + 2 < nblk) wait_vmcnt<DecoderSolo::NI>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();
+    dec.rescale(alpha);
+    dec.phase<false>(slot(i + 1), slot(i), pb, pn, alpha, DecoderSolo::Copy{}, i + 2 == nblk && ragged, lim_last);
+    pb[0] = pn[0];
+    pb[1] = pn[1];
+  }
+  dec.rescale(alpha);
+  dec.values(slot(nblk - 1), pb);
+  dec.fence_o();
+  dec.finish(ring);
+}
 
 // fp8 cache.  Packed rows are copied into a staging buffer one step ahead
 // and expanded to bf16 into a ring of three slots one block before use; the
@@ -854,6 +1352,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
       case 4: decode_fp8_kernel<DecoderPair<4>, 1><<<grid, 256, 0, stream>>>(a); break;
       default: decode_fp8_kernel<DecoderPair<8>, 2><<<grid, 512, 0, stream>>>(a); break;
     }
+    return hipGetLastError();
+  }
+  if (nw == 8) {
+    decode_solo_kernel<<<grid, 256, 0, stream>>>(a);
     return hipGetLastError();
   }
   switch (nw) {

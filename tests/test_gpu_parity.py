@@ -224,6 +224,29 @@ def test_decode_ragged_lengths_and_heads(H):
         check_decode(w, o, lse, [(b, range(H)) for b in range(len(lens))], p_rounding_term=True)
 
 
+def _scale_rows_pow2(w, picks):
+    """Copy of w whose cached rows (b, token) are multiplied by 2^k exactly
+    (bf16 exponent field + k; the N(0,1) entries are normal numbers)."""
+    pool = w["cache_full"].copy()
+    for b, t, k in picks:
+        row = pool[w["block_table"][b][t // 64], t % 64]
+        nz = (row & 0x7F80) != 0
+        row[nz] = row[nz] + np.uint16(k << 7)
+    return dict(w, cache_full=pool)
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_decode_running_max_jumps(H):
+    """Late tokens whose scores exceed the running max by tens of log2 units:
+    exercises the rescale of the value accumulators (lazy and forced)."""
+    lens = [700, 1500, 333]
+    w = synth.gaussian_workload(50 + H, B=len(lens), H=H, seq_lens=lens)
+    w = _scale_rows_pow2(w, [(0, 300, 3), (0, 650, 5), (1, 40, 2), (1, 1200, 6), (2, 332, 4)])
+    for split in [0, 256, 1024]:
+        o, lse = run_decode(w, split_tokens=split)
+        check_decode(w, o, lse, [(b, range(H)) for b in range(len(lens))], p_rounding_term=True)
+
+
 def test_decode_without_lse_and_all_empty():
     w = synth.gaussian_workload(40, B=3, H=16, seq_lens=[0, 0, 0])
     o, _ = run_decode(w, with_lse=False)
