@@ -583,6 +583,7 @@ struct DecoderSolo {
   static constexpr int KSL = DC / 16;              // the first 32 are latent
   static constexpr int NT = DC / 32;               // 16 value column tiles
   static_assert(NI * NW == NDMA && 3 * NI <= 63, "every wave copies the same share of a block");
+  static_assert(3 * (NI - 1) + 1 < 2 * (DC / 32), "every copy of a block is issued among its value MFMAs");
 
   const DecodeArgs &a;
   const int wave;
@@ -824,45 +825,47 @@ struct DecoderSolo {
     }
   }
 
-  // Scores of the block in `slot_s` (36 dependent MFMAs, with the copies of
-  // `cp` spread over them when COPY), then the value product of the block in
-  // `slot_v` (P = pv) with the softmax of the new scores spread over its 32
-  // MFMAs (mask: the new block is the last, partial one; lim = its valid
-  // tokens, less 16 on the lanes of the second half).  Returns the new block's P in pn and its rescale factor.
+  // One step of the pipeline, on blocks i (in `slot_v`, scores in s) and
+  // i + 1 (in `slot_s`): the 36 score MFMAs of block i + 1 with the softmax of
+  // block i spread over them (its steps between every second MFMA), the
+  // rescale of the value accumulators for block i, then the 32 value MFMAs of
+  // block i with the nine copies of `cp` (when COPY) spread over them.  s holds
+  // block i + 1's scores on return.  Block i is never the last block, so no
+  // masking.  first: block i is block 0 (the accumulators are still zero).
   template <bool COPY>
-  __device__ __forceinline__ void phase(const uint8_t *slot_s, const uint8_t *slot_v, const bf16x8 (&pv)[2],
-                                        bf16x8 (&pn)[2], float &alpha, const Copy &cp, bool mask, int lim) {
+  __device__ __forceinline__ void phase(const uint8_t *slot_s, const uint8_t *slot_v, f32x16 &s, bool first,
+                                        const Copy &cp) {
     const int l = lane_id();
-    const int kb = k_base(l), krb = kr_base(l), vb = v_base(l);
-    uint32_t voff = 0, roff = 0;
-    if (COPY) {
-      voff = static_cast<uint32_t>(opaque(l) << 4);
-      roff = rope_voff(cp, l);
-    }
+    const int kb = k_base(l), krb = kr_base(l);
     constexpr int RK = 4, RV = 4, NV = 2 * NT;
     bf16x8 kr[KS], vf[NV];
-    f32x16 s;
+    f32x16 sn;
+    Soft st;
 #pragma unroll
     for (int ks = 0; ks < RK; ++ks) kr[ks] = kread(slot_s, kb, krb, ks);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + RK < KS) kr[ks + RK] = kread(slot_s, kb, krb, ks + RK);
-      mfma_s(s, kr[ks], qf[ks], ks == 0, ks == KS - 1);
-      if (COPY && (ks & 3) == 1 && (ks >> 2) < NI) copy(cp, ks >> 2, voff, roff);
+      mfma_s(sn, kr[ks], qf[ks], ks == 0, ks == KS - 1);
+      if ((ks & 1) == 0 && ks / 2 < 13) soft_step(ks / 2, s, st, false, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    rescale(first ? 1.0f : st.alpha);
+    const int vb = v_base(l);
+    uint32_t voff = 0, roff = 0;
+    if (COPY) {
+      voff = static_cast<uint32_t>(opaque(l) << 4);
+      roff = rope_voff(cp, l);
     }
 #pragma unroll
     for (int n = 0; n < RV; ++n) vf[n] = vread(slot_v, vb, n);
-    Soft st;
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
       if (n + RV < NV) vf[n + RV] = vread(slot_v, vb, n + RV);
-      mfma_o(o[n & 15], vf[n], pv[n >> 4], n == 0, false);
-      if (n >= 1 && n <= 13) soft_step(n - 1, s, st, mask, lim);
-      __builtin_amdgcn_sched_barrier(0);
+      mfma_o(o[n & 15], vf[n], st.p[n >> 4], n == 0, false);
+      if (COPY && n % 3 == 1 && n / 3 < NI) copy(cp, n / 3, voff, roff);   // copies k = 0..8 at n = 3 k + 1
     }
-    pn[0] = st.p[0];
-    pn[1] = st.p[1];
-    alpha = st.alpha;
+    s = sn;
   }
 
   // Scores of the first block (no value product yet).
@@ -1130,42 +1133,30 @@ void decode_solo_kernel(DecodeArgs a) {
   else if (nblk > 1) wait_vmcnt<DecoderSolo::NI>();
   else wait_vmcnt<0>();
   barrier_no_fence();         // block 0 visible
-  bf16x8 pb[2], pn[2];
-  float alpha;
-  {
-    f32x16 s0 = dec.scores(slot(0));
-    DecoderSolo::Soft st;
-    dec.softmax_all(s0, st, nblk == 1 && ragged, lim_last);
-    pb[0] = st.p[0];
-    pb[1] = st.p[1];
-    alpha = 1.0f;             // the value accumulators are still zero
-  }
-  // Iteration i: [wait own copies of i + 1] barrier [rescale for block i]
-  // [scores i + 1 (+ copies of i + 3 into the slot of i - 1)]
-  // [values i + softmax i + 1].  The barrier makes block i + 1 visible and
-  // certifies that every wave is done with block i - 1.
+  f32x16 s = dec.scores(slot(0));
+  // Iteration i: [wait own copies of i + 1] barrier [scores i + 1 with the
+  // softmax of i] [rescale] [values i with the copies of i + 3 into the slot
+  // of i - 1].  The barrier makes block i + 1 visible and certifies that
+  // every wave is done with block i - 1.
   int i = 0;
   for (; i + 3 < nblk; ++i) {
     const int phys = dec.page_of(i + 3);
     wait_vmcnt<DecoderSolo::NI>();
     barrier_no_fence();
-    const DecoderSolo::Copy cp = dec.copy_of(i + 3, phys, slot(i + 3));
-    dec.rescale(alpha);
-    dec.phase<true>(slot(i + 1), slot(i), pb, pn, alpha, cp, false, 0);
-    pb[0] = pn[0];
-    pb[1] = pn[1];
+    dec.phase<true>(slot(i + 1), slot(i), s, i == 0, dec.copy_of(i + 3, phys, slot(i + 3)));
   }
   for (; i + 1 < nblk; ++i) {
     if (i + 2 < nblk) wait_vmcnt<DecoderSolo::NI>();
     else wait_vmcnt<0>();
     barrier_no_fence();
-    dec.rescale(alpha);
-    dec.phase<false>(slot(i + 1), slot(i), pb, pn, alpha, DecoderSolo::Copy{}, i + 2 == nblk && ragged, lim_last);
-    pb[0] = pn[0];
-    pb[1] = pn[1];
+    dec.phase<false>(slot(i + 1), slot(i), s, i == 0, DecoderSolo::Copy{});
   }
-  dec.rescale(alpha);
-  dec.values(slot(nblk - 1), pb);
+  {
+    DecoderSolo::Soft st;
+    dec.softmax_all(s, st, ragged, lim_last);
+    dec.rescale(nblk == 1 ? 1.0f : st.alpha);
+    dec.values(slot(nblk - 1), st.p);
+  }
   dec.fence_o();
   dec.finish(ring);
 }
