@@ -6,8 +6,7 @@ Workload: one decode step of a DeepSeek-V3-shaped MLA layer, B = 32 sequences
 of 4096 cached tokens, H = 128 heads, bf16 paged latent cache (64-token pages
 in a random permutation), inputs from the seeded generator (synth.workload(2)).
 A step is the whole hot path through the C ABI:
-  mla_absorb_q -> mla_rope_append_cache -> mla_decode_partial
-  -> mla_decode_combine_absorb_out
+  mla_absorb_q_rope_append -> mla_decode_partial -> mla_decode_combine_absorb_out
 (partial + combine are mla_decode_paged split in two, so the decode kernel can
 be timed on its own with HIP events on the launch stream; the combine is fused
 with the value absorption, whose results equal mla_decode_combine followed by
@@ -170,18 +169,15 @@ def main():
         c = i % COPIES
         if ev is not None:
             ev[0].record(stream)
-        mla.mla_absorb_q(q_nope, w_uks[c], q)
+        mla.mla_absorb_q_rope_append(q_nope, w_uks[c], q_pe, kv_new, sl, bt, caches[c], mla.KV_BF16, w["theta"], q)
         if ev is not None:
             ev[1].record(stream)
-        mla.mla_rope_append_cache(q_pe, kv_new, sl, bt, caches[c], mla.KV_BF16, w["theta"], q)
-        if ev is not None:
-            ev[2].record(stream)
         mla.mla_decode_partial(q, caches[c], mla.KV_BF16, bt, sl, S, w["scale"], ws, split_tokens=split)
         if ev is not None:
-            ev[3].record(stream)
+            ev[2].record(stream)
         mla.mla_decode_combine_absorb_out(ws, sl, S, w_uvs[c], o, split_tokens=split)
         if ev is not None:
-            ev[4].record(stream)
+            ev[3].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -223,19 +219,19 @@ def main():
     # ---- per-kernel durations: the same steps launched eagerly behind a GPU
     # sleep, so every launch is queued before the GPU reaches it and the HIP
     # events on the launch stream bracket kernel time only.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     torch.cuda._sleep(200_000_000)      # long enough for every launch below to be queued first
     for i in range(args.steps):
         step(i, events[i])
     torch.cuda.synchronize()
-    names = ["absorb_q", "rope_append", "decode", "combine_absorb_out"]
+    names = ["absorb_q_rope_append", "decode", "combine_absorb_out"]
     per = {n: [] for n in names}
     for ev in events:
         for k, n in enumerate(names):
             per[n].append(ev[k].elapsed_time(ev[k + 1]) * 1e3)     # us
     avg_us = {n: float(np.mean(v)) for n, v in per.items()}
-    eager_step_us = float(np.mean([ev[0].elapsed_time(ev[4]) * 1e3 for ev in events]))
+    eager_step_us = float(np.mean([ev[0].elapsed_time(ev[3]) * 1e3 for ev in events]))
 
     cache_bytes = B * S * ROW_BYTES                    # algorithmic: every cached row read once
     flops = 2.0 * B * H * S * (576 + 512)

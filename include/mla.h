@@ -120,6 +120,20 @@ int mla_rope_append_cache(const void *q_pe, const void *kv_new, const int32_t *s
                           void *stream);
 
 /*
+ * mla_absorb_q followed by mla_rope_append_cache in a single launch (the
+ * query side of one decode step): q[:, :, 0:d_c] = q_nope . W_UK,
+ * q[:, :, d_c:d_c+d_r] = RoPE(q_pe, p_b) and the cache row of every sequence
+ * appended, with exactly the arithmetic of the two calls (results are
+ * bit-identical to them).  Arguments, layouts, requirements and errors are
+ * those of the two calls.  Reads of q_pe / kv_new and writes of q / kv_cache
+ * must not overlap.
+ */
+int mla_absorb_q_rope_append(const void *q_nope, const void *w_uk, const void *q_pe, const void *kv_new,
+                             const int32_t *seq_lens, const int32_t *block_table, int max_blocks_per_seq,
+                             void *kv_cache, int kv_dtype, int num_blocks, int block_size, float rope_theta,
+                             void *q, int B, int H, int d_nope, int d_c, int d_r, void *stream);
+
+/*
  * Bytes of the split-KV workspace for these sizes: partial outputs
  * o_part[B][n_chunks][H][512] bf16 followed (at the next 256-byte boundary)
  * by lse_part[B][n_chunks][H] fp32, n_chunks = ceil(max_seq_len / split).

@@ -21,7 +21,7 @@ __all__ = [
     "FP8_ROW_BYTES", "library_path", "lib", "abi_version",
     "mla_absorb_q", "mla_rope_append_cache", "mla_decode_paged", "mla_absorb_out",
     "mla_decode_workspace_bytes", "mla_decode_split_tokens", "mla_decode_partial", "mla_decode_combine",
-    "mla_decode_combine_absorb_out",
+    "mla_decode_combine_absorb_out", "mla_absorb_q_rope_append",
 ]
 
 KV_BF16 = 0
@@ -67,6 +67,9 @@ def lib():
     L.mla_rope_append_cache.argtypes = [vp, vp, i32p, i32p, c_int, vp, c_int, c_int, c_int, c_float,
                                         vp, c_int, c_int, c_int, c_int, vp]
     L.mla_rope_append_cache.restype = c_int
+    L.mla_absorb_q_rope_append.argtypes = [vp, vp, vp, vp, i32p, i32p, c_int, vp, c_int, c_int, c_int, c_float,
+                                           vp, c_int, c_int, c_int, c_int, c_int, vp]
+    L.mla_absorb_q_rope_append.restype = c_int
     L.mla_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
     L.mla_decode_workspace_bytes.restype = c_size
     L.mla_decode_split_tokens.argtypes = [c_int, c_int, c_int]
@@ -137,6 +140,22 @@ def mla_rope_append_cache(q_pe, kv_new, seq_lens, block_table, kv_cache, kv_dtyp
         _ptr(q_pe), _ptr(kv_new), _ptr(seq_lens), _ptr(block_table), block_table.shape[1],
         _ptr(kv_cache), int(kv_dtype), kv_cache.shape[0], kv_cache.shape[1], float(rope_theta),
         _ptr(q), B, H, kv_new.shape[1] - dr, dr, _stream(stream)))
+
+
+def mla_absorb_q_rope_append(q_nope, w_uk, q_pe, kv_new, seq_lens, block_table, kv_cache, kv_dtype, rope_theta, q,
+                             stream=None):
+    """mla_absorb_q then mla_rope_append_cache in one launch (bit-identical results)."""
+    B, H, dn = q_nope.shape
+    dr = q_pe.shape[2]
+    for t, n in ((q_nope, "q_nope"), (w_uk, "w_uk"), (q_pe, "q_pe"), (kv_new, "kv_new"), (q, "q")):
+        _dense(t, n, torch.bfloat16)
+    _dense(seq_lens, "seq_lens", torch.int32)
+    _dense(block_table, "block_table", torch.int32)
+    _dense(kv_cache, "kv_cache")
+    _check("mla_absorb_q_rope_append", lib().mla_absorb_q_rope_append(
+        _ptr(q_nope), _ptr(w_uk), _ptr(q_pe), _ptr(kv_new), _ptr(seq_lens), _ptr(block_table), block_table.shape[1],
+        _ptr(kv_cache), int(kv_dtype), kv_cache.shape[0], kv_cache.shape[1], float(rope_theta),
+        _ptr(q), B, H, dn, w_uk.shape[2], dr, _stream(stream)))
 
 
 def mla_decode_workspace_bytes(B, H, max_seq_len, split_tokens=0) -> int:

@@ -21,6 +21,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "rope.h"
 
 namespace mla {
 namespace {
@@ -35,22 +36,16 @@ __device__ __forceinline__ int wsw(int k) {
   return NT == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
 }
 
-template <int K, int N, int NT, int OUT_ROW>
-__global__ __launch_bounds__(NT * 2) void absorb_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out,
-                                                        int B, int H) {
+// Weight tile W[h][0:K][n0:n0+NT] -> LDS (row k, position p <- chunk
+// p ^ wsw(k) of the row) with 16-byte DMA copies; the caller waits.
+template <int K, int N, int NT>
+__device__ __forceinline__ void absorb_load_weights(const uint16_t *w, int h, int n0, uint8_t *tile, int wave,
+                                                    int lane) {
   constexpr int CPR = NT * 2 / 16;                      // 16-byte chunks per tile row
   constexpr int CHUNKS = K * CPR;
   constexpr int NWAVE = NT / 32;
   constexpr int PER_WAVE = CHUNKS / (64 * NWAVE);       // DMA copies per wave
   static_assert(CHUNKS % (64 * NWAVE) == 0, "tile must split evenly over the waves");
-  __shared__ __attribute__((aligned(16))) uint8_t tile[K * NT * 2];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * NT;
-  const int h = blockIdx.y;
-
-  // ---- weight tile -> LDS (row k, position p <- chunk p ^ wsw(k) of the row)
   const uint8_t *wg = reinterpret_cast<const uint8_t *>(w + (static_cast<size_t>(h) * K) * N + n0);
   const uint32_t tile_lds = lds_addr(tile);
 #pragma unroll 4
@@ -61,44 +56,119 @@ __global__ __launch_bounds__(NT * 2) void absorb_kernel(const uint16_t *act, con
     const int c = (p % CPR) ^ wsw<NT>(k);
     dma16(wg + static_cast<size_t>(k) * N * 2 + c * 16, __builtin_amdgcn_readfirstlane(tile_lds + base * 16));
   }
-  wait_vmcnt<0>();
-  __syncthreads();
+}
 
-  // ---- per-lane LDS offsets of the transposed B reads (lane 16g + q reads
-  // rows 8 (g >> 1) + q / 4 (+4 for the second read) of each 16-row k-step,
-  // columns 32 wave + 16 (g & 1) + 4 (q & 3) .. +4)
+// Activations of batch tile b0 (A operand, K-contiguous): lane (row r, half
+// hl) holds act[b0 + r, h, 16 kb + 8 hl .. + 8] for every k-step kb; rows
+// past the batch read as zero.
+template <int K>
+__device__ __forceinline__ void absorb_load_act(const uint16_t *act, int B, int H, int h, int b0, int lane,
+                                                u32x4 (&av)[K / 16]) {
+  const int r = lane & 31, hl = lane >> 5;
+  const bool aval = r < B - b0;
+  const uint16_t *ap = act + (static_cast<size_t>(b0 + (aval ? r : 0)) * H + h) * K + hl * 8;
+#pragma unroll
+  for (int kb = 0; kb < K / 16; ++kb) {
+    av[kb] = *reinterpret_cast<const u32x4 *>(ap + kb * 16);
+    if (!aval) av[kb] = u32x4{0, 0, 0, 0};
+  }
+}
+
+// out[b0 + row, h, n0 + 32 wave + col] for one batch tile: 32x32x16 MFMAs
+// over the K-steps, the weight operand read transposed from the LDS tile
+// (lane 16 g + q reads rows 8 (g >> 1) + q / 4 (+4 for the second read) of
+// each 16-row k-step, columns 32 wave + 16 (g & 1) + 4 (q & 3) .. +4).
+template <int K, int N, int NT, int OUT_ROW>
+__device__ __forceinline__ void absorb_tile(const u32x4 (&av)[K / 16], const uint8_t *tile, uint16_t *out, int B,
+                                            int H, int h, int n0, int b0, int wave, int lane) {
   const int g = lane >> 4, q = lane & 15;
   const int krow = 8 * (g >> 1) + (q >> 2);
   const int chunk = 4 * wave + 2 * (g & 1) + ((q & 3) >> 1);
   const int boff0 = krow * (NT * 2) + ((chunk ^ wsw<NT>(krow)) << 4) + (q & 1) * 8;
   const int boff1 = (krow + 4) * (NT * 2) + ((chunk ^ wsw<NT>(krow + 4)) << 4) + (q & 1) * 8;
-
-  const int r = lane & 31, hl = lane >> 5;
-  const size_t ld_act = static_cast<size_t>(H) * K;
-  const size_t ld_out = static_cast<size_t>(H) * OUT_ROW;
-  for (int b0 = 0; b0 < B; b0 += 32) {
-    const int rows = B - b0;
-    const bool aval = r < rows;
-    const uint16_t *ap = act + (static_cast<size_t>(b0 + (aval ? r : 0)) * H + h) * K + hl * 8;
-    f32x16 acc = {};
+  f32x16 acc = {};
 #pragma unroll 8
-    for (int kb = 0; kb < K / 16; ++kb) {
-      u32x4 av = *reinterpret_cast<const u32x4 *>(ap + kb * 16);
-      if (!aval) av = u32x4{0, 0, 0, 0};
-      // rows kb*16 + ... : the swizzle depends on k & 3 / (k >> 1) & 1 only, which 16 kb keeps
-      const uint8_t *t0 = tile + kb * 16 * (NT * 2);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t0 + boff0));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t0 + boff1));
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bv, acc, 0, 0, 0);
-    }
-    // row (batch) b0 + (i/4)*8 + 4*hl + i%4, column n0 + 32 wave + r
-    uint16_t *op = out + static_cast<size_t>(b0) * ld_out + static_cast<size_t>(h) * OUT_ROW + n0 + wave * 32 + r;
+  for (int kb = 0; kb < K / 16; ++kb) {
+    // rows kb*16 + ... : the swizzle depends on k & 3 / (k >> 1) & 1 only, which 16 kb keeps
+    const uint8_t *t0 = tile + kb * 16 * (NT * 2);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t0 + boff0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t0 + boff1));
+    const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[kb]), bv, acc, 0, 0, 0);
+  }
+  // row (batch) b0 + (i/4)*8 + 4*hl + i%4, column n0 + 32 wave + r
+  const int r = lane & 31, hl = lane >> 5, rows = B - b0;
+  const size_t ld_out = static_cast<size_t>(H) * OUT_ROW;
+  uint16_t *op = out + static_cast<size_t>(b0) * ld_out + static_cast<size_t>(h) * OUT_ROW + n0 + wave * 32 + r;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = (i >> 2) * 8 + hl * 4 + (i & 3);
-      if (row < rows) op[row * ld_out] = bf16_bits(to_bf16(acc[i]));
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int row = (i >> 2) * 8 + hl * 4 + (i & 3);
+    if (row < rows) op[row * ld_out] = bf16_bits(to_bf16(acc[i]));
+  }
+}
+
+template <int K, int N, int NT, int OUT_ROW>
+__global__ __launch_bounds__(NT * 2) void absorb_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out,
+                                                        int B, int H) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[K * NT * 2];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * NT;
+  const int h = blockIdx.y;
+  absorb_load_weights<K, N, NT>(w, h, n0, tile, wave, lane);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int b0 = 0; b0 < B; b0 += 32) {
+    u32x4 av[K / 16];
+    absorb_load_act<K>(act, B, H, h, b0, lane, av);
+    absorb_tile<K, N, NT, OUT_ROW>(av, tile, out, B, H, h, n0, b0, wave, lane);
+  }
+}
+
+// The query side of a decode step in one launch: q[:, :, 0:512] =
+// q_nope . W_UK (the GEMM of absorb_kernel<128, 512, 128, 576>, grid
+// (4 column tiles, H heads)) and, while the weight tile is in flight, the
+// work of rope_append_kernel: workgroup (x, h) turns the query pairs of head
+// h for the sequences b = x (mod 4), and workgroup h * 4 + x appends the rows
+// of sequences b = h * 4 + x (mod 4 H).  The arithmetic is that of the two
+// separate launches, so the results are bit-identical to them.
+__global__ __launch_bounds__(256) void query_kernel(const uint16_t *q_nope, const uint16_t *w_uk, RopeAppendArgs ra) {
+  constexpr int K = DNOPE, N = DC, NT = 128;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[K * NT * 2];
+  __shared__ float cs[DR / 2], sn[DR / 2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * NT;
+  const int h = blockIdx.y;
+  const int B = ra.B, H = ra.H;
+  absorb_load_weights<K, N, NT>(w_uk, h, n0, tile, wave, lane);
+  u32x4 av[K / 16];
+  absorb_load_act<K>(q_nope, B, H, h, 0, lane, av);
+
+  // query rotary pairs: thread (j = tid / 32, pair i = tid % 32), sequences
+  // b = x + 4 j + 32 m
+  for (int b = blockIdx.x + 4 * (tid >> 5); b < B; b += 4 * (256 / 32)) {
+    float c, s;
+    rope_cos_sin(ra, rope_position(ra.seq_lens[b]), tid & 31, c, s);
+    rope_query_pair(ra, b, h, tid & 31, c, s);
+  }
+  // cache rows
+  const int nwg = gridDim.x * gridDim.y;
+  for (int b = h * gridDim.x + blockIdx.x; b < B; b += nwg) {
+    const int S = ra.seq_lens[b];
+    if (S <= 0) continue;
+    __syncthreads();   // cs / sn free again
+    if (tid < DR / 2) rope_cos_sin(ra, rope_position(S), tid, cs[tid], sn[tid]);
+    __syncthreads();
+    append_row(ra, b, S, tid, cs, sn);
+  }
+
+  wait_vmcnt<0>();
+  __syncthreads();
+  absorb_tile<K, N, NT, DROW>(av, tile, ra.q, B, H, h, n0, 0, wave, lane);
+  for (int b0 = 32; b0 < B; b0 += 32) {
+    absorb_load_act<K>(q_nope, B, H, h, b0, lane, av);
+    absorb_tile<K, N, NT, DROW>(av, tile, ra.q, B, H, h, n0, b0, wave, lane);
   }
 }
 
@@ -290,6 +360,11 @@ hipError_t launch_combine_absorb_out(const CombineOutArgs &args, hipStream_t str
 hipError_t launch_absorb_q(const uint16_t *q_nope, const uint16_t *w_uk, uint16_t *q, int B, int H,
                            hipStream_t stream) {
   absorb_kernel<DNOPE, DC, 128, DROW><<<dim3(DC / 128, H), 256, 0, stream>>>(q_nope, w_uk, q, B, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_query(const uint16_t *q_nope, const uint16_t *w_uk, const RopeAppendArgs &ra, hipStream_t stream) {
+  query_kernel<<<dim3(DC / 128, ra.H), 256, 0, stream>>>(q_nope, w_uk, ra);
   return hipGetLastError();
 }
 

@@ -79,10 +79,12 @@ int mla_absorb_q(const void *q_nope, const void *w_uk, void *q, int B, int H, in
                                         static_cast<uint16_t *>(q), B, H, static_cast<hipStream_t>(stream)));
 }
 
-int mla_rope_append_cache(const void *q_pe, const void *kv_new, const int32_t *seq_lens,
-                          const int32_t *block_table, int max_blocks_per_seq, void *kv_cache, int kv_dtype,
-                          int num_blocks, int block_size, float rope_theta, void *q, int B, int H, int d_c,
-                          int d_r, void *stream) {
+namespace {
+
+// Validation and argument block of mla_rope_append_cache; MLA_OK or an error.
+int rope_args(const void *q_pe, const void *kv_new, const int32_t *seq_lens, const int32_t *block_table,
+              int max_blocks_per_seq, void *kv_cache, int kv_dtype, int num_blocks, int block_size,
+              float rope_theta, void *q, int B, int H, int d_c, int d_r, mla::RopeAppendArgs *a) {
   if (!aligned16(q_pe) || !aligned16(kv_new) || !aligned16(seq_lens) || !aligned16(block_table) ||
       !aligned16(kv_cache) || !aligned16(q) || B < 1 || H < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
       !(rope_theta > 0.0f) || !isfinite(rope_theta))
@@ -90,20 +92,47 @@ int mla_rope_append_cache(const void *q_pe, const void *kv_new, const int32_t *s
   if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_INVALID_ARGUMENT;
   if (d_c != MLA_D_C || d_r != MLA_D_R || block_size != MLA_BLOCK_SIZE)
     return MLA_ERR_UNSUPPORTED;
-  mla::RopeAppendArgs a;
-  a.q_pe = static_cast<const uint16_t *>(q_pe);
-  a.kv_new = static_cast<const uint16_t *>(kv_new);
-  a.seq_lens = seq_lens;
-  a.block_table = block_table;
-  a.max_blocks = max_blocks_per_seq;
-  a.cache = static_cast<uint8_t *>(kv_cache);
-  a.kv_fp8 = kv_dtype == MLA_KV_FP8_E4M3;
+  a->q_pe = static_cast<const uint16_t *>(q_pe);
+  a->kv_new = static_cast<const uint16_t *>(kv_new);
+  a->seq_lens = seq_lens;
+  a->block_table = block_table;
+  a->max_blocks = max_blocks_per_seq;
+  a->cache = static_cast<uint8_t *>(kv_cache);
+  a->kv_fp8 = kv_dtype == MLA_KV_FP8_E4M3;
   for (int i = 0; i < MLA_D_R / 2; ++i)
-    a.inv_freq[i] = std::pow(static_cast<double>(rope_theta), -(2.0 * i) / static_cast<double>(MLA_D_R));
-  a.q = static_cast<uint16_t *>(q);
-  a.B = B;
-  a.H = H;
+    a->inv_freq[i] = std::pow(static_cast<double>(rope_theta), -(2.0 * i) / static_cast<double>(MLA_D_R));
+  a->q = static_cast<uint16_t *>(q);
+  a->B = B;
+  a->H = H;
+  return MLA_OK;
+}
+
+}  // namespace
+
+int mla_rope_append_cache(const void *q_pe, const void *kv_new, const int32_t *seq_lens,
+                          const int32_t *block_table, int max_blocks_per_seq, void *kv_cache, int kv_dtype,
+                          int num_blocks, int block_size, float rope_theta, void *q, int B, int H, int d_c,
+                          int d_r, void *stream) {
+  mla::RopeAppendArgs a;
+  const int st = rope_args(q_pe, kv_new, seq_lens, block_table, max_blocks_per_seq, kv_cache, kv_dtype, num_blocks,
+                           block_size, rope_theta, q, B, H, d_c, d_r, &a);
+  if (st != MLA_OK) return st;
   return status_of(mla::launch_rope_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int mla_absorb_q_rope_append(const void *q_nope, const void *w_uk, const void *q_pe, const void *kv_new,
+                             const int32_t *seq_lens, const int32_t *block_table, int max_blocks_per_seq,
+                             void *kv_cache, int kv_dtype, int num_blocks, int block_size, float rope_theta,
+                             void *q, int B, int H, int d_nope, int d_c, int d_r, void *stream) {
+  if (!aligned16(q_nope) || !aligned16(w_uk)) return MLA_ERR_INVALID_ARGUMENT;
+  mla::RopeAppendArgs a;
+  const int st = rope_args(q_pe, kv_new, seq_lens, block_table, max_blocks_per_seq, kv_cache, kv_dtype, num_blocks,
+                           block_size, rope_theta, q, B, H, d_c, d_r, &a);
+  if (st != MLA_OK) return st;
+  if (B > 65535 * 32 || H > 65535) return MLA_ERR_UNSUPPORTED;
+  if (d_nope != MLA_D_NOPE) return MLA_ERR_UNSUPPORTED;
+  return status_of(mla::launch_query(static_cast<const uint16_t *>(q_nope), static_cast<const uint16_t *>(w_uk), a,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int mla_decode_split_tokens(int B, int H, int max_seq_len) {

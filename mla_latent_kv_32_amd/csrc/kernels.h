@@ -79,5 +79,7 @@ struct RopeAppendArgs {
 };
 
 hipError_t launch_rope_append(const RopeAppendArgs &a, hipStream_t stream);
+// mla_absorb_q and mla_rope_append_cache in one launch (ra.q receives both parts).
+hipError_t launch_query(const uint16_t *q_nope, const uint16_t *w_uk, const RopeAppendArgs &ra, hipStream_t stream);
 
 }  // namespace mla

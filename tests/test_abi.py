@@ -122,6 +122,25 @@ def test_validation_rejects_before_launch():
     assert fused(FAKE, 1 << 30, FAKE, 256, 64, FAKE, FAKE, NULL, NULL, 2, 70000, 512, 128, NULL) == -2
 
 
+def test_fused_query_call_validates_like_its_parts():
+    L = mla.lib()
+    q = L.mla_absorb_q_rope_append
+
+    def call(qn=FAKE, wuk=FAKE, qpe=FAKE, kvn=FAKE, sl=FAKE, bt=FAKE, mb=4, kv=FAKE, dt=0, nb=16, bs=64,
+             theta=10000.0, qo=FAKE, B=2, H=128, dn=128, dc=512, dr=64):
+        return q(qn, wuk, qpe, kvn, sl, bt, mb, kv, dt, nb, bs, ctypes.c_float(theta), qo, B, H, dn, dc, dr, NULL)
+
+    assert call(qn=NULL) == -1
+    assert call(wuk=FAKE + 2) == -1
+    assert call(qpe=NULL) == -1
+    assert call(dt=7) == -1
+    assert call(theta=0.0) == -1
+    assert call(B=0) == -1
+    assert call(dn=64) == -2
+    assert call(dc=256) == -2
+    assert call(bs=32) == -2
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mla, "_LIB", None)
     monkeypatch.setenv("MLA_LIBRARY", str(tmp_path / "missing.so"))

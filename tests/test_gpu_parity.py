@@ -194,6 +194,35 @@ def test_rope_append_fp8():
     _append_and_check(w)
 
 
+def _fused_query_cases():
+    lens45 = [0, 1, 2, 63, 64, 65, 100000] + [int(x) for x in np.arange(38) * 97 + 5]
+    return [synth.workload(1), synth.workload(2),
+            synth.gaussian_workload(60, B=45, H=3, seq_lens=lens45),
+            synth.gaussian_workload(61, B=9, H=20, seq_lens=[0, 1, 64, 65, 500, 8192, 3, 129, 4000],
+                                    kv_dtype=synth.KV_FP8)]
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_absorb_q_rope_append_fused_equals_separate(case):
+    """The one-launch query side gives exactly what mla_absorb_q + mla_rope_append_cache give."""
+    w = _fused_query_cases()[case]
+    B, H = w["B"], w["H"]
+    key = "cache_step" if "cache_step" in w else "cache_full"
+    pool = w[key]
+    dev = (lambda x: to_dev_bf16(x)) if w["kv_dtype"] == synth.KV_BF16 else (lambda x: to_dev(x))
+    sl, bt = to_dev(w["seq_lens"]), to_dev(w["block_table"])
+    qn, wuk = to_dev_bf16(w["q_nope"]), to_dev_bf16(w["w_uk"])
+    qpe, kvn = to_dev_bf16(w["q_pe"]), to_dev_bf16(w["kv_new"])
+    q1, kv1 = nan_bf16(B, H, 576), dev(pool)
+    mla.mla_absorb_q(qn, wuk, q1)
+    mla.mla_rope_append_cache(qpe, kvn, sl, bt, kv1, w["kv_dtype"], w["theta"], q1)
+    q2, kv2 = nan_bf16(B, H, 576), dev(pool)
+    mla.mla_absorb_q_rope_append(qn, wuk, qpe, kvn, sl, bt, kv2, w["kv_dtype"], w["theta"], q2)
+    torch.cuda.synchronize()
+    assert torch.equal(q1.view(torch.int16), q2.view(torch.int16))
+    assert torch.equal(kv1.view(torch.uint8), kv2.view(torch.uint8))
+
+
 # --------------------------------------------------------------------- K3/K4
 def test_decode_workload1_all_heads():
     w = synth.workload(1)
