@@ -50,10 +50,10 @@ COPIES = 3
 # reported only while that source is unchanged.
 DECODE_TRAFFIC = {
     "sources_sha256": {
-        "mla_latent_kv_32_amd/csrc/decode.hip": "8ed0a26dc51d2b4ee4ea106521cc4fba9089f835c03880ed835abbf89324ceb8",
+        "mla_latent_kv_32_amd/csrc/decode.hip": "8ceb1adcf7b1c381908b91df38b88c93a0679a126c5f8dde5f903a183c9c8851",
         "mla_latent_kv_32_amd/csrc/common.h": "9119e84c6a1340e11077a316e161bf93b3bc7e62a88e7300f6ef510da895fad9",
     },
-    "fetch_kib": 76356.8,
+    "fetch_kib": 76228.3,
     "write_kib": 32896.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
