@@ -868,6 +868,117 @@ struct DecoderSolo {
     s = sn;
   }
 
+  // ---- fp8 cache.  A packed row is [512 E4M3 codes | 64 bf16 rotary values
+  // | 4 fp32 group scales] (656 bytes) and the 32 rows of a block are
+  // contiguous in the page.  Wave w copies rows 8 w .. 8 w + 7 of a block
+  // unchanged into a staging buffer (5248 contiguous bytes, six wave-wide
+  // copies) and later expands exactly those rows into the bf16 slot layout,
+  // so copy and expansion need no workgroup barrier between them.
+  static constexpr int ROWS8 = TB / NW;                            // rows per wave
+  static constexpr int CH8 = ROWS8 * FP8_ROW_BYTES / 16;           // 328 16-byte pieces
+  static constexpr int NI8 = (CH8 + 63) / 64;                      // 6 copies per wave per block
+  static constexpr int TAIL8 = CH8 - (NI8 - 1) * 64;               // lanes of the last copy
+  static_assert(ROWS8 * FP8_ROW_BYTES % 16 == 0 && 3 * NI8 <= 63, "fp8 copy ranges");
+  __device__ __forceinline__ void copy8(int blk, int phys, uint8_t *stage, int k) const {
+    const uint8_t *src = a.cache + (static_cast<size_t>(phys) * PAGE + ((t_begin + blk * TB) & 32) + wave * ROWS8) *
+                                       FP8_ROW_BYTES;
+    const int ln = lane_id();
+    if (k + 1 < NI8 || ln < TAIL8)
+      dma16_s(static_cast<uint32_t>((k * 64 + ln) * 16), src,
+              __builtin_amdgcn_readfirstlane(lds_addr(stage + wave * ROWS8 * FP8_ROW_BYTES) + k * 1024));
+  }
+  __device__ __forceinline__ void issue8(int blk, int phys, uint8_t *stage) const {
+#pragma unroll
+    for (int k = 0; k < NI8; ++k) copy8(blk, phys, stage, k);
+  }
+  // Expand row k (0..7) of this wave's share of block blk from `stage` into
+  // `slot`: latent value j = code_j * scale[j / 128], formed in fp32 (the
+  // E4M3 code converts exactly) and rounded to bf16; lane l writes 16-byte
+  // chunk l of the padded latent row.  Rows past the end of the chunk become
+  // zeros (their scores are masked; zeros keep their products finite).
+  __device__ __forceinline__ void expand8_row(int blk, const uint8_t *stage, uint8_t *slot, int k) const {
+    const int l = lane_id();
+    const int r = wave * ROWS8 + k;
+    u32x4 out = u32x4{0, 0, 0, 0};
+    if (t_begin + blk * TB + r < t_end) {
+      const uint8_t *src = stage + r * FP8_ROW_BYTES;
+      const u32x2 codes = *reinterpret_cast<const u32x2 *>(src + l * 8);
+      const float sc = *reinterpret_cast<const float *>(src + FP8_SCALE_OFF + (l >> 4) * 4);
+      bf16x8 v;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes[h]), false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes[h]), true);
+        v[4 * h + 0] = to_bf16(lo[0] * sc);
+        v[4 * h + 1] = to_bf16(lo[1] * sc);
+        v[4 * h + 2] = to_bf16(hi[0] * sc);
+        v[4 * h + 3] = to_bf16(hi[1] * sc);
+      }
+      out = __builtin_bit_cast(u32x4, v);
+    }
+    *reinterpret_cast<u32x4 *>(slot + r * S_LROW + l * 16) = out;
+  }
+  // The rotary parts of this wave's 8 rows: lane l copies chunk l % 8 of row
+  // 8 w + l / 8 (stored at chunk (l % 8) ^ fr(row) of the rotary region).
+  __device__ __forceinline__ void expand8_rope(int blk, const uint8_t *stage, uint8_t *slot) const {
+    const int l = lane_id();
+    const int r = wave * ROWS8 + (l >> 3), c = l & 7;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (t_begin + blk * TB + r < t_end) v = *reinterpret_cast<const u32x4 *>(stage + r * FP8_ROW_BYTES + DC + c * 16);
+    *reinterpret_cast<u32x4 *>(slot + S_LAT + r * ROPE_BYTES + ((c ^ fr(r)) << 4)) = v;
+  }
+  __device__ __forceinline__ void expand8(int blk, const uint8_t *stage, uint8_t *slot) const {
+#pragma unroll
+    for (int k = 0; k < ROWS8; ++k) expand8_row(blk, stage, slot, k);
+    expand8_rope(blk, stage, slot);
+  }
+
+  // fp8 pipeline step on blocks i (values, `slot_v`) and i + 1 (scores,
+  // `slot_s`): part A as in phase(), with the copies of block i + 3 into
+  // `stage_n` (COPY) spread over its first MFMAs; part B: the value MFMAs of
+  // block i with [wait for this wave's copies of block i + 2] [expansion of
+  // block i + 2 from `stage_e` into `slot_e`, a row every four MFMAs]
+  // (EXPAND) spread over them.
+  template <bool COPY, bool EXPAND>
+  __device__ __forceinline__ void phase8(const uint8_t *slot_s, const uint8_t *slot_v, f32x16 &s, bool first,
+                                         int blk_n, int phys_n, uint8_t *stage_n, int blk_e, const uint8_t *stage_e,
+                                         uint8_t *slot_e) {
+    const int l = lane_id();
+    const int kb = k_base(l), krb = kr_base(l);
+    constexpr int RK = 4, RV = 4, NV = 2 * NT;
+    bf16x8 kr[KS], vf[NV];
+    f32x16 sn;
+    Soft st;
+#pragma unroll
+    for (int ks = 0; ks < RK; ++ks) kr[ks] = kread(slot_s, kb, krb, ks);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + RK < KS) kr[ks + RK] = kread(slot_s, kb, krb, ks + RK);
+      mfma_s(sn, kr[ks], qf[ks], ks == 0, ks == KS - 1);
+      if ((ks & 1) == 0 && ks / 2 < 13) soft_step(ks / 2, s, st, false, 0);
+      if (COPY && (ks & 1) == 1 && ks / 2 < NI8) copy8(blk_n, phys_n, stage_n, ks / 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    rescale(first ? 1.0f : st.alpha);
+    const int vb = v_base(l);
+#pragma unroll
+    for (int n = 0; n < RV; ++n) vf[n] = vread(slot_v, vb, n);
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      if (n + RV < NV) vf[n + RV] = vread(slot_v, vb, n + RV);
+      mfma_o(o[n & 15], vf[n], st.p[n >> 4], n == 0, false);
+      if (EXPAND) {
+        if (n == 0) {
+          if (COPY) wait_vmcnt<NI8>();
+          else wait_vmcnt<0>();
+        }
+        if ((n & 3) == 1) expand8_row(blk_e, stage_e, slot_e, n >> 2);
+        if (n == NV - 1) expand8_rope(blk_e, stage_e, slot_e);
+      }
+    }
+    s = sn;
+  }
+
   // Scores of the first block (no value product yet).
   __device__ __forceinline__ f32x16 scores(const uint8_t *slot) const {
     const int l = lane_id();
@@ -1161,6 +1272,98 @@ void decode_solo_kernel(DecodeArgs a) {
   dec.finish(ring);
 }
 
+// fp8 cache, one wave per SIMD.  Three bf16 slots (block i in slot i % 3)
+// and two staging buffers of packed rows (block i in stage i % 2).
+// Iteration i: barrier (block i + 1's expansion visible; every wave done with
+// block i - 1, whose slot receives block i + 2) [scores i + 1 with the
+// softmax of i and the copies of block i + 3 into the stage of block i + 1
+// (expanded by this same wave one step earlier)] [rescale] [values i with:
+// wait for this wave's copies of block i + 2, expansion of block i + 2].
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void decode_solo_fp8_kernel(DecodeArgs a) {
+  constexpr int RING = 3 * S_SLOT;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[RING + 2 * STAGE_BYTES];
+  static_assert(DecoderSolo::HEADS * LAT_BYTES <= RING + 2 * STAGE_BYTES, "the output tile is staged in LDS");
+  uint8_t *const stage0 = lds + RING;
+
+  int item = blockIdx.x;
+  if ((gridDim.x & 7) == 0) item = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int b = item / a.n_splits;
+  const int split = item - b * a.n_splits;
+  const int S = a.seq_lens[b];
+  const int t_begin = split * a.split_tokens;
+  const int t_end = min(S, t_begin + a.split_tokens);
+
+  if (t_begin >= t_end) {
+    if (a.direct) {
+      const int t = threadIdx.x;
+      const int head = blockIdx.y * DecoderSolo::HEADS + t / 2;      // 2 threads per head
+      if (head < a.H) {
+        uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + (t % 2) * (DC / 2);
+        for (int c = 0; c < DC / 2; c += 8) *reinterpret_cast<u32x4 *>(dst + c) = u32x4{0, 0, 0, 0};
+        if (t % 2 == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = -INFINITY;
+      }
+    }
+    return;
+  }
+
+  DecoderSolo dec(a, b, split, t_begin, t_end);
+  dec.begin();
+  const int nblk = (t_end - t_begin + TB - 1) / TB;
+  const int lim_last = t_end - t_begin - (nblk - 1) * TB - 16 * (threadIdx.x >> 5 & 1);
+  const bool ragged = (t_end - t_begin) % TB != 0;
+  auto slot = [&](int i) { return lds + (i % 3) * S_SLOT; };
+  auto stage = [&](int i) { return stage0 + (i & 1) * STAGE_BYTES; };
+  constexpr int NI8 = DecoderSolo::NI8;
+  // Blocks 0 and 1 and the query go out together; block 0 is expanded first,
+  // then block 2 is requested into its stage and block 1 expanded.
+  dec.issue8(0, dec.page_of(0), stage(0));
+  dec.load_q();
+  if (nblk > 1) {
+    dec.issue8(1, dec.page_of(1), stage(1));
+    wait_vmcnt<NI8>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  dec.expand8(0, stage(0), slot(0));
+  if (nblk > 1) {
+    if (nblk > 2) {
+      dec.issue8(2, dec.page_of(2), stage(0));
+      wait_vmcnt<NI8>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    dec.expand8(1, stage(1), slot(1));
+  }
+  barrier_lds();              // blocks 0 and 1 visible
+  f32x16 s = dec.scores(slot(0));
+  int i = 0;
+  for (; i + 3 < nblk; ++i) {
+    const int phys = dec.page_of(i + 3);
+    barrier_lds();
+    dec.phase8<true, true>(slot(i + 1), slot(i), s, i == 0, i + 3, phys, stage(i + 3), i + 2, stage(i + 2),
+                           slot(i + 2));
+  }
+  if (i + 2 < nblk) {
+    barrier_lds();
+    dec.phase8<false, true>(slot(i + 1), slot(i), s, i == 0, 0, 0, nullptr, i + 2, stage(i + 2), slot(i + 2));
+    ++i;
+  }
+  if (i + 1 < nblk) {
+    barrier_lds();
+    dec.phase8<false, false>(slot(i + 1), slot(i), s, i == 0, 0, 0, nullptr, 0, nullptr, nullptr);
+    ++i;
+  }
+  {
+    DecoderSolo::Soft st;
+    dec.softmax_all(s, st, ragged, lim_last);
+    dec.rescale(nblk == 1 ? 1.0f : st.alpha);
+    dec.values(slot(nblk - 1), st.p);
+  }
+  dec.fence_o();
+  dec.finish(lds);
+}
+
 // fp8 cache.  Packed rows are copied into a staging buffer one step ahead
 // and expanded to bf16 into a ring of three slots one block before use; the
 // score, softmax and value phases are those of the bf16 kernel.
@@ -1337,6 +1540,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int hpw = decode_heads_per_wave(a.H);
   const int groups = (a.H + hpw * nw - 1) / (hpw * nw);
   dim3 grid(a.B * a.n_splits, groups);
+  if (a.kv_fp8 && nw == 8) {
+    decode_solo_fp8_kernel<<<grid, 256, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   if (a.kv_fp8) {
     switch (nw) {
       case 2: decode_fp8_kernel<DecoderPair<2>, 1><<<grid, 128, 0, stream>>>(a); break;
