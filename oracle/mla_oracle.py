@@ -27,7 +27,8 @@ Readings where the pages are silent (each is listed with its reason in the
 design notes): interleaved RoPE pairs; the decode query sits at position
 S-1 and attends to itself; softmax scale 1/sqrt(d_nope + d_rope) on the sum of
 the latent and rotary score parts; empty sequence -> zero output and
-lse = -inf; fp8 = OCP E4M3 (max 448) with one fp32 scale per 128-wide group,
+lse = -inf; several new tokens decoded together see the cache causally (query
+j of q_len at position S-q_len+j sees rows 0..S-q_len+j); fp8 = OCP E4M3 (max 448) with one fp32 scale per 128-wide group,
 scale = amax/448 in fp32 and codes by round-to-nearest-even after an fp32
 division.
 
@@ -243,6 +244,43 @@ def decode_absorbed(q_lat, q_rot, c, kr, scale, with_magnitude=False):
     return o_lat, lse
 
 
+def decode_multi_token(q_lat, q_rot, c, kr, scale):
+    """Decode of q_len new tokens of one sequence against its whole cache.
+
+    [Riju] "Interaction with quantisation and paging": speculative decoding
+    and multi-token prediction heads use the latent cache like any other
+    decode; read here as the causal rule of decoder attention ([Su] MHA
+    equation with the decoder's causal mask): the new tokens are the last
+    q_len of the S cached rows, and query j (position S - q_len + j) sees the
+    rows t <= S - q_len + j.
+        q_lat [q_len, H, d_c], q_rot [q_len, H, d_r]; c [S, d_c], kr [S, d_r]
+        s[j,h,t] = scale * (q_lat[j,h] . c_t + q_rot[j,h] . kr_t)  (visible t)
+        o_lat[j,h] = sum_t softmax(s[j,h])_t c_t,  lse[j,h] = log sum_t e^s
+    A query that sees no row (S - q_len + j < 0) gives zeros and lse = -inf.
+    Written with an explicit visibility mask over all S rows.
+    """
+    q_lat = np.asarray(q_lat, F64)
+    q_rot = np.asarray(q_rot, F64)
+    c = np.asarray(c, F64)
+    kr = np.asarray(kr, F64)
+    q_len, H = q_lat.shape[:2]
+    S = c.shape[0]
+    s = scale * (q_lat.reshape(q_len * H, -1) @ c.T + q_rot.reshape(q_len * H, -1) @ kr.T)
+    s = s.reshape(q_len, H, S)
+    last = S - q_len + np.arange(q_len)                     # last visible row of query j
+    visible = np.arange(S)[None, :] <= last[:, None]        # [q_len, S]
+    vis = np.broadcast_to(visible[:, None, :], s.shape)
+    any_vis = vis.any(axis=-1)
+    m = np.where(any_vis, np.where(vis, s, -np.inf).max(axis=-1, initial=-np.inf), 0.0)
+    e = np.where(vis, np.exp(np.where(vis, s, 0.0) - m[..., None]), 0.0)
+    z = e.sum(axis=-1)
+    zs = np.where(any_vis, z, 1.0)
+    o_lat = (e / zs[..., None]).reshape(q_len * H, S) @ c if S else np.zeros((q_len * H, c.shape[1]))
+    o_lat = np.where(any_vis[..., None], o_lat.reshape(q_len, H, -1), 0.0)
+    lse = np.where(any_vis, m + np.log(zs), -np.inf)
+    return o_lat, lse
+
+
 def combine_partials(o_parts, lse_parts):
     """Merge attention over disjoint token chunks from (o_c, lse_c) pairs.
 
@@ -306,6 +344,20 @@ def reference_decode(inp, b, heads=None, with_magnitude=False):
     q = bf16_to_f64(inp["q_decode"][b])
     heads = list(range(q.shape[0])) if heads is None else list(heads)
     return decode_absorbed(q[heads, :512], q[heads, 512:], c, kr, inp["scale"], with_magnitude)
+
+
+def reference_decode_multi(inp, q_multi, b, heads=None):
+    """Multi-token decode reference for sequence b: queries q_multi [B, q_len, H, 576]
+    (bf16 bits) against all S_b rows of inp["cache_full"] (decode_multi_token).
+    Returns (o_lat [q_len, h, 512], lse [q_len, h])."""
+    S = int(inp["seq_lens"][b])
+    fp8 = inp["kv_dtype"] == 1
+    rows = gather_rows(inp["cache_full"], inp["block_table"], b, S, inp["block_size"])
+    c, kr = rows_to_latent_rope(rows, fp8)
+    q = bf16_to_f64(np.asarray(q_multi)[b])
+    heads = list(range(q.shape[1])) if heads is None else list(heads)
+    q = q[:, heads]
+    return decode_multi_token(q[..., :512], q[..., 512:], c, kr, inp["scale"])
 
 
 def reference_step(inp, b, heads=None):

@@ -292,6 +292,16 @@ def workload(cfg: int, seed: int | None = None):
     raise ValueError(f"unknown workload {cfg}")
 
 
+def multi_token_query(seed, B, q_len, H):
+    """Queries of q_len new tokens per sequence [B, q_len, H, 576] (bf16 bits),
+    drawn like the decode-only query: latent part N(0, d_nope/d_c), rotary
+    part N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    q_lat = _normal(rng, (B, q_len, H, D_C), math.sqrt(D_NOPE / D_C))
+    q_rot = _normal(rng, (B, q_len, H, D_R))
+    return f32_to_bf16_bits(np.concatenate([q_lat, q_rot], -1))
+
+
 def random_bf16(seed, shape, std=1.0):
     """Plain N(0, std^2) draw rounded to bf16 bits (stand-alone operands for single-kernel tests)."""
     return f32_to_bf16_bits(_normal(np.random.default_rng(seed), shape, std))

@@ -400,3 +400,92 @@ def test_reference_decode_empty_sequence():
     np.testing.assert_array_equal(o1, np.broadcast_to(c[0], o1.shape))
     r = oracle.reference_step(w, 0)
     assert (r["o"] == 0).all() and np.isneginf(r["lse"]).all()
+
+
+# ------------------------------------------------- multi-token decode (PIN-11)
+def _brute_multi(q, c, kr, scale):
+    """Tiny-case brute force: plain Python loops over the masked softmax."""
+    q_len, H = len(q), len(q[0])
+    S = len(c)
+    o = [[None] * H for _ in range(q_len)]
+    lse = [[None] * H for _ in range(q_len)]
+    for j in range(q_len):
+        last = S - q_len + j
+        for h in range(H):
+            qv = q[j][h]
+            sc = []
+            for t in range(S):
+                if t > last:
+                    continue
+                dot = sum(qv[d] * c[t][d] for d in range(len(c[t])))
+                dot += sum(qv[len(c[t]) + d] * kr[t][d] for d in range(len(kr[t])))
+                sc.append((t, scale * dot))
+            if not sc:
+                o[j][h] = [0.0] * len(c[0])
+                lse[j][h] = -math.inf
+                continue
+            z = sum(math.exp(v) for _, v in sc)
+            o[j][h] = [sum(math.exp(v) / z * c[t][d] for t, v in sc) for d in range(len(c[0]))]
+            lse[j][h] = math.log(z)
+    return np.array(o), np.array(lse)
+
+
+@pytest.mark.parametrize("S,q_len", [(6, 3), (3, 3), (2, 4), (1, 1), (9, 1)])
+def test_multi_token_matches_brute_force(S, q_len):
+    rng = np.random.default_rng(100 + 10 * S + q_len)
+    H, dc, dr = 2, 5, 3
+    c, kr = rng.standard_normal((S, dc)), rng.standard_normal((S, dr))
+    q = rng.standard_normal((q_len, H, dc + dr))
+    o, lse = oracle.decode_multi_token(q[..., :dc], q[..., dc:], c, kr, 0.6)
+    ob, lb = _brute_multi(q.tolist(), c.tolist(), kr.tolist(), 0.6)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(lb))
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(lse[fin], lb[fin], rtol=1e-12)
+
+
+def test_multi_token_each_query_is_a_prefix_decode():
+    """Query j equals the single-token decode over rows 0 .. S - q_len + j."""
+    rng = np.random.default_rng(7)
+    S, q_len, H = 130, 5, 4
+    c, kr = rng.standard_normal((S, 512)), rng.standard_normal((S, 64))
+    q = rng.standard_normal((q_len, H, 576)) * 0.05
+    o, lse = oracle.decode_multi_token(q[..., :512], q[..., 512:], c, kr, 0.09)
+    for j in range(q_len):
+        n = S - q_len + j + 1
+        oj, lj = oracle.decode_absorbed(q[j, :, :512], q[j, :, 512:], c[:n], kr[:n], 0.09)
+        np.testing.assert_allclose(o[j], oj, rtol=1e-11, atol=1e-14)
+        np.testing.assert_allclose(lse[j], lj, rtol=1e-13)
+    # the last query sees every row; the first does not see the last q_len - 1
+    assert not np.allclose(o[0], oracle.decode_absorbed(q[0, :, :512], q[0, :, 512:], c, kr, 0.09)[0])
+
+
+def test_multi_token_short_sequence_and_single_query():
+    rng = np.random.default_rng(8)
+    c, kr = rng.standard_normal((1, 512)), rng.standard_normal((1, 64))
+    q = rng.standard_normal((3, 2, 576))
+    o, lse = oracle.decode_multi_token(q[..., :512], q[..., 512:], c, kr, 0.1)
+    # S = 1 < q_len: queries 0 and 1 see nothing; query 2 sees row 0 alone (weight 1)
+    assert (o[:2] == 0).all() and np.isneginf(lse[:2]).all()
+    np.testing.assert_allclose(o[2], np.broadcast_to(c[0], (2, 512)), rtol=1e-15)
+    np.testing.assert_allclose(lse[2], 0.1 * (q[2, :, :512] @ c[0] + q[2, :, 512:] @ kr[0]), rtol=1e-12)
+    # q_len = 1 is the decode of every row
+    c, kr = rng.standard_normal((40, 512)), rng.standard_normal((40, 64))
+    q = rng.standard_normal((1, 3, 576)) * 0.05
+    o, lse = oracle.decode_multi_token(q[..., :512], q[..., 512:], c, kr, 0.2)
+    o1, l1 = oracle.decode_absorbed(q[0, :, :512], q[0, :, 512:], c, kr, 0.2)
+    np.testing.assert_allclose(o[0], o1, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(lse[0], l1, rtol=1e-13)
+
+
+def test_reference_decode_multi_last_query_is_the_decode():
+    w = synth.gaussian_workload(9, B=3, H=4, seq_lens=[70, 1, 200])
+    qm = synth.multi_token_query(10, B=3, q_len=3, H=4)
+    qm[:, -1] = w["q_decode"]
+    for b in range(3):
+        o, lse = oracle.reference_decode_multi(w, qm, b)
+        od, ld = oracle.reference_decode(w, b)
+        np.testing.assert_allclose(o[-1], od, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(lse[-1], ld, rtol=1e-13)
+    o, lse = oracle.reference_decode_multi(w, qm, 1)
+    assert (o[:2] == 0).all() and np.isneginf(lse[:2]).all()
