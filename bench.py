@@ -1,6 +1,7 @@
 """MLA absorbed-decode benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --q-len 2      # multi-token decode on the same workload (one JSON line)
 
 Workload: one decode step of a DeepSeek-V3-shaped MLA layer, B = 32 sequences
 of 4096 cached tokens, H = 128 heads, bf16 paged latent cache (64-token pages
@@ -71,6 +72,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="> 1: time the multi-token decode (q_len new tokens per sequence) on the same cache")
+    ap.add_argument("--heads", type=int, default=128,
+                    help="with --q-len: heads per token (128: the DeepSeek-V3-shaped workload; other values: "
+                         "the same shape with N(0,1) entries, e.g. 16 = one GPU's share under 8-way head "
+                         "parallelism)")
     return ap.parse_args()
 
 
@@ -128,6 +135,115 @@ def cpu_baseline(w, budget_s):
     }
 
 
+def main_multi(args):
+    """--q-len > 1: the multi-token decode (mla_decode_paged_multi: decode + combine) of q_len
+    new tokens per sequence on the same workload and cache, against the alternative of
+    single-token decodes of the B * q_len virtual sequences (mla_decode_paged, same chunking),
+    which reads the cache q_len times."""
+    import torch
+    import mla_latent_kv_32_amd as mla
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    mla.lib()
+    dev = "cuda"
+    w = synth.workload(2) if args.heads == 128 else synth.gaussian_workload(2, B=32, H=args.heads,
+                                                                             seq_lens=[4096] * 32)
+    B, H = w["B"], w["H"]
+    S = int(w["seq_lens"].max())
+    L = args.q_len
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    caches = [bf16(w["cache_full"]) for _ in range(COPIES)]
+    qm_bits = synth.multi_token_query(600, B, L, H)
+    qm = bf16(qm_bits)
+    sl = torch.from_numpy(w["seq_lens"]).to(dev)
+    bt = torch.from_numpy(w["block_table"]).to(dev)
+    split = args.split_tokens or mla.mla_decode_split_tokens(B, L * H, S)
+    ws = torch.empty(max(1, mla.mla_decode_workspace_bytes(B, L * H, S, split)), dtype=torch.uint8, device=dev)
+    o = torch.empty((B, L, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, L, H), dtype=torch.float32, device=dev)
+    vlens = torch.from_numpy(np.maximum(0, w["seq_lens"][:, None] - L + 1 + np.arange(L)[None]).astype(np.int32)
+                             .reshape(-1)).to(dev)
+    vbt = torch.from_numpy(np.repeat(w["block_table"], L, axis=0)).to(dev)
+    vws = torch.empty(max(1, mla.mla_decode_workspace_bytes(B * L, H, S, split)), dtype=torch.uint8, device=dev)
+    vo = torch.empty((B * L, H, 512), dtype=torch.bfloat16, device=dev)
+    vq = qm.view(B * L, H, 576)
+    stream = torch.cuda.current_stream()
+
+    def multi(i):
+        mla.mla_decode_paged_multi(qm, caches[i % COPIES], mla.KV_BF16, bt, sl, S, w["scale"], o, lse,
+                                   split_tokens=split, workspace=ws)
+
+    def virtual(i):
+        mla.mla_decode_paged(vq, caches[i % COPIES], mla.KV_BF16, vbt, vlens, S, w["scale"], vo,
+                             split_tokens=split, workspace=vws)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(200_000_000)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3, time.perf_counter() - t0
+
+    multi_us, wall = timed(multi)
+    virtual_us, _ = timed(virtual)
+
+    import oracle
+    worst = 0.0
+    for b, heads in [(0, [0, H - 1]), (31, [H // 2])]:
+        ro, _ = oracle.reference_decode_multi(w, qm_bits, b, heads)
+        got = o[b][:, heads].float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ro)
+        assert (err <= 2e-3 + 2e-2 * np.abs(ro)).all(), "benchmarked output differs from the oracle"
+        worst = max(worst, float(err.max()))
+
+    cache_bytes = B * S * ROW_BYTES
+    flops = 2.0 * B * L * H * S * (576 + 512)
+    achieved = cache_bytes / (multi_us * 1e-6) / 1e9
+    out = {
+        "metric": f"MLA multi-token decode latent-KV GB/s, q_len={L}, H={H} B=32 ctx=4K, 1 GPU",
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(multi_us * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"multi-token decode of {L} new tokens per sequence (causal among them): B=32, "
+                        f"H={H}, context 4096, bf16 paged latent cache; mla_decode_paged_multi "
+                        f"(decode + combine launches)",
+            "B": B, "H": H, "q_len": L, "seq_len": S, "split_tokens": split, "parallelism": "single GPU",
+        },
+        "tflops": round(flops / (multi_us * 1e-6) / 1e12, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": cache_bytes,
+                     "scope": "decode + combine launches of one call (HIP events around the call)"},
+        "virtual_sequences": {"us": round(virtual_us, 3), "speedup": round(virtual_us / multi_us, 3),
+                              "what": f"mla_decode_paged on the {B * L} virtual sequences (b, j), same "
+                                      f"chunking: reads the cache {L} times"},
+        "parity": {"checked": f"o_latent of every new token for (b,h) in (0,0),(0,{H - 1}),(31,{H // 2})",
+                   "max_abs_err": worst, "ok": True},
+        "timing": {"wall_s": round(wall, 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -138,6 +254,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.q_len > 1:
+        main_multi(args)
         return
 
     import mla_latent_kv_32_amd as mla

@@ -183,6 +183,44 @@ int mla_decode_paged(const void *q, const void *kv_cache, int kv_dtype,
                      void *workspace, size_t workspace_bytes,
                      void *o_latent, float *lse, int B, int H, void *stream);
 
+/* Most new tokens per sequence that mla_decode_paged_multi takes. */
+#define MLA_MAX_Q_LEN 32
+
+/*
+ * Multi-token decode: q_len new tokens per sequence (speculative decoding,
+ * multi-token prediction heads) in one pass over the cache.  Such tokens use
+ * the latent cache like any other decode (Riju, "Interaction with
+ * quantisation and paging"); they attend causally among themselves, the rule
+ * of decoder attention (Su, MHA equation with the causal mask).  The new
+ * tokens are the last q_len rows of each sequence (already appended and
+ * counted in seq_lens); query j sits at position seq_lens[b] - q_len + j and
+ * sees the rows t <= seq_lens[b] - q_len + j:
+ *   s[b,j,h,t]      = softmax_scale * (q[b,j,h,:] . row_t)
+ *   o_latent[b,j,h] = sum_t softmax(s)_t row_t[0:d_c],  lse = log sum_t exp(s_t)
+ *   q          [B, q_len, H, 576] bf16
+ *   o_latent   [B, q_len, H, 512] bf16 output
+ *   lse        [B, q_len, H] fp32 natural-log output, or NULL
+ *   q_len      1 .. MLA_MAX_Q_LEN (1 gives mla_decode_paged's results)
+ * Every other argument is as for mla_decode_paged, with R = q_len * H query
+ * rows in place of H for the split choice and the workspace: split_tokens 0
+ * means mla_decode_split_tokens(B, R, max_seq_len), and the workspace needs
+ * mla_decode_workspace_bytes(B, R, max_seq_len, split_tokens) bytes.  A
+ * query that sees no row (seq_lens[b] - q_len + j < 0) gives zeros and
+ * lse = -inf.  The rows of a chunk are read once for up to 128 query rows;
+ * above that, the workgroups of one chunk are numbered to run side by side
+ * on one XCD, where their reads share the L2.  The query side of such a step
+ * is the single-token calls on B * q_len virtual sequences: sequence (b, j)
+ * of length seq_lens[b] - q_len + j + 1 with block-table row b.
+ * Errors: MLA_ERR_INVALID_ARGUMENT for q_len < 1 and as mla_decode_paged;
+ * MLA_ERR_UNSUPPORTED for q_len > MLA_MAX_Q_LEN.
+ */
+int mla_decode_paged_multi(const void *q, const void *kv_cache, int kv_dtype,
+                           const int32_t *block_table, int max_blocks_per_seq,
+                           const int32_t *seq_lens, int max_seq_len, int num_blocks,
+                           int block_size, float softmax_scale, int split_tokens,
+                           void *workspace, size_t workspace_bytes,
+                           void *o_latent, float *lse, int B, int H, int q_len, void *stream);
+
 /*
  * The two halves of mla_decode_paged, for callers that merge chunks
  * themselves (e.g. chunks computed on different devices, which is the same

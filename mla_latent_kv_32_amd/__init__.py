@@ -21,13 +21,14 @@ __all__ = [
     "FP8_ROW_BYTES", "library_path", "lib", "abi_version",
     "mla_absorb_q", "mla_rope_append_cache", "mla_decode_paged", "mla_absorb_out",
     "mla_decode_workspace_bytes", "mla_decode_split_tokens", "mla_decode_partial", "mla_decode_combine",
-    "mla_decode_combine_absorb_out", "mla_absorb_q_rope_append",
+    "mla_decode_combine_absorb_out", "mla_absorb_q_rope_append", "mla_decode_paged_multi", "MAX_Q_LEN",
 ]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
 D_C, D_R, D_NOPE, D_V, BLOCK_SIZE = 512, 64, 128, 128, 64
 FP8_ROW_BYTES = 656
+MAX_Q_LEN = 32
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -77,6 +78,9 @@ def lib():
     L.mla_decode_paged.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
                                    vp, c_size, vp, vp, c_int, c_int, vp]
     L.mla_decode_paged.restype = c_int
+    L.mla_decode_paged_multi.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
+                                         vp, c_size, vp, vp, c_int, c_int, c_int, vp]
+    L.mla_decode_paged_multi.restype = c_int
     L.mla_decode_partial.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
                                      vp, c_size, c_int, c_int, vp]
     L.mla_decode_partial.restype = c_int
@@ -192,6 +196,34 @@ def mla_decode_paged(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, 
         _ptr(q), _ptr(kv_cache), int(kv_dtype), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
         int(max_seq_len), kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(split_tokens),
         _ptr(workspace), ws_bytes, _ptr(o_latent), _ptr(lse), B, H, _stream(stream)))
+
+
+def mla_decode_paged_multi(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, softmax_scale, o_latent,
+                           lse=None, split_tokens=0, workspace=None, stream=None):
+    """Decode of q_len new tokens per sequence (causal among them) in one pass over the cache.
+
+    q [B,q_len,H,576] bf16; o_latent [B,q_len,H,512] bf16; lse [B,q_len,H] float32 or None;
+    the other arguments as for mla_decode_paged.  Split and workspace are sized for
+    q_len * H query rows; a workspace is allocated with torch when not given.
+    """
+    B, q_len, H, _ = q.shape
+    _dense(q, "q", torch.bfloat16)
+    _dense(o_latent, "o_latent", torch.bfloat16)
+    _dense(kv_cache, "kv_cache")
+    _dense(block_table, "block_table", torch.int32)
+    _dense(seq_lens, "seq_lens", torch.int32)
+    if lse is not None:
+        _dense(lse, "lse", torch.float32)
+    rows = q_len * H
+    sp = split_tokens or mla_decode_split_tokens(B, rows, max_seq_len)
+    need = mla_decode_workspace_bytes(B, rows, max_seq_len, split_tokens) if max_seq_len > sp else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_decode_paged_multi", lib().mla_decode_paged_multi(
+        _ptr(q), _ptr(kv_cache), int(kv_dtype), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+        int(max_seq_len), kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(split_tokens),
+        _ptr(workspace), ws_bytes, _ptr(o_latent), _ptr(lse), B, H, q_len, _stream(stream)))
 
 
 def mla_decode_partial(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, softmax_scale, workspace,

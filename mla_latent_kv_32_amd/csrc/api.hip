@@ -173,7 +173,7 @@ int prepare_decode(DecodeMode mode, const void *q, const void *kv_cache, int kv_
   if (split_tokens > MLA_MAX_SPLIT_TOKENS) return MLA_ERR_UNSUPPORTED;
   const int split = split_tokens ? split_tokens : plan_split(B, H, max_seq_len);
   const int n_splits = max_seq_len > 0 ? (max_seq_len + split - 1) / split : 1;
-  if (static_cast<long>(B) * n_splits > 2147483647L) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<long>(B) * n_splits * head_groups(H) > 2147483647L) return MLA_ERR_UNSUPPORTED;
   const bool direct = paged && n_splits == 1;
   const size_t need = direct ? 0 : workspace_for(B, H, n_splits);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
@@ -190,6 +190,8 @@ int prepare_decode(DecodeMode mode, const void *q, const void *kv_cache, int kv_
   a->direct = direct ? 1 : 0;
   a->kv_fp8 = kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 0;
   a->scale_log2 = softmax_scale * 1.44269504088896340736f;
+  a->q_len = 1;
+  a->heads = H;
   a->o_latent = static_cast<uint16_t *>(o_latent);
   a->lse = lse;
   const size_t rows = static_cast<size_t>(B) * n_splits * H;
@@ -213,6 +215,27 @@ int mla_decode_paged(const void *q, const void *kv_cache, int kv_dtype, const in
                                 seq_lens, max_seq_len, num_blocks, block_size, softmax_scale, split_tokens,
                                 workspace, workspace_bytes, o_latent, lse, B, H, &a);
   if (st != MLA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = mla::launch_decode(a, s);
+  if (e != hipSuccess || a.direct) return status_of(e);
+  return status_of(mla::launch_combine(a, s));
+}
+
+int mla_decode_paged_multi(const void *q, const void *kv_cache, int kv_dtype, const int32_t *block_table,
+                           int max_blocks_per_seq, const int32_t *seq_lens, int max_seq_len, int num_blocks,
+                           int block_size, float softmax_scale, int split_tokens, void *workspace,
+                           size_t workspace_bytes, void *o_latent, float *lse, int B, int H, int q_len,
+                           void *stream) {
+  if (q_len < 1 || H < 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (q_len > MLA_MAX_Q_LEN || static_cast<long>(H) * q_len > 2147483647L) return MLA_ERR_UNSUPPORTED;
+  const int rows = H * q_len;
+  mla::DecodeArgs a;
+  const int st = prepare_decode(DecodeMode::Paged, q, kv_cache, kv_dtype, block_table, max_blocks_per_seq,
+                                seq_lens, max_seq_len, num_blocks, block_size, softmax_scale, split_tokens,
+                                workspace, workspace_bytes, o_latent, lse, B, rows, &a);
+  if (st != MLA_OK) return st;
+  a.q_len = q_len;
+  a.heads = H;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = mla::launch_decode(a, s);
   if (e != hipSuccess || a.direct) return status_of(e);
@@ -247,6 +270,8 @@ int mla_decode_combine(const void *workspace, size_t workspace_bytes, const int3
   a.seq_lens = seq_lens;
   a.B = B;
   a.H = H;
+  a.q_len = 1;
+  a.heads = H;
   a.split_tokens = split;
   a.n_splits = n_splits;
   a.o_latent = static_cast<uint16_t *>(o_latent);

@@ -195,7 +195,7 @@ struct DecoderPair {
   const DecodeArgs &a;
   const int wave, half;                          // wave-uniform
   const int b, split;
-  const int t_begin, t_end;
+  const int seq_len, t_begin, t_end;
   const int32_t *bt_row;                         // block-table row of the sequence
   uint8_t *px;                                   // LDS: this pair's P tile
   float *ax;                                     // LDS: this pair's per-head rescale factors
@@ -210,11 +210,11 @@ struct DecoderPair {
   // unrounded weights (gives an lse free of the bf16 rounding of P).
   float m_run, l_run, e_run;
 
-  __device__ DecoderPair(const DecodeArgs &args, uint8_t *px_, float *ax_, float *fx_, int b_, int split_, int t0,
-                         int t1)
+  __device__ DecoderPair(const DecodeArgs &args, uint8_t *px_, float *ax_, float *fx_, int b_, int split_, int S,
+                         int t0, int t1)
       : a(args), wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)),
         half(__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 1)),
-        b(b_), split(split_), t_begin(t0), t_end(t1),
+        b(b_), split(split_), seq_len(S), t_begin(t0), t_end(t1),
         bt_row(args.block_table + static_cast<size_t>(b_) * args.max_blocks),
         px(px_ + (threadIdx.x >> 7) * PX_BYTES), ax(ax_ + (threadIdx.x >> 7) * 32),
         fx(fx_ + (threadIdx.x >> 7) * 32) {}
@@ -230,6 +230,16 @@ struct DecoderPair {
   // head scored by lane l, and the pair head a 32-wide lane layout maps to lane l
   __device__ __forceinline__ int score_head(int l) const { return blockIdx.y * HEADS + wave * 16 + (l & 15); }
   __device__ __forceinline__ int pair_head(int l) const { return blockIdx.y * HEADS + (wave >> 1) * 32 + (l & 31); }
+  // End (exclusive token index) of what query row v sees in this chunk: the
+  // chunk end for a single new token; with q_len new tokens, row v (token
+  // j = v / heads) does not see the q_len - 1 - j newest ones.  vis_min: the
+  // smallest of these over the rows (that of token 0).
+  __device__ __forceinline__ int vis_end(int v) const {
+    return a.q_len <= 1 ? t_end : min(t_end, seq_len - (a.q_len - 1) + v / a.heads);
+  }
+  __device__ __forceinline__ int vis_min() const {
+    return a.q_len <= 1 ? t_end : min(t_end, seq_len - (a.q_len - 1));
+  }
 
   // LDS byte offsets of the first read of each kind.  Every other read is one
   // of these XOR a compile-time constant plus an immediate: the XOR acts on
@@ -382,9 +392,10 @@ struct DecoderPair {
     // as one fma.
     const int tok0 = t_begin + blk * TB;
     const float c = a.scale_log2;
-    if (tok0 + TB > t_end) [[unlikely]] {
-      // last block of the chunk: tokens at or past t_end do not exist
-      const int lim = t_end - tok0 - 4 * g;
+    if (tok0 + TB > vis_min()) [[unlikely]] {
+      // last block of the chunk (tokens at or past t_end do not exist), or a
+      // block holding new tokens that some multi-token rows do not see
+      const int lim = vis_end(score_head(l)) - tok0 - 4 * g;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (i >= lim) s0[i] = -INFINITY;
@@ -490,9 +501,11 @@ struct DecoderPair {
     const int l = threadIdx.x & 63;
     const float l_tot = sum_xor32(sum_xor16(l_run));
     const float e_tot = sum_xor32(sum_xor16(e_run));
-    const float inv = 1.0f / l_tot;
-    const float lse_v = (m_run + __log2f(e_tot)) * LN2;
     const int sh = score_head(l);
+    // a multi-token row that sees none of this chunk's tokens: zeros, -inf
+    const bool seen = vis_end(sh) > t_begin;
+    const float inv = seen ? 1.0f / l_tot : 0.0f;
+    const float lse_v = seen ? (m_run + __log2f(e_tot)) * LN2 : -INFINITY;
     if (l < 16) {
       fx[half * 16 + l] = inv;
       if (sh < a.H) {
@@ -513,7 +526,7 @@ struct DecoderPair {
       for (int q = 0; q < 4; ++q) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[j][4 * q + e] * scale);
+        for (int e = 0; e < 4; ++e) v[e] = to_bf16(scale != 0.0f ? o[j][4 * q + e] * scale : 0.0f);
         const int c = half * 32 + j * 4 + q;                  // 16-byte chunk of the row
         *reinterpret_cast<bf16x4 *>(srow + ((c ^ (row & 15)) << 4)) = v;
       }
@@ -587,8 +600,8 @@ struct DecoderSolo {
 
   const DecodeArgs &a;
   const int wave;
-  const int b, split;
-  const int t_begin, t_end;
+  const int b, split, grp;
+  const int seq_len, t_begin, t_end;
   const int32_t *bt_row;
 
   bf16x8 qf[KS];
@@ -598,9 +611,10 @@ struct DecoderSolo {
   // bf16-rounded weights and of the unrounded weights.
   float m_run, l_run, e_run;
 
-  __device__ DecoderSolo(const DecodeArgs &args, int b_, int split_, int t0, int t1)
-      : a(args), wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)), b(b_), split(split_),
-        t_begin(t0), t_end(t1), bt_row(args.block_table + static_cast<size_t>(b_) * args.max_blocks) {}
+  __device__ DecoderSolo(const DecodeArgs &args, int b_, int split_, int grp_, int S, int t0, int t1)
+      : a(args), wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)), b(b_), split(split_), grp(grp_),
+        seq_len(S), t_begin(t0), t_end(t1),
+        bt_row(args.block_table + static_cast<size_t>(b_) * args.max_blocks) {}
 
   __device__ __forceinline__ static int lane_id() {
     int l = threadIdx.x & 63;
@@ -611,7 +625,20 @@ struct DecoderSolo {
     asm volatile("" : "+v"(x));
     return x;
   }
-  __device__ __forceinline__ int head_of(int l) const { return blockIdx.y * HEADS + wave * 32 + (l & 31); }
+  __device__ __forceinline__ int head_of(int l) const { return grp * HEADS + wave * 32 + (l & 31); }
+  // Tokens of this chunk that the query row of lane l sees: all of them for
+  // a single new token; with q_len new tokens, row v (token j = v / heads)
+  // does not see the q_len - 1 - j newest ones.
+  __device__ __forceinline__ int visible(int l) const {
+    if (a.q_len <= 1) return t_end - t_begin;
+    const int v = head_of(l);
+    return min(t_end, seq_len - (a.q_len - 1) + v / a.heads) - t_begin;
+  }
+  // Mask limit for block blk: token 16 hb + n of the block is visible while
+  // n < limit (lanes l and l + 32 hold the token halves hb = 0, 1).
+  __device__ __forceinline__ int mask_limit(int l, int blk) const {
+    return visible(l) - blk * TB - 16 * ((l >> 5) & 1);
+  }
 
   __device__ __forceinline__ void begin() {
     m_run = -INFINITY;
@@ -801,6 +828,14 @@ struct DecoderSolo {
       if (k == 12) e_run += st.pe;
     }
   }
+  // Scores of tokens at or past `lim` (mask_limit) set to -inf: the block
+  // before the last one, for multi-token rows (a no-op otherwise).
+  __device__ __forceinline__ void mask_scores(f32x16 &s, int lim) const {
+    if (a.q_len <= 1) return;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (4 * (i & 3) + 2 * (i >> 3) + ((i >> 2) & 1) >= lim) s[i] = -INFINITY;
+  }
   __device__ __forceinline__ void softmax_all(f32x16 &s, Soft &st, bool mask, int lim) {
 #pragma unroll
     for (int k = 0; k < 13; ++k) soft_step(k, s, st, mask, lim);
@@ -830,8 +865,10 @@ struct DecoderSolo {
   // block i spread over them (its steps between every second MFMA), the
   // rescale of the value accumulators for block i, then the 32 value MFMAs of
   // block i with the nine copies of `cp` (when COPY) spread over them.  s holds
-  // block i + 1's scores on return.  Block i is never the last block, so no
-  // masking.  first: block i is block 0 (the accumulators are still zero).
+  // block i + 1's scores on return.  first: block i is block 0 (the
+  // accumulators are still zero).  Block i is never the last block of the
+  // chunk; multi-token rows that do not see some of its tokens have them
+  // masked beforehand (mask_scores).
   template <bool COPY>
   __device__ __forceinline__ void phase(const uint8_t *slot_s, const uint8_t *slot_v, f32x16 &s, bool first,
                                         const Copy &cp) {
@@ -1019,8 +1056,10 @@ struct DecoderSolo {
     const int l = threadIdx.x & 63;
     const float l_tot = sum_xor32(l_run);
     const float e_tot = sum_xor32(e_run);
-    const float inv = 1.0f / l_tot;
-    const float lse_v = (m_run + __log2f(e_tot)) * LN2;
+    // a multi-token row that sees none of this chunk's tokens: zeros, -inf
+    const bool seen = visible(l) > 0;
+    const float inv = seen ? 1.0f / l_tot : 0.0f;
+    const float lse_v = seen ? (m_run + __log2f(e_tot)) * LN2 : -INFINITY;
     const int head = head_of(l);
     if (l < 32 && head < a.H) {
       if (a.direct) {
@@ -1038,7 +1077,7 @@ struct DecoderSolo {
       for (int q = 0; q < 4; ++q) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[j][4 * q + e] * inv);
+        for (int e = 0; e < 4; ++e) v[e] = to_bf16(seen ? o[j][4 * q + e] * inv : 0.0f);
         const int c = j * 4 + q;                            // 16-byte chunk of the row
         *reinterpret_cast<bf16x4 *>(srow + ((c ^ (row & 15)) << 4)) = v;
       }
@@ -1047,7 +1086,7 @@ struct DecoderSolo {
 #pragma unroll 4
     for (int k = 0; k < 32; ++k) {
       const int r = wave * 32 + k;
-      const int h = blockIdx.y * HEADS + r;
+      const int h = grp * HEADS + r;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * LAT_BYTES + ((l ^ (r & 15)) << 4));
       if (h < a.H) {
         uint16_t *dst = a.direct ? a.o_latent + (static_cast<size_t>(b) * a.H + h) * DC
@@ -1145,7 +1184,7 @@ void decode_bf16_kernel(DecodeArgs a) {
 
   // Page ids are read with scalar loads (the streaming loop's only vector
   // memory operations are its DMA copies, so vmcnt counts exactly those).
-  D dec(a, px, ax, fx, b, split, t_begin, t_end);
+  D dec(a, px, ax, fx, b, split, S, t_begin, t_end);
   dec.begin();
   const int nblk = (t_end - t_begin + TB - 1) / TB;
   // Block 0's copies go out before the query loads so the two latencies
@@ -1207,8 +1246,16 @@ void decode_solo_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT * S_SLOT];
   static_assert(DecoderSolo::HEADS * LAT_BYTES <= NSLOT * S_SLOT, "the output tile is staged in the slot ring");
 
+  // One workgroup per (sequence, chunk, head group), the head groups of a
+  // chunk numbered consecutively; workgroups are dealt to the 8 XCDs
+  // round-robin by id, so id -> (XCD id % 8, position id / 8) is remapped to
+  // consecutive indices per XCD: the chunks of a sequence, and the head
+  // groups that read the same chunk, share one L2.
   int item = blockIdx.x;
   if ((gridDim.x & 7) == 0) item = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int groups = (a.H + DecoderSolo::HEADS - 1) / DecoderSolo::HEADS;
+  const int grp = item % groups;
+  item /= groups;
   const int b = item / a.n_splits;
   const int split = item - b * a.n_splits;
   const int S = a.seq_lens[b];
@@ -1218,7 +1265,7 @@ void decode_solo_kernel(DecodeArgs a) {
   if (t_begin >= t_end) {
     if (a.direct) {
       const int t = threadIdx.x;
-      const int head = blockIdx.y * DecoderSolo::HEADS + t / 2;      // 2 threads per head
+      const int head = grp * DecoderSolo::HEADS + t / 2;      // 2 threads per head
       if (head < a.H) {
         uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + (t % 2) * (DC / 2);
         for (int c = 0; c < DC / 2; c += 8) *reinterpret_cast<u32x4 *>(dst + c) = u32x4{0, 0, 0, 0};
@@ -1228,11 +1275,10 @@ void decode_solo_kernel(DecodeArgs a) {
     return;
   }
 
-  DecoderSolo dec(a, b, split, t_begin, t_end);
+  DecoderSolo dec(a, b, split, grp, S, t_begin, t_end);
   dec.begin();
   const int nblk = (t_end - t_begin + TB - 1) / TB;
-  const int lim_last = t_end - t_begin - (nblk - 1) * TB - 16 * (threadIdx.x >> 5 & 1);
-  const bool ragged = (t_end - t_begin) % TB != 0;
+  const bool ragged = (t_end - t_begin) % TB != 0 || a.q_len > 1;
   auto slot = [&](int i) { return ring + (i & (NSLOT - 1)) * S_SLOT; };
   // Block 0's copies, the query and blocks 1 and 2 all go out at once; the
   // first wait covers block 0 and the query only.
@@ -1260,11 +1306,12 @@ void decode_solo_kernel(DecodeArgs a) {
     if (i + 2 < nblk) wait_vmcnt<DecoderSolo::NI>();
     else wait_vmcnt<0>();
     barrier_no_fence();
+    dec.mask_scores(s, dec.mask_limit(DecoderSolo::lane_id(), i));
     dec.phase<false>(slot(i + 1), slot(i), s, i == 0, DecoderSolo::Copy{});
   }
   {
     DecoderSolo::Soft st;
-    dec.softmax_all(s, st, ragged, lim_last);
+    dec.softmax_all(s, st, ragged, dec.mask_limit(DecoderSolo::lane_id(), nblk - 1));
     dec.rescale(nblk == 1 ? 1.0f : st.alpha);
     dec.values(slot(nblk - 1), st.p);
   }
@@ -1286,8 +1333,16 @@ void decode_solo_fp8_kernel(DecodeArgs a) {
   static_assert(DecoderSolo::HEADS * LAT_BYTES <= RING + 2 * STAGE_BYTES, "the output tile is staged in LDS");
   uint8_t *const stage0 = lds + RING;
 
+  // One workgroup per (sequence, chunk, head group), the head groups of a
+  // chunk numbered consecutively; workgroups are dealt to the 8 XCDs
+  // round-robin by id, so id -> (XCD id % 8, position id / 8) is remapped to
+  // consecutive indices per XCD: the chunks of a sequence, and the head
+  // groups that read the same chunk, share one L2.
   int item = blockIdx.x;
   if ((gridDim.x & 7) == 0) item = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int groups = (a.H + DecoderSolo::HEADS - 1) / DecoderSolo::HEADS;
+  const int grp = item % groups;
+  item /= groups;
   const int b = item / a.n_splits;
   const int split = item - b * a.n_splits;
   const int S = a.seq_lens[b];
@@ -1297,7 +1352,7 @@ void decode_solo_fp8_kernel(DecodeArgs a) {
   if (t_begin >= t_end) {
     if (a.direct) {
       const int t = threadIdx.x;
-      const int head = blockIdx.y * DecoderSolo::HEADS + t / 2;      // 2 threads per head
+      const int head = grp * DecoderSolo::HEADS + t / 2;      // 2 threads per head
       if (head < a.H) {
         uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + (t % 2) * (DC / 2);
         for (int c = 0; c < DC / 2; c += 8) *reinterpret_cast<u32x4 *>(dst + c) = u32x4{0, 0, 0, 0};
@@ -1307,11 +1362,10 @@ void decode_solo_fp8_kernel(DecodeArgs a) {
     return;
   }
 
-  DecoderSolo dec(a, b, split, t_begin, t_end);
+  DecoderSolo dec(a, b, split, grp, S, t_begin, t_end);
   dec.begin();
   const int nblk = (t_end - t_begin + TB - 1) / TB;
-  const int lim_last = t_end - t_begin - (nblk - 1) * TB - 16 * (threadIdx.x >> 5 & 1);
-  const bool ragged = (t_end - t_begin) % TB != 0;
+  const bool ragged = (t_end - t_begin) % TB != 0 || a.q_len > 1;
   auto slot = [&](int i) { return lds + (i % 3) * S_SLOT; };
   auto stage = [&](int i) { return stage0 + (i & 1) * STAGE_BYTES; };
   constexpr int NI8 = DecoderSolo::NI8;
@@ -1346,17 +1400,19 @@ void decode_solo_fp8_kernel(DecodeArgs a) {
   }
   if (i + 2 < nblk) {
     barrier_lds();
+    dec.mask_scores(s, dec.mask_limit(DecoderSolo::lane_id(), i));
     dec.phase8<false, true>(slot(i + 1), slot(i), s, i == 0, 0, 0, nullptr, i + 2, stage(i + 2), slot(i + 2));
     ++i;
   }
   if (i + 1 < nblk) {
     barrier_lds();
+    dec.mask_scores(s, dec.mask_limit(DecoderSolo::lane_id(), i));
     dec.phase8<false, false>(slot(i + 1), slot(i), s, i == 0, 0, 0, nullptr, 0, nullptr, nullptr);
     ++i;
   }
   {
     DecoderSolo::Soft st;
-    dec.softmax_all(s, st, ragged, lim_last);
+    dec.softmax_all(s, st, ragged, dec.mask_limit(DecoderSolo::lane_id(), nblk - 1));
     dec.rescale(nblk == 1 ? 1.0f : st.alpha);
     dec.values(slot(nblk - 1), st.p);
   }
@@ -1436,7 +1492,7 @@ void decode_fp8_kernel(DecodeArgs a) {
     return;
   }
 
-  D dec(a, px, ax, fx, b, split, t_begin, t_end);
+  D dec(a, px, ax, fx, b, split, S, t_begin, t_end);
   dec.begin();
   const int nblk = (t_end - t_begin + TB - 1) / TB;
   dec.issue8(0, dec.page_of(0), stage);
@@ -1478,13 +1534,15 @@ void decode_fp8_kernel(DecodeArgs a) {
 // Merge split-KV partials: o = sum_c w_c o_c / sum_c w_c, w_c = exp(lse_c - L),
 // L = max_c lse_c.  One 64-lane group per (sequence, head), 8 columns per
 // lane; the chunks' lse are reduced across the lanes first, then the partial
-// rows stream in groups of 8 so that 8 loads per lane are in flight.
+// rows stream in groups of 8 so that 8 loads per lane are in flight.  A
+// multi-token row merges the chunks that hold tokens it sees.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int b = blockIdx.x;
   const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int t = threadIdx.x & 63;
   if (head >= a.H) return;
-  const int S = a.seq_lens[b];
+  int S = a.seq_lens[b];
+  if (a.q_len > 1) S = max(0, S - (a.q_len - 1) + head / a.heads);
   const int nv = (S + a.split_tokens - 1) / a.split_tokens;
   uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + t * 8;
   if (nv <= 0) {
@@ -1540,27 +1598,24 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int hpw = decode_heads_per_wave(a.H);
   const int groups = (a.H + hpw * nw - 1) / (hpw * nw);
   dim3 grid(a.B * a.n_splits, groups);
+  // one-wave-per-SIMD kernels: head groups folded into the x dimension
+  const dim3 grid_solo(a.B * a.n_splits * groups, 1);
   if (a.kv_fp8 && nw == 8) {
-    decode_solo_fp8_kernel<<<grid, 256, 0, stream>>>(a);
+    decode_solo_fp8_kernel<<<grid_solo, 256, 0, stream>>>(a);
     return hipGetLastError();
   }
+  // H <= 64: two waves per SIMD (DecoderPair with 2 or 4 waves)
   if (a.kv_fp8) {
-    switch (nw) {
-      case 2: decode_fp8_kernel<DecoderPair<2>, 1><<<grid, 128, 0, stream>>>(a); break;
-      case 4: decode_fp8_kernel<DecoderPair<4>, 1><<<grid, 256, 0, stream>>>(a); break;
-      default: decode_fp8_kernel<DecoderPair<8>, 2><<<grid, 512, 0, stream>>>(a); break;
-    }
+    if (nw == 2) decode_fp8_kernel<DecoderPair<2>, 1><<<grid, 128, 0, stream>>>(a);
+    else decode_fp8_kernel<DecoderPair<4>, 1><<<grid, 256, 0, stream>>>(a);
     return hipGetLastError();
   }
   if (nw == 8) {
-    decode_solo_kernel<<<grid, 256, 0, stream>>>(a);
+    decode_solo_kernel<<<grid_solo, 256, 0, stream>>>(a);
     return hipGetLastError();
   }
-  switch (nw) {
-    case 2: decode_bf16_kernel<DecoderPair<2>, 1><<<grid, 128, 0, stream>>>(a); break;
-    case 4: decode_bf16_kernel<DecoderPair<4>, 1><<<grid, 256, 0, stream>>>(a); break;
-    default: decode_bf16_kernel<DecoderPair<8>, 2><<<grid, 512, 0, stream>>>(a); break;
-  }
+  if (nw == 2) decode_bf16_kernel<DecoderPair<2>, 1><<<grid, 128, 0, stream>>>(a);
+  else decode_bf16_kernel<DecoderPair<4>, 1><<<grid, 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

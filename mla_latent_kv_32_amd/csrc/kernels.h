@@ -21,6 +21,11 @@ struct DecodeArgs {
   int direct;                   // 1: one chunk, write o_latent / lse directly
   int kv_fp8;                   // 1: packed fp8 rows (656 bytes), else bf16 rows (1152 bytes)
   float scale_log2;             // softmax_scale * log2(e)
+  // Multi-token decode: H = q_len * heads query rows per sequence, row
+  // v = j * heads + h for new token j; row v sees the tokens t <
+  // seq_len - (q_len - 1) + v / heads.  q_len <= 1 is the single-token case.
+  int q_len;
+  int heads;
   uint16_t *o_latent;           // [B, H, 512] bf16
   float *lse;                   // [B, H] or null
   uint16_t *o_part;             // [B, n_splits, H, 512] bf16 partial outputs

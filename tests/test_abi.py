@@ -141,6 +141,27 @@ def test_fused_query_call_validates_like_its_parts():
     assert call(bs=32) == -2
 
 
+@needs_lib
+def test_multi_token_call_validates():
+    L = mla.lib()
+    dec = L.mla_decode_paged_multi
+
+    def call(q_len=2, H=16, split=0, ws=NULL, ws_bytes=0, max_seq=256, block=64):
+        return dec(FAKE, FAKE, 0, FAKE, 4, FAKE, max_seq, 16, block, ctypes.c_float(0.07), split,
+                   ws, ws_bytes, FAKE, NULL, 2, H, q_len, NULL)
+    assert call(q_len=0) == -1
+    assert call(q_len=-3) == -1
+    assert call(q_len=mla.MAX_Q_LEN + 1) == -2
+    assert call(H=0) == -1
+    assert call(split=100) == -1
+    assert call(block=32) == -2
+    assert call(max_seq=257) == -1
+    # the workspace is sized for q_len * H query rows
+    need = L.mla_decode_workspace_bytes(2, 2 * 16, 256, 64)
+    assert need == L.mla_decode_workspace_bytes(2, 32, 256, 64) > L.mla_decode_workspace_bytes(2, 16, 256, 64)
+    assert call(split=64, ws=FAKE, ws_bytes=need - 256) == -3
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mla, "_LIB", None)
     monkeypatch.setenv("MLA_LIBRARY", str(tmp_path / "missing.so"))
