@@ -183,8 +183,10 @@ __global__ __launch_bounds__(256) void query_kernel(const uint16_t *q_nope, cons
 // row j's chunk log-sum-exps (one pass for up to 32 chunks, loaded together
 // with the sequence lengths), the row maximum is a 32-lane shuffle reduction,
 // and the weights reach the accumulation as wave-uniform values; all partial
-// rows of a batch of 16 chunks are loaded together.  Each row sums its chunks
-// in chunk order with the arithmetic of combine_kernel, so o_latent and lse
+// rows of a batch of 8 chunks are loaded together, the first batch before
+// the lengths and lse values have arrived and before the W_UV copies, so the
+// merge does not wait behind them.  Each row sums its chunks in chunk order
+// in batches of 8 with the arithmetic of combine_kernel, so o_latent and lse
 // equal the separate merge bit for bit.  The merged bf16 rows go to an LDS
 // tile (16-byte chunk c of row r at position c ^ (r & 15)) whose rows 16..31
 // stay zero, and waves 0-3 multiply it by W_UV[h] with 32x32x16 MFMAs, 32
@@ -194,7 +196,7 @@ void combine_absorb_out_kernel(CombineOutArgs a) {
   constexpr int K = DC, N = DV, NT = 128;
   constexpr int NWAVE = 8, ROWS = 16, RPW = ROWS / NWAVE;   // 2 tile rows per wave
   constexpr int LPR = 64 / RPW;                             // 32 lanes per row in the lse phase
-  constexpr int VB = 16;                                    // chunks per load batch
+  constexpr int VB = 8;                                     // chunks per load batch
   constexpr int CPR = NT * 2 / 16;                          // 16-byte chunks per W row
   constexpr int PER_WAVE = K * CPR / (64 * NWAVE);          // 16 DMA copies per wave
   __shared__ __attribute__((aligned(16))) uint8_t wt[K * NT * 2];     // 128 KB
@@ -208,17 +210,20 @@ void combine_absorb_out_kernel(CombineOutArgs a) {
   const int item = (G & 7) == 0 ? (L & 7) * (G >> 3) + (L >> 3) : L;
   const int h = item / slots, slot = item % slots;
 
-  // ---- W_UV[h] -> LDS (row k, position p <- chunk p ^ wsw(k) of the row)
+  // W_UV[h] -> LDS (row k, position p <- chunk p ^ wsw(k) of the row); issued
+  // after the first tile's merge loads, so that those do not queue behind it
   const uint8_t *wg = reinterpret_cast<const uint8_t *>(a.w_uv + static_cast<size_t>(h) * K * N);
   const uint32_t wt_lds = lds_addr(wt);
+  auto load_w = [&]() {
 #pragma unroll 4
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int base = (wave * PER_WAVE + i) * 64;
-    const int p = base + lane;
-    const int k = p / CPR;
-    const int c = (p % CPR) ^ wsw<NT>(k);
-    dma16(wg + static_cast<size_t>(k) * N * 2 + c * 16, __builtin_amdgcn_readfirstlane(wt_lds + base * 16));
-  }
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int base = (wave * PER_WAVE + i) * 64;
+      const int p = base + lane;
+      const int k = p / CPR;
+      const int c = (p % CPR) ^ wsw<NT>(k);
+      dma16(wg + static_cast<size_t>(k) * N * 2 + c * 16, __builtin_amdgcn_readfirstlane(wt_lds + base * 16));
+    }
+  };
   // rows 16..31 of the A tile: zero for the whole kernel
   reinterpret_cast<u32x4 *>(at + ROWS * DC * 2)[threadIdx.x] = u32x4{0, 0, 0, 0};
   reinterpret_cast<u32x4 *>(at + ROWS * DC * 2)[threadIdx.x + 512] = u32x4{0, 0, 0, 0};
@@ -243,58 +248,82 @@ void combine_absorb_out_kernel(CombineOutArgs a) {
     const float l0 = kl < a.n_splits ? lp_l[kl * stride] : -INFINITY;
     int nv_l = 0;
     if (bl < a.B) nv_l = max(0, (a.seq_lens[bl] + a.split_tokens - 1) / a.split_tokens);
+    const uint16_t *op[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int b = b0 + wave + NWAVE * j;
+      op[j] = a.o_part + (static_cast<size_t>(b < a.B ? b : 0) * a.n_splits * stride + h) * DC + lane * 8;
+    }
+    // The first batch of chunks of every row is requested before the lengths
+    // are known (the chunks lie inside the workspace; those past a row's
+    // count are zeroed after the load), then the W_UV tile on the first pass.
+    u32x4 v0[RPW][VB];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+#pragma unroll
+      for (int k = 0; k < VB; ++k)
+        v0[j][k] = k < a.n_splits ? *reinterpret_cast<const u32x4 *>(op[j] + k * stride * DC) : u32x4{0, 0, 0, 0};
+    if (first) load_w();
     float mx = kl < nv_l ? l0 : -INFINITY;
     for (int c = kl + LPR; c < nv_l; c += LPR) mx = fmaxf(mx, lp_l[c * stride]);
 #pragma unroll
     for (int sh = 1; sh < LPR; sh <<= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
     int nv[RPW];
     float Lm[RPW];
-    const uint16_t *op[RPW];
     int ncmax = 0;
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
       nv[j] = __builtin_amdgcn_readlane(nv_l, LPR * j);
       Lm[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), LPR * j));
       ncmax = max(ncmax, nv[j]);
-      const int b = b0 + wave + NWAVE * j;
-      op[j] = a.o_part + (static_cast<size_t>(b < a.B ? b : 0) * a.n_splits * stride + h) * DC + lane * 8;
     }
 
-    // ---- weighted sums, VB chunks of every row per batch
+    // ---- weighted sums in chunk order, VB chunks of every row per batch
+    // (the batching of combine_kernel, so the sums are the same)
     float acc[RPW][8] = {};
     float z[RPW] = {};
-    for (int cb = 0; cb < ncmax; cb += LPR) {
-      // lane LPR j + k: weight of chunk cb + k of row j
-      float w_l = 0.f;
-      if (cb + kl < nv_l) w_l = expf((cb == 0 ? l0 : lp_l[(cb + kl) * stride]) - mx);
+    // lane LPR j + k: weight of chunk cb + k of row j
+    float w_l = kl < nv_l ? expf(l0 - mx) : 0.f;
+    auto accumulate = [&](const u32x4 (&v)[RPW][VB], int part) {
 #pragma unroll
-      for (int part = 0; part < LPR; part += VB) {
-        const int c0 = cb + part;
-        if (c0 >= ncmax) break;
-        u32x4 v[RPW][VB];
+      for (int j = 0; j < RPW; ++j) {
 #pragma unroll
-        for (int j = 0; j < RPW; ++j) {
+        for (int k = 0; k < VB; ++k) {
+          const float wk = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), LPR * j + part + k));
+          z[j] += wk;
 #pragma unroll
-          for (int k = 0; k < VB; ++k) {
-            if (c0 + k < nv[j]) v[j][k] = *reinterpret_cast<const u32x4 *>(op[j] + (c0 + k) * stride * DC);
-            else v[j][k] = u32x4{0, 0, 0, 0};
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < RPW; ++j) {
-#pragma unroll
-          for (int k = 0; k < VB; ++k) {
-            const float wk = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), LPR * j + part + k));
-            z[j] += wk;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              acc[j][2 * e] += wk * __uint_as_float(v[j][k][e] << 16);
-              acc[j][2 * e + 1] += wk * __uint_as_float(v[j][k][e] & 0xFFFF0000u);
-            }
+          for (int e = 0; e < 4; ++e) {
+            acc[j][2 * e] += wk * __uint_as_float(v[j][k][e] << 16);
+            acc[j][2 * e + 1] += wk * __uint_as_float(v[j][k][e] & 0xFFFF0000u);
           }
         }
       }
+    };
+    if (ncmax > 0) {
+#pragma unroll
+      for (int j = 0; j < RPW; ++j)
+#pragma unroll
+        for (int k = 0; k < VB; ++k)
+          if (k >= nv[j]) v0[j][k] = u32x4{0, 0, 0, 0};
+      accumulate(v0, 0);
+    }
+    for (int c0 = VB; c0 < ncmax; c0 += VB) {
+      const int part = c0 & (LPR - 1);
+      if (part == 0) {
+        w_l = 0.f;
+        if (c0 + kl < nv_l) w_l = expf(lp_l[(c0 + kl) * stride] - mx);
+      }
+      u32x4 v[RPW][VB];
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+#pragma unroll
+        for (int k = 0; k < VB; ++k) {
+          if (c0 + k < nv[j]) v[j][k] = *reinterpret_cast<const u32x4 *>(op[j] + (c0 + k) * stride * DC);
+          else v[j][k] = u32x4{0, 0, 0, 0};
+        }
+      }
+      accumulate(v, part);
     }
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
@@ -342,7 +371,7 @@ void combine_absorb_out_kernel(CombineOutArgs a) {
     }
     __syncthreads();                    // the tile is rebuilt for the next rows
   }
-  if (first) wait_vmcnt<0>();           // no tile: still drain the W copies before exit
+  // (every workgroup has at least one tile: slot < tiles)
 }
 
 }  // namespace
