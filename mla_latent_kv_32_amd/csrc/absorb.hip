@@ -78,9 +78,8 @@ __device__ __forceinline__ void absorb_load_act(const uint16_t *act, int B, int 
 // over the K-steps, the weight operand read transposed from the LDS tile
 // (lane 16 g + q reads rows 8 (g >> 1) + q / 4 (+4 for the second read) of
 // each 16-row k-step, columns 32 wave + 16 (g & 1) + 4 (q & 3) .. +4).
-template <int K, int N, int NT, int OUT_ROW>
-__device__ __forceinline__ void absorb_tile(const u32x4 (&av)[K / 16], const uint8_t *tile, uint16_t *out, int B,
-                                            int H, int h, int n0, int b0, int wave, int lane) {
+template <int K, int N, int NT>
+__device__ __forceinline__ f32x16 absorb_mfma(const u32x4 (&av)[K / 16], const uint8_t *tile, int wave, int lane) {
   const int g = lane >> 4, q = lane & 15;
   const int krow = 8 * (g >> 1) + (q >> 2);
   const int chunk = 4 * wave + 2 * (g & 1) + ((q & 3) >> 1);
@@ -96,6 +95,13 @@ __device__ __forceinline__ void absorb_tile(const u32x4 (&av)[K / 16], const uin
     const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[kb]), bv, acc, 0, 0, 0);
   }
+  return acc;
+}
+
+template <int K, int N, int NT, int OUT_ROW>
+__device__ __forceinline__ void absorb_tile(const u32x4 (&av)[K / 16], const uint8_t *tile, uint16_t *out, int B,
+                                            int H, int h, int n0, int b0, int wave, int lane) {
+  const f32x16 acc = absorb_mfma<K, N, NT>(av, tile, wave, lane);
   // row (batch) b0 + (i/4)*8 + 4*hl + i%4, column n0 + 32 wave + r
   const int r = lane & 31, hl = lane >> 5, rows = B - b0;
   const size_t ld_out = static_cast<size_t>(H) * OUT_ROW;
@@ -104,6 +110,33 @@ __device__ __forceinline__ void absorb_tile(const u32x4 (&av)[K / 16], const uin
   for (int i = 0; i < 16; ++i) {
     const int row = (i >> 2) * 8 + hl * 4 + (i & 3);
     if (row < rows) op[row * ld_out] = bf16_bits(to_bf16(acc[i]));
+  }
+}
+
+// absorb_tile with the output tile (32 batch rows x NT columns, bf16) staged
+// through LDS: every thread then stores two whole 16-byte pieces of a row
+// instead of sixteen 2-byte values scattered over 16 rows.  `stage` holds
+// 32 * NT bf16; the caller separates consecutive uses by a barrier.
+template <int K, int N, int NT, int OUT_ROW>
+__device__ __forceinline__ void absorb_tile_staged(const u32x4 (&av)[K / 16], const uint8_t *tile, uint16_t *stage,
+                                                   uint16_t *out, int B, int H, int h, int n0, int b0, int wave,
+                                                   int lane) {
+  const f32x16 acc = absorb_mfma<K, N, NT>(av, tile, wave, lane);
+  const int r = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = (i >> 2) * 8 + hl * 4 + (i & 3);
+    stage[row * NT + wave * 32 + r] = bf16_bits(to_bf16(acc[i]));
+  }
+  __syncthreads();
+  constexpr int PIECES = NT / 8;                       // 16-byte pieces per row
+  const int t = threadIdx.x;                           // NT * 2 threads, 2 pieces each
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int p = t * 2 + k, row = p / PIECES, c = p % PIECES;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * NT + c * 8);
+    if (row < B - b0)
+      *reinterpret_cast<u32x4 *>(out + (static_cast<size_t>(b0 + row) * H + h) * OUT_ROW + n0 + c * 8) = v;
   }
 }
 
@@ -135,6 +168,7 @@ __global__ __launch_bounds__(NT * 2) void absorb_kernel(const uint16_t *act, con
 __global__ __launch_bounds__(256) void query_kernel(const uint16_t *q_nope, const uint16_t *w_uk, RopeAppendArgs ra) {
   constexpr int K = DNOPE, N = DC, NT = 128;
   __shared__ __attribute__((aligned(16))) uint8_t tile[K * NT * 2];
+  __shared__ __attribute__((aligned(16))) uint16_t stage[32 * NT];
   __shared__ float cs[DR / 2], sn[DR / 2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -147,10 +181,12 @@ __global__ __launch_bounds__(256) void query_kernel(const uint16_t *q_nope, cons
 
   // query rotary pairs: thread (j = tid / 32, pair i = tid % 32), sequences
   // b = x + 4 j + 32 m
+  // (the q_pe pair is requested with the length, before the angle is formed)
   for (int b = blockIdx.x + 4 * (tid >> 5); b < B; b += 4 * (256 / 32)) {
+    const uint32_t pr = rope_query_load(ra, b, h, tid & 31);
     float c, s;
     rope_cos_sin(ra, rope_position(ra.seq_lens[b]), tid & 31, c, s);
-    rope_query_pair(ra, b, h, tid & 31, c, s);
+    rope_query_store(ra, b, h, tid & 31, pr, c, s);
   }
   // cache rows
   const int nwg = gridDim.x * gridDim.y;
@@ -165,10 +201,11 @@ __global__ __launch_bounds__(256) void query_kernel(const uint16_t *q_nope, cons
 
   wait_vmcnt<0>();
   __syncthreads();
-  absorb_tile<K, N, NT, DROW>(av, tile, ra.q, B, H, h, n0, 0, wave, lane);
+  absorb_tile_staged<K, N, NT, DROW>(av, tile, stage, ra.q, B, H, h, n0, 0, wave, lane);
   for (int b0 = 32; b0 < B; b0 += 32) {
     absorb_load_act<K>(q_nope, B, H, h, b0, lane, av);
-    absorb_tile<K, N, NT, DROW>(av, tile, ra.q, B, H, h, n0, b0, wave, lane);
+    __syncthreads();           // the previous tile's stores have read the stage
+    absorb_tile_staged<K, N, NT, DROW>(av, tile, stage, ra.q, B, H, h, n0, b0, wave, lane);
   }
 }
 

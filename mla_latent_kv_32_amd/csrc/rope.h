@@ -63,10 +63,16 @@ __device__ __forceinline__ uint32_t rope_rotate_pair(uint32_t pr, float c, float
 }
 
 // Query pair i of (b, h): q[b, h, 512 + 2i .. 512 + 2i + 1] = RoPE(q_pe[b, h]).
+__device__ __forceinline__ uint32_t rope_query_load(const RopeAppendArgs &a, int b, int h, int i) {
+  return *reinterpret_cast<const uint32_t *>(a.q_pe + (static_cast<size_t>(b) * a.H + h) * DR + 2 * i);
+}
+__device__ __forceinline__ void rope_query_store(const RopeAppendArgs &a, int b, int h, int i, uint32_t pr, float c,
+                                                 float s) {
+  *reinterpret_cast<uint32_t *>(a.q + (static_cast<size_t>(b) * a.H + h) * DROW + DC + 2 * i) =
+      rope_rotate_pair(pr, c, s);
+}
 __device__ __forceinline__ void rope_query_pair(const RopeAppendArgs &a, int b, int h, int i, float c, float s) {
-  const size_t bh = static_cast<size_t>(b) * a.H + h;
-  const uint32_t pr = *reinterpret_cast<const uint32_t *>(a.q_pe + bh * DR + 2 * i);
-  *reinterpret_cast<uint32_t *>(a.q + bh * DROW + DC + 2 * i) = rope_rotate_pair(pr, c, s);
+  rope_query_store(a, b, h, i, rope_query_load(a, b, h, i), c, s);
 }
 
 // Append the new token's row of sequence b (S = seq_lens[b] > 0) at position
