@@ -271,7 +271,7 @@ struct DecoderPair {
   }
 
   __device__ __forceinline__ void begin() {
-    m_run = -INFINITY;
+    m_run = -FLT_MAX;         // finite: a row whose tokens are all masked keeps weights exp2(-inf) = 0
     l_run = 0.f;
     e_run = 0.f;
 #pragma unroll
@@ -502,10 +502,10 @@ struct DecoderPair {
     const float l_tot = sum_xor32(sum_xor16(l_run));
     const float e_tot = sum_xor32(sum_xor16(e_run));
     const int sh = score_head(l);
-    // a multi-token row that sees none of this chunk's tokens: zeros, -inf
-    const bool seen = vis_end(sh) > t_begin;
-    const float inv = seen ? 1.0f / l_tot : 0.0f;
-    const float lse_v = seen ? (m_run + __log2f(e_tot)) * LN2 : -INFINITY;
+    // l_tot >= 1 unless the row saw no token of the chunk (a multi-token row
+    // past its position): then o = 0 and lse = log 0 = -inf
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float lse_v = (m_run + __log2f(e_tot)) * LN2;
     if (l < 16) {
       fx[half * 16 + l] = inv;
       if (sh < a.H) {
@@ -526,7 +526,7 @@ struct DecoderPair {
       for (int q = 0; q < 4; ++q) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = to_bf16(scale != 0.0f ? o[j][4 * q + e] * scale : 0.0f);
+        for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[j][4 * q + e] * scale);
         const int c = half * 32 + j * 4 + q;                  // 16-byte chunk of the row
         *reinterpret_cast<bf16x4 *>(srow + ((c ^ (row & 15)) << 4)) = v;
       }
@@ -641,7 +641,7 @@ struct DecoderSolo {
   }
 
   __device__ __forceinline__ void begin() {
-    m_run = -INFINITY;
+    m_run = -FLT_MAX;         // finite: a row whose tokens are all masked keeps weights exp2(-inf) = 0
     l_run = 0.f;
     e_run = 0.f;
 #pragma unroll
@@ -802,7 +802,7 @@ struct DecoderSolo {
     } else if (k == 2) {
       const float m_new = fmaxf(m_run, max_xor32(st.mx) * c);
       const bool up = m_new > m_run + SOLO_SLACK;
-      const float e = __builtin_amdgcn_exp2f(m_run - m_new);       // 0 while m_run = -inf
+      const float e = __builtin_amdgcn_exp2f(m_run - m_new);       // 0 on the first block (m_run = -FLT_MAX)
       st.alpha = up ? e : 1.0f;
       m_run = up ? m_new : m_run;
       l_run *= st.alpha;
@@ -1056,10 +1056,10 @@ struct DecoderSolo {
     const int l = threadIdx.x & 63;
     const float l_tot = sum_xor32(l_run);
     const float e_tot = sum_xor32(e_run);
-    // a multi-token row that sees none of this chunk's tokens: zeros, -inf
-    const bool seen = visible(l) > 0;
-    const float inv = seen ? 1.0f / l_tot : 0.0f;
-    const float lse_v = seen ? (m_run + __log2f(e_tot)) * LN2 : -INFINITY;
+    // l_tot >= 1 unless the row saw no token of the chunk (a multi-token row
+    // past its position): then o = 0 and lse = log 0 = -inf
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float lse_v = (m_run + __log2f(e_tot)) * LN2;
     const int head = head_of(l);
     if (l < 32 && head < a.H) {
       if (a.direct) {
@@ -1077,7 +1077,7 @@ struct DecoderSolo {
       for (int q = 0; q < 4; ++q) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = to_bf16(seen ? o[j][4 * q + e] * inv : 0.0f);
+        for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[j][4 * q + e] * inv);
         const int c = j * 4 + q;                            // 16-byte chunk of the row
         *reinterpret_cast<bf16x4 *>(srow + ((c ^ (row & 15)) << 4)) = v;
       }
