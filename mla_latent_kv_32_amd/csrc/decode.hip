@@ -808,6 +808,10 @@ struct DecoderSolo {
       l_run *= st.alpha;
       e_run *= st.alpha;
       st.pe = 0.f;
+      // Each step's results are pinned where the step stands: the compiler
+      // would otherwise sink the softmax past the rescale branch, out from
+      // under the score MFMAs it is spread over.
+      asm volatile("" : "+v"(m_run), "+v"(st.alpha), "+v"(l_run), "+v"(e_run));
     } else if (k < 11) {
       // two registers per step: 2 (k - 3), 2 (k - 3) + 1
 #pragma unroll
@@ -817,6 +821,7 @@ struct DecoderSolo {
         st.pe += f;
         st.p[i >> 3][i & 7] = to_bf16(f);
       }
+      asm volatile("" : "+v"(st.pe), "+v"(st.p[(2 * (k - 3)) >> 3]));
     } else if (k < 13) {
       // sum of the rounded weights (bf16 pairs dotted with (1, 1))
       const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
@@ -826,6 +831,7 @@ struct DecoderSolo {
       for (int i = 0; i < 4; ++i) ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{q[2 * i], q[2 * i + 1]}, one2, ps, false);
       l_run = ps;
       if (k == 12) e_run += st.pe;
+      asm volatile("" : "+v"(l_run), "+v"(e_run));
     }
   }
   // Scores of tokens at or past `lim` (mask_limit) set to -inf: the block
@@ -868,7 +874,9 @@ struct DecoderSolo {
   // block i + 1's scores on return.  first: block i is block 0 (the
   // accumulators are still zero).  Block i is never the last block of the
   // chunk; multi-token rows that do not see some of its tokens have them
-  // masked beforehand (mask_scores).
+  // masked beforehand (mask_scores).  Operands are read in order and used in
+  // swapped pairs (MFMA slot 2m takes read 2m + 1, slot 2m + 1 read 2m), so a
+  // single LDS wait before each pair covers both of its reads.
   template <bool COPY>
   __device__ __forceinline__ void phase(const uint8_t *slot_s, const uint8_t *slot_v, f32x16 &s, bool first,
                                         const Copy &cp) {
@@ -883,7 +891,7 @@ struct DecoderSolo {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + RK < KS) kr[ks + RK] = kread(slot_s, kb, krb, ks + RK);
-      mfma_s(sn, kr[ks], qf[ks], ks == 0, ks == KS - 1);
+      mfma_s(sn, kr[ks ^ 1], qf[ks ^ 1], ks == 0, ks == KS - 1);
       if ((ks & 1) == 0 && ks / 2 < 13) soft_step(ks / 2, s, st, false, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -899,7 +907,7 @@ struct DecoderSolo {
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
       if (n + RV < NV) vf[n + RV] = vread(slot_v, vb, n + RV);
-      mfma_o(o[n & 15], vf[n], st.p[n >> 4], n == 0, false);
+      mfma_o(o[(n ^ 1) & 15], vf[n ^ 1], st.p[(n ^ 1) >> 4], n == 0, false);
       if (COPY && n % 3 == 1 && n / 3 < NI) copy(cp, n / 3, voff, roff);   // copies k = 0..8 at n = 3 k + 1
     }
     s = sn;
@@ -991,7 +999,7 @@ struct DecoderSolo {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + RK < KS) kr[ks + RK] = kread(slot_s, kb, krb, ks + RK);
-      mfma_s(sn, kr[ks], qf[ks], ks == 0, ks == KS - 1);
+      mfma_s(sn, kr[ks ^ 1], qf[ks ^ 1], ks == 0, ks == KS - 1);
       if ((ks & 1) == 0 && ks / 2 < 13) soft_step(ks / 2, s, st, false, 0);
       if (COPY && (ks & 1) == 1 && ks / 2 < NI8) copy8(blk_n, phys_n, stage_n, ks / 2);
       __builtin_amdgcn_sched_barrier(0);
@@ -1003,7 +1011,7 @@ struct DecoderSolo {
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
       if (n + RV < NV) vf[n + RV] = vread(slot_v, vb, n + RV);
-      mfma_o(o[n & 15], vf[n], st.p[n >> 4], n == 0, false);
+      mfma_o(o[(n ^ 1) & 15], vf[n ^ 1], st.p[(n ^ 1) >> 4], n == 0, false);
       if (EXPAND) {
         if (n == 0) {
           if (COPY) wait_vmcnt<NI8>();
