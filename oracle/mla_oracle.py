@@ -438,6 +438,49 @@ def prefill_mha_form(x, w_dkv, w_kr, w_q, w_uk, w_uv, d_nope, d_r, scale, theta=
     return o, c, kr, q_nope, q_rot
 
 
+def prefill_explicit(q_nope, q_pe, c, k_pe, w_uk, w_uv, scale, theta=10000.0):
+    """Causal prefill of one prompt of T tokens in the explicit (MHA) form, from its
+    projected inputs.
+
+    [Su] Part 3 MHA form (eq:mla-mha) with the Part 2 decoupled RoPE; [Riju]
+    non-absorbed module.  Token t sits at position t.  q_nope [T,H,d_nope],
+    q_pe [T,H,d_r] and k_pe [T,d_r] unrotated, c [T,d_c], W_UK [H,d_nope,d_c],
+    W_UV [H,d_c,d_v]:
+        K^(h) = [c W_UK[h]^T | RoPE(k_pe)],  V^(h) = c W_UV[h],
+        Q^(h) = [q_nope[:,h] | RoPE(q_pe[:,h])]
+        o_t^(h) = sum_{i<=t} softmax_i(scale Q_t^(h) . K_i^(h)) V_i^(h)
+    Returns (o [T,H,d_v], rows [T, d_c + d_r]) where rows are the latent-cache
+    rows [c_t | RoPE(k_pe_t, t)] the prompt leaves behind.
+    """
+    q_nope = np.asarray(q_nope, F64)
+    c = np.asarray(c, F64)
+    T, H = q_nope.shape[:2]
+    pos = np.arange(T, dtype=F64)
+    kr = rope(np.asarray(k_pe, F64), pos, theta)
+    q_rot = rope(np.asarray(q_pe, F64), pos[:, None], theta)
+    causal = np.tril(np.ones((T, T), bool))
+    o = np.zeros((T, H, np.asarray(w_uv).shape[2]))
+    for h in range(H):
+        k_h = np.concatenate([c @ np.asarray(w_uk[h], F64).T, kr], 1)
+        v_h = c @ np.asarray(w_uv[h], F64)
+        q_h = np.concatenate([q_nope[:, h], q_rot[:, h]], 1)
+        p, _ = softmax_lse(np.where(causal, scale * (q_h @ k_h.T), -np.inf))
+        o[:, h] = p @ v_h
+    return o, np.concatenate([c, kr], 1)
+
+
+def reference_prefill(inp, b, heads=None):
+    """Prefill reference for prompt b of a batch from synth.prefill_workload:
+    (o [T_b, h, d_v], rows [T_b, d_c + d_r]) by prefill_explicit on its tokens."""
+    t0, t1 = int(inp["cu_seqlens"][b]), int(inp["cu_seqlens"][b + 1])
+    H = np.asarray(inp["q_nope"]).shape[1]
+    heads = list(range(H)) if heads is None else list(heads)
+    return prefill_explicit(bf16_to_f64(inp["q_nope"][t0:t1])[:, heads], bf16_to_f64(inp["q_pe"][t0:t1])[:, heads],
+                            bf16_to_f64(inp["c"][t0:t1]), bf16_to_f64(inp["k_pe"][t0:t1]),
+                            bf16_to_f64(inp["w_uk"])[heads], bf16_to_f64(inp["w_uv"])[heads],
+                            inp["scale"], inp["theta"])
+
+
 # --------------------------------------------------------------------------
 # cache-size arithmetic ([Riju] "The Cache Arithmetic", "Worked numbers")
 # --------------------------------------------------------------------------

@@ -302,6 +302,30 @@ def multi_token_query(seed, B, q_len, H):
     return f32_to_bf16_bits(np.concatenate([q_lat, q_rot], -1))
 
 
+def prefill_workload(seed, H, lens, kv_dtype=KV_BF16):
+    """Prompts of the given lengths for the explicit-form prefill, packed
+    token-major (cu_seqlens offsets): q_nope [T, H, 128], q_pe [T, H, 64],
+    c [T, 512], k_pe [T, 64] drawn N(0, 1) (c W_UK^T then has unit variance,
+    like the decode workloads' keys), W_UK / W_UV N(0, 1/d_c) as elsewhere,
+    and a page layout for the cache rows the prompts leave (64-token pages in
+    a seeded permutation)."""
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in lens]
+    T = int(sum(lens))
+    w_uk = f32_to_bf16_bits(_normal(rng, (H, D_NOPE, D_C), 1 / math.sqrt(D_C)))
+    w_uv = f32_to_bf16_bits(_normal(rng, (H, D_C, D_V), 1 / math.sqrt(D_C)))
+    q_nope = f32_to_bf16_bits(_normal(rng, (T, H, D_NOPE)))
+    q_pe = f32_to_bf16_bits(_normal(rng, (T, H, D_R)))
+    c = f32_to_bf16_bits(_normal(rng, (T, D_C)))
+    k_pe = f32_to_bf16_bits(_normal(rng, (T, D_R)))
+    table, nblocks = page_layout(rng, np.asarray(lens, np.int32))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return dict(B=len(lens), H=H, lens=np.asarray(lens, np.int32), cu_seqlens=cu, T=T,
+                q_nope=q_nope, q_pe=q_pe, c=c, k_pe=k_pe, w_uk=w_uk, w_uv=w_uv,
+                block_table=table, num_blocks=nblocks, block_size=BLOCK, kv_dtype=kv_dtype,
+                theta=ROPE_THETA, scale=1 / math.sqrt(D_NOPE + D_R))
+
+
 def random_bf16(seed, shape, std=1.0):
     """Plain N(0, std^2) draw rounded to bf16 bits (stand-alone operands for single-kernel tests)."""
     return f32_to_bf16_bits(_normal(np.random.default_rng(seed), shape, std))

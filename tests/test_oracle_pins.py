@@ -489,3 +489,65 @@ def test_reference_decode_multi_last_query_is_the_decode():
         np.testing.assert_allclose(lse[-1], ld, rtol=1e-13)
     o, lse = oracle.reference_decode_multi(w, qm, 1)
     assert (o[:2] == 0).all() and np.isneginf(lse[:2]).all()
+
+
+# --------------------------------------------- explicit-form prefill (PIN-12)
+def _tiny_prefill(rng, T, H, dn=6, dr=4, dc=10, dv=5):
+    return (rng.standard_normal((T, H, dn)), rng.standard_normal((T, H, dr)), rng.standard_normal((T, dc)),
+            rng.standard_normal((T, dr)), rng.standard_normal((H, dn, dc)) / 3, rng.standard_normal((H, dc, dv)) / 3)
+
+
+def test_prefill_explicit_matches_brute_force():
+    """Plain loops over the causal MHA definition with per-head K and V."""
+    rng = np.random.default_rng(21)
+    T, H = 7, 2
+    qn, qp, c, kp, wuk, wuv = _tiny_prefill(rng, T, H)
+    o, rows = oracle.prefill_explicit(qn, qp, c, kp, wuk, wuv, 0.4, theta=100.0)
+    kr = oracle.rope(kp, np.arange(T, dtype=float), 100.0)
+    qr = oracle.rope(qp, np.arange(T, dtype=float)[:, None], 100.0)
+    for t in range(T):
+        for h in range(H):
+            q = list(qn[t, h]) + list(qr[t, h])
+            sc = []
+            for i in range(t + 1):
+                k = [sum(c[i, m] * wuk[h, d, m] for m in range(c.shape[1])) for d in range(qn.shape[2])] + list(kr[i])
+                sc.append(0.4 * sum(a * b for a, b in zip(q, k)))
+            z = sum(math.exp(v) for v in sc)
+            v_rows = [[sum(c[i, m] * wuv[h, m, e] for m in range(c.shape[1])) for e in range(wuv.shape[2])]
+                      for i in range(t + 1)]
+            want = [sum(math.exp(sc[i]) / z * v_rows[i][e] for i in range(t + 1)) for e in range(wuv.shape[2])]
+            np.testing.assert_allclose(o[t, h], want, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(rows, np.concatenate([c, kr], 1), rtol=0, atol=0)
+
+
+def test_prefill_rows_equal_absorbed_decode_of_each_prefix():
+    """Token t of the prefill equals the absorbed decode of the prefix 0..t
+    followed by the value up-projection (the absorption identity)."""
+    rng = np.random.default_rng(22)
+    T, H = 40, 3
+    qn, qp, c, kp = (rng.standard_normal((T, H, 128)), rng.standard_normal((T, H, 64)),
+                     rng.standard_normal((T, 512)), rng.standard_normal((T, 64)))
+    wuk, wuv = rng.standard_normal((H, 128, 512)) / 22.6, rng.standard_normal((H, 512, 128)) / 22.6
+    o, rows = oracle.prefill_explicit(qn, qp, c, kp, wuk, wuv, 1 / math.sqrt(192))
+    q_rot = oracle.rope(qp, np.arange(T, dtype=float)[:, None])
+    for t in [0, 1, 17, T - 1]:
+        o_lat, _ = oracle.decode_absorbed(oracle.absorb_q(qn[t], wuk), q_rot[t], rows[:t + 1, :512],
+                                          rows[:t + 1, 512:], 1 / math.sqrt(192))
+        np.testing.assert_allclose(oracle.absorb_out(o_lat, wuv), o[t], rtol=1e-10, atol=1e-12)
+    # token 0 sees only itself: o_0 = c_0 W_UV
+    np.testing.assert_allclose(o[0], np.einsum("m,hme->he", c[0], wuv), rtol=1e-12)
+
+
+def test_prefill_explicit_equals_mha_form_workload0():
+    """From the projections of workload 0, the explicit prefill gives the
+    MHA-form result computed from the hidden states."""
+    w = synth.workload(0)
+    o, c, kr, q_nope, q_rot = oracle.prefill_mha_form(
+        w["x"], w["w_dkv"], w["w_kr"], w["w_q"], w["w_uk"], w["w_uv"], w["d_nope"], w["d_r"], w["scale"], w["theta"])
+    x = np.asarray(w["x"], np.float64)
+    q = (x @ np.asarray(w["w_q"], np.float64)).reshape(w["S"], w["H"], -1)
+    o2, rows = oracle.prefill_explicit(q[..., :w["d_nope"]], q[..., w["d_nope"]:], c,
+                                       x @ np.asarray(w["w_kr"], np.float64), w["w_uk"], w["w_uv"],
+                                       w["scale"], w["theta"])
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(rows[:, w["d_c"]:], kr, rtol=1e-13, atol=1e-15)
