@@ -279,6 +279,40 @@ int mla_decode_combine_absorb_out(const void *workspace, size_t workspace_bytes,
                                   const void *w_uv, void *o, void *o_latent, float *lse,
                                   int B, int H, int d_c, int d_v, void *stream);
 
+/*
+ * Prefill of whole prompts in the explicit (non-absorbed) form, which needs
+ * (192 + 128) / (576 + 512) of the absorbed form's attention FLOPs (Su, Part
+ * 3: the MHA form eq:mla-mha for prefill, the MQA form for decoding; Riju,
+ * non-absorbed module).  Prompt b is tokens cu_seqlens[b] ..
+ * cu_seqlens[b + 1] - 1 of the packed inputs, token t of a prompt at position
+ * t; for every head h
+ *   K^(h) = [c W_UK[h]^T | RoPE(k_pe)],  V^(h) = c W_UV[h]
+ *   o[t,h] = sum_{i <= t} softmax_i(softmax_scale [q_nope | RoPE(q_pe)]_t . K_i^(h)) V_i^(h)
+ * and row t of prompt b, [c_t | RoPE(k_pe_t, t)], is written to the paged
+ * cache at position t of block-table row b (bf16, or fp8 quantised as in
+ * mla_rope_append_cache), ready for the decode steps.
+ *   q_nope      [T, H, 128] bf16        q_pe  [T, H, 64] bf16 (unrotated)
+ *   c_kv        [T, 512] bf16 latents   k_pe  [T, 64] bf16 (unrotated)
+ *   w_uk        [H, 128, 512] bf16      w_uv  [H, 512, 128] bf16
+ *   cu_seqlens  [B + 1] int32 device, non-decreasing, cu_seqlens[0] = 0,
+ *               cu_seqlens[B] = total_tokens (T); host bounds: max_seqlen >=
+ *               every prompt length, <= max_blocks_per_seq * block_size
+ *   kv_cache, kv_dtype, block_table, num_blocks, block_size as for
+ *               mla_rope_append_cache
+ *   o           [T, H, 128] bf16 output
+ *   workspace   device buffer of mla_prefill_workspace_bytes(T, H) bytes
+ *               (rotated queries and keys, per-head K and V, W_UK transposed)
+ * Empty prompts write nothing.  Errors as for the decode calls.
+ */
+size_t mla_prefill_workspace_bytes(int total_tokens, int H);
+
+int mla_prefill(const void *q_nope, const void *q_pe, const void *c_kv, const void *k_pe,
+                const void *w_uk, const void *w_uv, const int32_t *cu_seqlens, int B,
+                int total_tokens, int max_seqlen, int H, float softmax_scale, float rope_theta,
+                const int32_t *block_table, int max_blocks_per_seq, void *kv_cache, int kv_dtype,
+                int num_blocks, int block_size, void *o, void *workspace, size_t workspace_bytes,
+                void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,6 +22,7 @@ __all__ = [
     "mla_absorb_q", "mla_rope_append_cache", "mla_decode_paged", "mla_absorb_out",
     "mla_decode_workspace_bytes", "mla_decode_split_tokens", "mla_decode_partial", "mla_decode_combine",
     "mla_decode_combine_absorb_out", "mla_absorb_q_rope_append", "mla_decode_paged_multi", "MAX_Q_LEN",
+    "mla_prefill", "mla_prefill_workspace_bytes",
 ]
 
 KV_BF16 = 0
@@ -81,6 +82,11 @@ def lib():
     L.mla_decode_paged_multi.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
                                          vp, c_size, vp, vp, c_int, c_int, c_int, vp]
     L.mla_decode_paged_multi.restype = c_int
+    L.mla_prefill_workspace_bytes.argtypes = [c_int, c_int]
+    L.mla_prefill_workspace_bytes.restype = c_size
+    L.mla_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32p, c_int, c_int, c_int, c_int, c_float, c_float,
+                              i32p, c_int, vp, c_int, c_int, c_int, vp, vp, c_size, vp]
+    L.mla_prefill.restype = c_int
     L.mla_decode_partial.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
                                      vp, c_size, c_int, c_int, vp]
     L.mla_decode_partial.restype = c_int
@@ -224,6 +230,37 @@ def mla_decode_paged_multi(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq
         _ptr(q), _ptr(kv_cache), int(kv_dtype), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
         int(max_seq_len), kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(split_tokens),
         _ptr(workspace), ws_bytes, _ptr(o_latent), _ptr(lse), B, H, q_len, _stream(stream)))
+
+
+def mla_prefill_workspace_bytes(total_tokens, H) -> int:
+    return int(lib().mla_prefill_workspace_bytes(total_tokens, H))
+
+
+def mla_prefill(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, cu_seqlens, max_seqlen, softmax_scale, rope_theta,
+                block_table, kv_cache, kv_dtype, o, workspace=None, stream=None):
+    """Causal prefill of packed prompts in the explicit form; also writes their cache rows.
+
+    q_nope [T,H,128], q_pe [T,H,64], c_kv [T,512], k_pe [T,64], w_uk [H,128,512], w_uv [H,512,128]
+    (bf16); cu_seqlens [B+1] int32; block_table [B, max_blocks] int32; kv_cache as for
+    mla_rope_append_cache; o [T,H,128] bf16.  A workspace of mla_prefill_workspace_bytes(T, H)
+    bytes is allocated with torch when not given.
+    """
+    T, H, _ = q_nope.shape
+    for t, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (c_kv, "c_kv"), (k_pe, "k_pe"), (w_uk, "w_uk"),
+                 (w_uv, "w_uv"), (o, "o")):
+        _dense(t, n, torch.bfloat16)
+    _dense(cu_seqlens, "cu_seqlens", torch.int32)
+    _dense(block_table, "block_table", torch.int32)
+    _dense(kv_cache, "kv_cache")
+    B = cu_seqlens.shape[0] - 1
+    if workspace is None and T > 0:
+        workspace = torch.empty(mla_prefill_workspace_bytes(T, H), dtype=torch.uint8, device=q_nope.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_prefill", lib().mla_prefill(
+        _ptr(q_nope), _ptr(q_pe), _ptr(c_kv), _ptr(k_pe), _ptr(w_uk), _ptr(w_uv), _ptr(cu_seqlens), B, T,
+        int(max_seqlen), H, float(softmax_scale), float(rope_theta), _ptr(block_table), block_table.shape[1],
+        _ptr(kv_cache), int(kv_dtype), kv_cache.shape[0], kv_cache.shape[1], _ptr(o), _ptr(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def mla_decode_partial(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, softmax_scale, workspace,

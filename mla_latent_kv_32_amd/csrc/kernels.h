@@ -87,4 +87,34 @@ hipError_t launch_rope_append(const RopeAppendArgs &a, hipStream_t stream);
 // mla_absorb_q and mla_rope_append_cache in one launch (ra.q receives both parts).
 hipError_t launch_query(const uint16_t *q_nope, const uint16_t *w_uk, const RopeAppendArgs &ra, hipStream_t stream);
 
+// Explicit-form prefill of B packed prompts (T tokens in all, token-major,
+// prompt b = tokens cu_seqlens[b] .. cu_seqlens[b + 1] - 1 at positions 0..).
+struct PrefillArgs {
+  const uint16_t *q_nope;       // [T, H, 128]
+  const uint16_t *q_pe;         // [T, H, 64], unrotated
+  const uint16_t *c;            // [T, 512] latents
+  const uint16_t *k_pe;         // [T, 64], unrotated shared rotary key
+  const uint16_t *w_uk;         // [H, 128, 512]
+  const uint16_t *w_uv;         // [H, 512, 128]
+  const int32_t *cu_seqlens;    // [B + 1]
+  const int32_t *block_table;   // [B, max_blocks]
+  int max_blocks;
+  uint8_t *cache;
+  int kv_fp8;
+  double inv_freq[32];
+  float scale_log2;             // softmax_scale * log2(e)
+  int B, H, T, max_len;
+  uint16_t *o;                  // [T, H, 128]
+  // workspace
+  uint16_t *q_rot;              // [T, H, 64]
+  uint16_t *k_rot;              // [T, 64]
+  uint16_t *k_nope;             // [T, H, 128]
+  uint16_t *v;                  // [T, H, 128]
+  uint16_t *w_ukt;              // [H, 512, 128] = W_UK transposed per head
+};
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+// out[t, h, :] = act[t, :] . W[h]  (act [T, 512] shared by the heads, W [H, 512, 128], out [T, H, 128])
+hipError_t launch_shared_act_gemm(const uint16_t *act, const uint16_t *w, uint16_t *out, int T, int H,
+                                  hipStream_t stream);
+
 }  // namespace mla

@@ -1,0 +1,283 @@
+// Prefill of whole prompts in the explicit (non-absorbed) form.
+//
+// For prompts the absorbed form would multiply the attention FLOPs by
+// (576 + 512) / (192 + 128) = 3.4 (Su, "The Ultimate Tug-of-War Between Cache
+// and Performance", Part 3: MHA form eq:mla-mha for training and prefill, the
+// MQA form eq:mla-mqa for decoding; Riju, "Multi-Head Latent Attention vs GQA
+// vs MQA", non-absorbed module).  So each head gets its own keys and values,
+// rebuilt from the latent:
+//   K^(h) = [c W_UK[h]^T | RoPE(k_pe)]   (192 wide; the rotary part shared)
+//   V^(h) = c W_UV[h]                    (128 wide)
+//   o_t^(h) = sum_{i <= t} softmax_i(scale [q_nope | RoPE(q_pe)]_t . K_i^(h)) V_i^(h)
+// and the prompt's rows [c_t | RoPE(k_pe_t, t)] go to the paged latent cache
+// for the decode steps that follow.  Token t of a prompt sits at position t.
+//
+// Launches: RoPE + cache rows; W_UK transposed per head; the two
+// up-projections (shared_act_kernel in absorb.hip); causal attention.
+#include "common.h"
+#include "kernels.h"
+#include "rope.h"
+
+namespace mla {
+namespace {
+
+// ---- RoPE of the prompt tokens and their cache rows.  Workgroup (b, y)
+// handles positions 8 y .. 8 y + 7 of prompt b: the query pairs of every
+// head (to the workspace), the shared rotary key (to the workspace, for the
+// attention) and the cache row.
+constexpr int ROPE_TOK = 8;
+
+__global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
+  __shared__ float cs[DR / 2], sn[DR / 2];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int t_begin = a.cu_seqlens[b];
+  const int L = a.cu_seqlens[b + 1] - t_begin;
+  for (int j = 0; j < ROPE_TOK; ++j) {
+    const int pos = blockIdx.y * ROPE_TOK + j;
+    if (pos >= L) break;
+    const size_t t = static_cast<size_t>(t_begin) + pos;
+    __syncthreads();                       // cs / sn free again
+    if (tid < DR / 2) rope_cos_sin(a.inv_freq, pos, tid, cs[tid], sn[tid]);
+    __syncthreads();
+    for (int idx = tid; idx < a.H * (DR / 2); idx += blockDim.x) {
+      const int h = idx / (DR / 2), i = idx % (DR / 2);
+      const size_t th = t * a.H + h;
+      const uint32_t pr = *reinterpret_cast<const uint32_t *>(a.q_pe + th * DR + 2 * i);
+      *reinterpret_cast<uint32_t *>(a.q_rot + th * DR + 2 * i) = rope_rotate_pair(pr, cs[i], sn[i]);
+    }
+    if (tid < DR / 2) {
+      const uint32_t pr = *reinterpret_cast<const uint32_t *>(a.k_pe + t * DR + 2 * tid);
+      *reinterpret_cast<uint32_t *>(a.k_rot + t * DR + 2 * tid) = rope_rotate_pair(pr, cs[tid], sn[tid]);
+    }
+    const int page = a.block_table[static_cast<size_t>(b) * a.max_blocks + pos / PAGE];
+    store_cache_row(a.cache, a.kv_fp8, static_cast<size_t>(page) * PAGE + pos % PAGE, a.c + t * DC,
+                    a.k_pe + t * DR, tid, cs, sn);
+  }
+}
+
+// ---- W_UK[h] [128, 512] -> W_UK[h]^T [512, 128] (32 x 32 tiles through LDS)
+__global__ __launch_bounds__(256) void transpose_wuk_kernel(const uint16_t *w, uint16_t *wt) {
+  __shared__ uint16_t tile[32][33];
+  const int k0 = blockIdx.x * 32, n0 = blockIdx.y * 32, h = blockIdx.z;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;           // 32 x 8
+  const uint16_t *src = w + static_cast<size_t>(h) * DNOPE * DC;
+  uint16_t *dst = wt + static_cast<size_t>(h) * DC * DNOPE;
+  for (int r = ty; r < 32; r += 8) tile[r][tx] = src[static_cast<size_t>(n0 + r) * DC + k0 + tx];
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) dst[static_cast<size_t>(k0 + r) * DNOPE + n0 + tx] = tile[tx][r];
+}
+
+// ---- causal attention, one head and 128 query rows per workgroup.
+//
+// Four waves of 32 query rows each; keys in blocks of 32, staged in LDS and
+// shared by the four waves.  Both products are v_mfma_f32_32x32x16_bf16 with
+// the query rows as the 32-wide N dimension, the layout of the decode's
+// one-wave-per-SIMD kernel:
+//   scores   S^T[key, q] = K[key, 0:192] . Q^T over 12 k-steps; the query
+//            fragments (48 VGPRs) stay in registers
+//   softmax  on the score accumulator: lane (q row l % 32, hb = l / 32) holds
+//            keys pi(8 (i / 4) + 4 hb + i % 4) of register i
+//   values   O^T[d, q] += V^T[d, key] . P^T[key, q]; registers 8 t .. 8 t + 7
+//            of the score accumulator, rounded to bf16, are the B operand of
+//            key step t as they stand (keys stored in natural order, the
+//            MFMA's K-row m reading key pi(m))
+// LDS rows are padded to strides that are odd multiples of 16 bytes (400 for
+// K, 272 for V), so the score reads (row pi(l % 32), one 16-byte chunk) and
+// the transposed value reads (rows 4 apart) spread over all bank quads.
+constexpr int FA_Q = 128;                       // query rows per workgroup
+constexpr int FA_KB = 32;                       // keys per block
+constexpr int FA_KS = (DNOPE + DR) / 16;        // 12 score k-steps
+constexpr int FA_KLROW = (DNOPE + DR) * 2 + 16; // 400
+constexpr int FA_VLROW = DV * 2 + 16;           // 272
+constexpr int FA_KBUF = FA_KB * FA_KLROW;       // 12800
+constexpr int FA_BUF = FA_KBUF + FA_KB * FA_VLROW;   // 21504
+constexpr int FA_KCH = FA_KB * (DNOPE + DR) / 8;     // 768 16-byte chunks of a K block
+constexpr int FA_VCH = FA_KB * DV / 8;               // 512 of a V block
+constexpr int FA_LD = (FA_KCH + FA_VCH) / 256;       // 5 chunk loads per thread per block
+constexpr float FA_SLACK = 16.0f;                    // lazy rescale margin (log2 units)
+static_assert((FA_KCH + FA_VCH) % 256 == 0, "block chunks split evenly over 256 threads");
+static_assert(FA_Q * DV * 2 <= 2 * FA_BUF, "the output tile is staged in the block buffers");
+
+__device__ __forceinline__ int fa_pi(int m) {
+  return 16 * ((m >> 2) & 1) + 4 * (m & 3) + 2 * ((m >> 4) & 1) + ((m >> 3) & 1);
+}
+__device__ __forceinline__ float fa_max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float fa_sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void prefill_attention_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * FA_BUF];
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int t_begin = a.cu_seqlens[b];
+  const int L = a.cu_seqlens[b + 1] - t_begin;
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * FA_Q;     // longest tiles first
+  if (q0 >= L) return;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hb = l >> 5;
+  const int qi = q0 + wave * 32 + (l & 31);                 // this lane's query row (position)
+  const int H = a.H;
+  const int nkb = (min(L, q0 + FA_Q) + FA_KB - 1) / FA_KB;
+
+  // query fragments: lane (q row, hb) holds dims 16 ks + 8 hb .. + 8
+  bf16x8 qf[FA_KS];
+  {
+    const size_t th = (static_cast<size_t>(t_begin) + min(qi, L - 1)) * H + h;
+#pragma unroll
+    for (int ks = 0; ks < FA_KS; ++ks) {
+      const uint16_t *src = ks < DNOPE / 16 ? a.q_nope + th * DNOPE + 16 * ks + 8 * hb
+                                            : a.q_rot + th * DR + 16 * (ks - DNOPE / 16) + 8 * hb;
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src));
+    }
+  }
+
+  // block loads: thread chunk idx = tid + 256 j; K chunks first, then V
+  u32x4 stg[FA_LD];
+  auto load_block = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < FA_LD; ++j) {
+      const int idx = tid + 256 * j;
+      if (idx < FA_KCH) {
+        const int n = idx / 24, c = idx % 24;
+        const size_t t = static_cast<size_t>(t_begin) + min(kb * FA_KB + n, L - 1);
+        const uint16_t *src = c < 16 ? a.k_nope + (t * H + h) * DNOPE + 8 * c : a.k_rot + t * DR + 8 * (c - 16);
+        stg[j] = *reinterpret_cast<const u32x4 *>(src);
+      } else {
+        const int v = idx - FA_KCH, n = v / 16, c = v % 16;
+        const size_t t = static_cast<size_t>(t_begin) + min(kb * FA_KB + n, L - 1);
+        stg[j] = *reinterpret_cast<const u32x4 *>(a.v + (t * H + h) * DV + 8 * c);
+      }
+    }
+  };
+  auto store_block = [&](uint8_t *buf) {
+#pragma unroll
+    for (int j = 0; j < FA_LD; ++j) {
+      const int idx = tid + 256 * j;
+      if (idx < FA_KCH) {
+        const int n = idx / 24, c = idx % 24;
+        *reinterpret_cast<u32x4 *>(buf + n * FA_KLROW + 16 * c) = stg[j];
+      } else {
+        const int v = idx - FA_KCH, n = v / 16, c = v % 16;
+        *reinterpret_cast<u32x4 *>(buf + FA_KBUF + n * FA_VLROW + 16 * c) = stg[j];
+      }
+    }
+  };
+
+  // per-lane read bases
+  const int kbase = fa_pi(l & 31) * FA_KLROW + 16 * hb;     // + 32 ks
+  const int vrow = 16 * hb + 4 * ((l & 15) >> 2);
+  const int csub = 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
+  const int vbase = FA_KBUF + vrow * FA_VLROW + 16 * csub + 8 * (l & 1);   // + 2 t FA_VLROW + 64 j (+ FA_VLROW: hi)
+
+  f32x16 o[DV / 32];
+#pragma unroll
+  for (int j = 0; j < DV / 32; ++j) o[j] = f32x16{};
+  float m_run = -FLT_MAX, l_run = 0.f;
+  const float c = a.scale_log2;
+
+  load_block(0);
+  store_block(lds);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    uint8_t *buf = lds + (kb & 1) * FA_BUF;
+    if (kb + 1 < nkb) load_block(kb + 1);
+    // scores
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < FA_KS; ++ks) {
+      const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(buf + kbase + 32 * ks);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qf[ks], s, 0, 0, 0);
+    }
+    // causal mask: key kb * 32 + tok(i) is visible to query qi while <= qi
+    const int lim = qi - kb * FA_KB - 16 * hb;                // visible while tok - 16 hb <= lim
+    if (kb * FA_KB + FA_KB - 1 > q0 + wave * 32) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (4 * (i & 3) + 2 * (i >> 3) + ((i >> 2) & 1) > lim) s[i] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    const float m_new = fmaxf(m_run, fa_max_xor32(mx) * c);
+    float alpha = 1.0f;
+    if (m_new > m_run + FA_SLACK) {
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+    }
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int j = 0; j < DV / 32; ++j) o[j] *= alpha;
+    }
+    bf16x8 p[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i >> 3][i & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m_run)));
+    const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[i >> 2][2 * (i & 3)], p[i >> 2][2 * (i & 3) + 1]}, one2,
+                                              l_run, false);
+    // values
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int j = 0; j < DV / 32; ++j) {
+        const uint8_t *r0 = buf + vbase + 2 * t * FA_VLROW + 64 * j;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)r0);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(r0 + FA_VLROW));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[t], o[j], 0, 0, 0);
+      }
+    }
+    if (kb + 1 < nkb) store_block(lds + ((kb + 1) & 1) * FA_BUF);
+    __syncthreads();
+  }
+
+  // normalise; stage rows (query row = 32 wave + l % 32, 16-byte chunk x at
+  // position x ^ (row & 15)) and store whole 256-byte rows
+  const float inv = 1.0f / fa_sum_xor32(l_run);
+  const int row = wave * 32 + (l & 31);
+#pragma unroll
+  for (int j = 0; j < DV / 32; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[j][4 * q + e] * inv);
+      // columns 32 j + 8 q + 4 hb .. + 4: half of 16-byte chunk 4 j + q
+      const int x = 4 * j + q;
+      *reinterpret_cast<bf16x4 *>(lds + row * (DV * 2) + ((x ^ (row & 15)) << 4) + 8 * hb) = v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = wave * 32 + 4 * k + (l >> 4), x = l & 15;
+    const int qr = q0 + r;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + r * (DV * 2) + ((x ^ (r & 15)) << 4));
+    if (qr < L) *reinterpret_cast<u32x4 *>(a.o + ((static_cast<size_t>(t_begin) + qr) * H + h) * DV + 8 * x) = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
+  if (a.max_len <= 0 || a.T <= 0) return hipSuccess;
+  prefill_rope_kernel<<<dim3(a.B, (a.max_len + ROPE_TOK - 1) / ROPE_TOK), 256, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  transpose_wuk_kernel<<<dim3(DC / 32, DNOPE / 32, a.H), 256, 0, stream>>>(a.w_uk, a.w_ukt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_shared_act_gemm(a.c, a.w_ukt, a.k_nope, a.T, a.H, stream)) != hipSuccess) return e;
+  if ((e = launch_shared_act_gemm(a.c, a.w_uv, a.v, a.T, a.H, stream)) != hipSuccess) return e;
+  prefill_attention_kernel<<<dim3((a.max_len + FA_Q - 1) / FA_Q, a.H, a.B), 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

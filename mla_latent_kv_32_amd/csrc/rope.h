@@ -47,11 +47,14 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float x) {
 __device__ __forceinline__ int rope_position(int S) { return S > 0 ? S - 1 : 0; }
 
 // cos and sin of pos * inv_freq[i] (angle formed and reduced in float64).
-__device__ __forceinline__ void rope_cos_sin(const RopeAppendArgs &a, int pos, int i, float &c, float &s) {
+__device__ __forceinline__ void rope_cos_sin(const double *inv_freq, int pos, int i, float &c, float &s) {
   double sv, cv;
-  sincos(static_cast<double>(pos) * a.inv_freq[i], &sv, &cv);
+  sincos(static_cast<double>(pos) * inv_freq[i], &sv, &cv);
   c = static_cast<float>(cv);
   s = static_cast<float>(sv);
+}
+__device__ __forceinline__ void rope_cos_sin(const RopeAppendArgs &a, int pos, int i, float &c, float &s) {
+  rope_cos_sin(a.inv_freq, pos, i, c, s);
 }
 
 // One interleaved bf16 pair (packed low | high << 16) turned by the angle.
@@ -75,30 +78,27 @@ __device__ __forceinline__ void rope_query_pair(const RopeAppendArgs &a, int b, 
   rope_query_store(a, b, h, i, rope_query_load(a, b, h, i), c, s);
 }
 
-// Append the new token's row of sequence b (S = seq_lens[b] > 0) at position
-// S - 1: the latent part copied (bf16) or quantised (fp8, wave g quantises
-// group g), the rotary key turned by (cs[i], sn[i]) = angle of pair i at that
-// position.  Called by all 256 threads of a workgroup.
-__device__ __forceinline__ void append_row(const RopeAppendArgs &a, int b, int S, int tid, const float *cs,
-                                           const float *sn) {
-  const int pos = rope_position(S);
-  const int page = a.block_table[static_cast<size_t>(b) * a.max_blocks + (pos / PAGE)];
-  const uint16_t *src = a.kv_new + static_cast<size_t>(b) * DROW;
-  const size_t slot = static_cast<size_t>(page) * PAGE + (pos % PAGE);
-  uint8_t *row = a.cache + slot * (a.kv_fp8 ? FP8_ROW_BYTES : ROW_BYTES);
-  const int rope_off = a.kv_fp8 ? DC : 2 * DC;   // byte offset of the rotary key in the row
+// Store one latent-cache row at slot `slot` of the pool (page * 64 + offset):
+// the latent part `lat` (512 bf16) copied (bf16 pool) or quantised (fp8 pool:
+// wave g quantises group g), the rotary key `kpe` (64 bf16, unrotated) turned
+// by (cs[i], sn[i]) = angle of pair i at the token's position.  Called by all
+// 256 threads of a workgroup.
+__device__ __forceinline__ void store_cache_row(uint8_t *cache, int kv_fp8, size_t slot, const uint16_t *lat,
+                                                const uint16_t *kpe, int tid, const float *cs, const float *sn) {
+  uint8_t *row = cache + slot * (kv_fp8 ? FP8_ROW_BYTES : ROW_BYTES);
+  const int rope_off = kv_fp8 ? DC : 2 * DC;     // byte offset of the rotary key in the row
 
   if (tid < DR / 2) {
-    const uint32_t pr = *reinterpret_cast<const uint32_t *>(src + DC + 2 * tid);
+    const uint32_t pr = *reinterpret_cast<const uint32_t *>(kpe + 2 * tid);
     *reinterpret_cast<uint32_t *>(row + rope_off + 4 * tid) = rope_rotate_pair(pr, cs[tid], sn[tid]);
   }
-  if (!a.kv_fp8) {
+  if (!kv_fp8) {
     if (tid < DC / 8)
-      *reinterpret_cast<u32x4 *>(row + tid * 16) = *reinterpret_cast<const u32x4 *>(src + tid * 8);
+      *reinterpret_cast<u32x4 *>(row + tid * 16) = *reinterpret_cast<const u32x4 *>(lat + tid * 8);
     return;
   }
   // fp8: wave g quantises latent group g (128 values, 2 per lane).
-  const uint32_t pr = *reinterpret_cast<const uint32_t *>(src + 2 * tid);
+  const uint32_t pr = *reinterpret_cast<const uint32_t *>(lat + 2 * tid);
   const float v0 = bf16_to_f32(pr & 0xFFFFu), v1 = bf16_to_f32(pr >> 16);
   float amax = fmaxf(fabsf(v0), fabsf(v1));
 #pragma unroll
@@ -107,6 +107,16 @@ __device__ __forceinline__ void append_row(const RopeAppendArgs &a, int b, int S
   const uint32_t c0 = e4m3_rne_sat(v0 / scale), c1 = e4m3_rne_sat(v1 / scale);
   *reinterpret_cast<uint16_t *>(row + 2 * tid) = static_cast<uint16_t>(c0 | (c1 << 8));
   if ((tid & 63) == 0) *reinterpret_cast<float *>(row + DC + 2 * DR + 4 * (tid >> 6)) = scale;
+}
+
+// Append the new token's row of sequence b (S = seq_lens[b] > 0) at position
+// S - 1 from kv_new[b] = [latent | unrotated rotary key].
+__device__ __forceinline__ void append_row(const RopeAppendArgs &a, int b, int S, int tid, const float *cs,
+                                           const float *sn) {
+  const int pos = rope_position(S);
+  const int page = a.block_table[static_cast<size_t>(b) * a.max_blocks + (pos / PAGE)];
+  const uint16_t *src = a.kv_new + static_cast<size_t>(b) * DROW;
+  store_cache_row(a.cache, a.kv_fp8, static_cast<size_t>(page) * PAGE + (pos % PAGE), src, src + DC, tid, cs, sn);
 }
 
 }  // namespace mla

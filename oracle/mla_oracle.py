@@ -438,7 +438,7 @@ def prefill_mha_form(x, w_dkv, w_kr, w_q, w_uk, w_uv, d_nope, d_r, scale, theta=
     return o, c, kr, q_nope, q_rot
 
 
-def prefill_explicit(q_nope, q_pe, c, k_pe, w_uk, w_uv, scale, theta=10000.0):
+def prefill_explicit(q_nope, q_pe, c, k_pe, w_uk, w_uv, scale, theta=10000.0, with_magnitude=False):
     """Causal prefill of one prompt of T tokens in the explicit (MHA) form, from its
     projected inputs.
 
@@ -450,7 +450,10 @@ def prefill_explicit(q_nope, q_pe, c, k_pe, w_uk, w_uv, scale, theta=10000.0):
         Q^(h) = [q_nope[:,h] | RoPE(q_pe[:,h])]
         o_t^(h) = sum_{i<=t} softmax_i(scale Q_t^(h) . K_i^(h)) V_i^(h)
     Returns (o [T,H,d_v], rows [T, d_c + d_r]) where rows are the latent-cache
-    rows [c_t | RoPE(k_pe_t, t)] the prompt leaves behind.
+    rows [c_t | RoPE(k_pe_t, t)] the prompt leaves behind; with_magnitude also
+    returns sum_i p_i |V_i| [T,H,d_v], the scale against which a relative
+    perturbation of the weights or values moves o (for stating tolerances;
+    not part of the method).
     """
     q_nope = np.asarray(q_nope, F64)
     c = np.asarray(c, F64)
@@ -460,25 +463,30 @@ def prefill_explicit(q_nope, q_pe, c, k_pe, w_uk, w_uv, scale, theta=10000.0):
     q_rot = rope(np.asarray(q_pe, F64), pos[:, None], theta)
     causal = np.tril(np.ones((T, T), bool))
     o = np.zeros((T, H, np.asarray(w_uv).shape[2]))
+    mag = np.zeros_like(o)
     for h in range(H):
         k_h = np.concatenate([c @ np.asarray(w_uk[h], F64).T, kr], 1)
         v_h = c @ np.asarray(w_uv[h], F64)
         q_h = np.concatenate([q_nope[:, h], q_rot[:, h]], 1)
         p, _ = softmax_lse(np.where(causal, scale * (q_h @ k_h.T), -np.inf))
         o[:, h] = p @ v_h
-    return o, np.concatenate([c, kr], 1)
+        if with_magnitude:
+            mag[:, h] = p @ np.abs(v_h)
+    rows = np.concatenate([c, kr], 1)
+    return (o, rows, mag) if with_magnitude else (o, rows)
 
 
-def reference_prefill(inp, b, heads=None):
+def reference_prefill(inp, b, heads=None, with_magnitude=False):
     """Prefill reference for prompt b of a batch from synth.prefill_workload:
-    (o [T_b, h, d_v], rows [T_b, d_c + d_r]) by prefill_explicit on its tokens."""
+    (o [T_b, h, d_v], rows [T_b, d_c + d_r][, magnitude]) by prefill_explicit
+    on its tokens."""
     t0, t1 = int(inp["cu_seqlens"][b]), int(inp["cu_seqlens"][b + 1])
     H = np.asarray(inp["q_nope"]).shape[1]
     heads = list(range(H)) if heads is None else list(heads)
     return prefill_explicit(bf16_to_f64(inp["q_nope"][t0:t1])[:, heads], bf16_to_f64(inp["q_pe"][t0:t1])[:, heads],
                             bf16_to_f64(inp["c"][t0:t1]), bf16_to_f64(inp["k_pe"][t0:t1]),
                             bf16_to_f64(inp["w_uk"])[heads], bf16_to_f64(inp["w_uv"])[heads],
-                            inp["scale"], inp["theta"])
+                            inp["scale"], inp["theta"], with_magnitude)
 
 
 # --------------------------------------------------------------------------

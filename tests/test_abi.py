@@ -162,6 +162,30 @@ def test_multi_token_call_validates():
     assert call(split=64, ws=FAKE, ws_bytes=need - 256) == -3
 
 
+@needs_lib
+def test_prefill_call_validates():
+    L = mla.lib()
+    pre = L.mla_prefill
+
+    def call(qn=FAKE, B=2, T=100, max_len=64, H=16, scale=0.07, theta=10000.0, mb=1, dt=0, bs=64, ws=FAKE,
+             ws_bytes=1 << 40):
+        return pre(qn, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, T, max_len, H, ctypes.c_float(scale),
+                   ctypes.c_float(theta), FAKE, mb, FAKE, dt, 16, bs, FAKE, ws, ws_bytes, NULL)
+    assert call(qn=NULL) == -1
+    assert call(qn=FAKE + 2) == -1
+    assert call(B=0) == -1
+    assert call(scale=float("nan")) == -1
+    assert call(theta=0.0) == -1
+    assert call(dt=5) == -1
+    assert call(bs=32) == -2
+    assert call(max_len=65) == -1            # beyond one page of block table
+    assert call(ws=NULL) == -3
+    assert call(ws_bytes=L.mla_prefill_workspace_bytes(100, 16) - 1) == -3
+    assert call(T=0) == 0                    # nothing to do, nothing launched
+    assert L.mla_prefill_workspace_bytes(0, 16) == 0
+    assert L.mla_prefill_workspace_bytes(100, 16) >= 100 * 16 * (64 + 2 * 128) * 2 + 100 * 64 * 2
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mla, "_LIB", None)
     monkeypatch.setenv("MLA_LIBRARY", str(tmp_path / "missing.so"))

@@ -1,0 +1,97 @@
+"""GPU parity of the explicit-form prefill (mla_prefill) against the fp64
+oracle: outputs within the bf16 bound |gpu - ref| <= 2e-3 + 2e-2 |ref|,
+widened by 2^-8 sum_i p_i |V_i| (the bf16 rounding of the softmax weights
+and of the materialised per-head values, 2^-9 each); the cache rows the
+prompts leave: latent copies and fp8 codes/scales bit for bit, rotated keys
+within the bf16 bound."""
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_32_amd as mla
+import oracle
+import synth
+from helpers import assert_close, bf16_tensor_to_f64, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+P_ROUNDING = 2.0 ** -8
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU parity tests need a ROCm device"
+    mla.lib()
+
+
+def run_prefill(w):
+    T, H = w["T"], w["H"]
+    fp8 = w["kv_dtype"] == synth.KV_FP8
+    shape = (w["num_blocks"], 64, 656 if fp8 else 576)
+    pool = torch.zeros(shape, dtype=torch.uint8 if fp8 else torch.bfloat16, device="cuda")
+    o = torch.full((T, H, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mla.mla_prefill(to_dev_bf16(w["q_nope"]), to_dev_bf16(w["q_pe"]), to_dev_bf16(w["c"]), to_dev_bf16(w["k_pe"]),
+                    to_dev_bf16(w["w_uk"]), to_dev_bf16(w["w_uv"]), to_dev(w["cu_seqlens"]), int(max(w["lens"])),
+                    w["scale"], w["theta"], to_dev(w["block_table"]), pool, w["kv_dtype"], o)
+    torch.cuda.synchronize()
+    pool = pool.cpu().numpy() if fp8 else pool.cpu().view(torch.int16).numpy().view(np.uint16)
+    return o, pool
+
+
+def check_prefill(w, o, pool, pairs, rows_for=()):
+    fp8 = w["kv_dtype"] == synth.KV_FP8
+    for b, heads in pairs:
+        heads = list(heads)
+        t0, t1 = int(w["cu_seqlens"][b]), int(w["cu_seqlens"][b + 1])
+        if t1 == t0:
+            continue
+        ref, rows, mag = oracle.reference_prefill(w, b, heads, with_magnitude=True)
+        got = bf16_tensor_to_f64(o[t0:t1][:, heads])
+        assert_close(got, ref, extra=P_ROUNDING * mag, what=f"o prompt b={b} L={t1 - t0}")
+        if b not in rows_for:
+            continue
+        for pos in range(t1 - t0):
+            page, slot = w["block_table"][b, pos // 64], pos % 64
+            row = pool[page, slot]
+            c_bits = w["c"][t0 + pos]
+            if fp8:
+                codes, scales = oracle.fp8_quantize_latent(c_bits)
+                np.testing.assert_array_equal(row[:512], codes, err_msg=f"fp8 codes b={b} pos={pos}")
+                np.testing.assert_array_equal(row[640:656].view(np.float32), scales, err_msg=f"scales b={b}")
+                got_kr = oracle.bf16_to_f64(row[512:640].view(np.uint16))
+            else:
+                np.testing.assert_array_equal(row[:512], c_bits, err_msg=f"latent copy b={b} pos={pos}")
+                got_kr = oracle.bf16_to_f64(row[512:])
+            assert_close(got_kr, rows[pos, 512:], what=f"k_rot b={b} pos={pos}")
+
+
+@pytest.mark.parametrize("H", [16, 128])
+@pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8])
+def test_prefill_matches_oracle(H, kv_dtype):
+    """Ragged prompts around the 32-key blocks and 128-row query tiles,
+    including a 1-token and an empty prompt."""
+    lens = [1, 0, 31, 33, 128, 129, 300]
+    w = synth.prefill_workload(700 + H + kv_dtype, H, lens, kv_dtype)
+    o, pool = run_prefill(w)
+    heads = range(H) if H <= 16 else [0, 1, 63, 127]
+    check_prefill(w, o, pool, [(b, heads) for b in range(len(lens))], rows_for=range(len(lens)))
+
+
+def test_prefill_rows_untouched_elsewhere():
+    """Only the prompts' own (page, slot) rows are written."""
+    lens = [5, 70, 64]
+    w = synth.prefill_workload(710, 4, lens)
+    o, pool = run_prefill(w)
+    touched = np.zeros(pool.shape[:2], bool)
+    for b, L in enumerate(lens):
+        for pos in range(L):
+            touched[w["block_table"][b, pos // 64], pos % 64] = True
+    assert (pool[~touched] == 0).all()
+
+
+def test_prefill_long_prompts_full_heads():
+    """Four 1024-token prompts with DeepSeek-V3's 128 heads (the benchmark's
+    prefill shape): sampled heads and every token of two prompts."""
+    w = synth.prefill_workload(720, 128, [1024] * 4)
+    o, pool = run_prefill(w)
+    assert not torch.isnan(o.float()).any().item()
+    check_prefill(w, o, pool, [(0, [0, 77]), (3, [127])])
