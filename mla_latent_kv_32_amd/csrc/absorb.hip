@@ -158,68 +158,6 @@ __global__ __launch_bounds__(NT * 2) void absorb_kernel(const uint16_t *act, con
   }
 }
 
-// Up-projection of latents shared by every head (the explicit-form prefill's
-// K and V): out[t, h, n0 .. n0 + NT) = act[t, :] . W[h][:, n0 .. n0 + NT) for
-// the tokens t of this workgroup's range, act [T, K], W [H, K, N], out
-// [T, H, N].  The weight tile goes to LDS once and serves every 32-token
-// tile of the range; each activation register is reloaded with the next
-// tile's value as soon as its MFMA has issued, so the next tile's loads fly
-// under the current tile's MFMAs.
-template <int K, int N, int NT>
-__global__ __attribute__((amdgpu_flat_work_group_size(NT * 2, NT * 2), amdgpu_waves_per_eu(1, 1)))
-void shared_act_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, int T, int H, int rows_per_wg) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[K * NT * 2];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * NT;
-  const int h = blockIdx.y;
-  const int t0 = blockIdx.z * rows_per_wg;
-  const int t1 = min(T, t0 + rows_per_wg);
-  if (t0 >= t1) return;
-  absorb_load_weights<K, N, NT>(w, h, n0, tile, wave, lane);
-  // lane (row r, half hl) holds act[b0 + r, 16 kb + 8 hl .. + 8]; rows past t1 read row t1 - 1
-  auto row_ptr = [&](int b0) {
-    return act + static_cast<size_t>(min(b0 + (lane & 31), t1 - 1)) * K + (lane >> 5) * 8;
-  };
-  u32x4 av[K / 16];
-  {
-    const uint16_t *ap = row_ptr(t0);
-#pragma unroll
-    for (int kb = 0; kb < K / 16; ++kb) av[kb] = *reinterpret_cast<const u32x4 *>(ap + kb * 16);
-  }
-  wait_vmcnt<0>();
-  __syncthreads();
-  // transposed B reads of the weight tile, as in absorb_mfma
-  const int g = lane >> 4, q = lane & 15;
-  const int krow = 8 * (g >> 1) + (q >> 2);
-  const int chunk = 4 * wave + 2 * (g & 1) + ((q & 3) >> 1);
-  const int boff0 = krow * (NT * 2) + ((chunk ^ wsw<NT>(krow)) << 4) + (q & 1) * 8;
-  const int boff1 = (krow + 4) * (NT * 2) + ((chunk ^ wsw<NT>(krow + 4)) << 4) + (q & 1) * 8;
-  const int r = lane & 31, hl = lane >> 5;
-  const size_t ld_out = static_cast<size_t>(H) * N;
-  for (int b0 = t0; b0 < t1; b0 += 32) {
-    const bool more = b0 + 32 < t1;
-    const uint16_t *an = row_ptr(b0 + 32);
-    f32x16 acc = {};
-#pragma unroll
-    for (int kb = 0; kb < K / 16; ++kb) {
-      const uint8_t *t0p = tile + kb * 16 * (NT * 2);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t0p + boff0));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t0p + boff1));
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[kb]), bv, acc, 0, 0, 0);
-      if (more) av[kb] = *reinterpret_cast<const u32x4 *>(an + kb * 16);
-    }
-    // row (token) b0 + (i/4)*8 + 4*hl + i%4, column n0 + 32 wave + r
-    uint16_t *op = out + static_cast<size_t>(b0) * ld_out + static_cast<size_t>(h) * N + n0 + wave * 32 + r;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = (i >> 2) * 8 + hl * 4 + (i & 3);
-      if (row < t1 - b0) op[row * ld_out] = bf16_bits(to_bf16(acc[i]));
-    }
-  }
-}
-
 // The query side of a decode step in one launch// The query side of a decode step in one launch: q[:, :, 0:512] =
 // q_nope . W_UK (the GEMM of absorb_kernel<128, 512, 128, 576>, grid
 // (4 column tiles, H heads)) and, while the weight tile is in flight, the
@@ -482,13 +420,6 @@ hipError_t launch_combine_absorb_out(const CombineOutArgs &args, hipStream_t str
   const int tiles = (a.B + 15) / 16;
   a.tile_slots = std::max(1, std::min(tiles, (256 + a.H - 1) / a.H));
   combine_absorb_out_kernel<<<dim3(a.H * a.tile_slots), 512, 0, stream>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_shared_act_gemm(const uint16_t *act, const uint16_t *w, uint16_t *out, int T, int H,
-                                  hipStream_t stream) {
-  constexpr int ROWS = 256;                    // tokens per workgroup
-  shared_act_kernel<DC, DV, 64><<<dim3(DV / 64, H, (T + ROWS - 1) / ROWS), 128, 0, stream>>>(act, w, out, T, H, ROWS);
   return hipGetLastError();
 }
 

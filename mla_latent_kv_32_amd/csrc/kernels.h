@@ -113,8 +113,5 @@ struct PrefillArgs {
   uint16_t *w_ukt;              // [H, 512, 128] = W_UK transposed per head
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
-// out[t, h, :] = act[t, :] . W[h]  (act [T, 512] shared by the heads, W [H, 512, 128], out [T, H, 128])
-hipError_t launch_shared_act_gemm(const uint16_t *act, const uint16_t *w, uint16_t *out, int T, int H,
-                                  hipStream_t stream);
 
 }  // namespace mla

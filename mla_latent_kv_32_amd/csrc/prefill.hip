@@ -13,7 +13,7 @@
 // for the decode steps that follow.  Token t of a prompt sits at position t.
 //
 // Launches: RoPE + cache rows; W_UK transposed per head; the two
-// up-projections (shared_act_kernel in absorb.hip); causal attention.
+// up-projections; causal attention.
 #include "common.h"
 #include "kernels.h"
 #include "rope.h"
@@ -22,36 +22,49 @@ namespace mla {
 namespace {
 
 // ---- RoPE of the prompt tokens and their cache rows.  Workgroup (b, y)
-// handles positions 8 y .. 8 y + 7 of prompt b: the query pairs of every
-// head (to the workspace), the shared rotary key (to the workspace, for the
-// attention) and the cache row.
+// handles positions 8 y .. 8 y + 7 of prompt b: the angles of all eight
+// tokens first (one thread per token and pair), then the query pairs of
+// every head in 16-byte pieces (to the workspace), the shared rotary key (to
+// the workspace, for the attention) and the cache rows.
 constexpr int ROPE_TOK = 8;
 
 __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
-  __shared__ float cs[DR / 2], sn[DR / 2];
+  __shared__ float cs[ROPE_TOK][DR / 2], sn[ROPE_TOK][DR / 2];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int t_begin = a.cu_seqlens[b];
   const int L = a.cu_seqlens[b + 1] - t_begin;
-  for (int j = 0; j < ROPE_TOK; ++j) {
-    const int pos = blockIdx.y * ROPE_TOK + j;
-    if (pos >= L) break;
+  const int p0 = blockIdx.y * ROPE_TOK;
+  if (p0 >= L) return;
+  const int ntok = min(ROPE_TOK, L - p0);
+  {
+    const int j = tid / (DR / 2), i = tid % (DR / 2);
+    if (j < ntok) rope_cos_sin(a.inv_freq, p0 + j, i, cs[j][i], sn[j][i]);
+  }
+  __syncthreads();
+  const int H = a.H;
+  constexpr int VEC = DR / 8;                          // 16-byte pieces of a rotary part
+  for (int idx = tid; idx < ntok * H * VEC; idx += blockDim.x) {
+    const int j = idx / (H * VEC), rem = idx % (H * VEC), h = rem / VEC, v = rem % VEC;
+    const size_t off = ((static_cast<size_t>(t_begin) + p0 + j) * H + h) * DR + 8 * v;
+    u32x4 pr = *reinterpret_cast<const u32x4 *>(a.q_pe + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = rope_rotate_pair(pr[e], cs[j][4 * v + e], sn[j][4 * v + e]);
+    *reinterpret_cast<u32x4 *>(a.q_rot + off) = pr;
+  }
+  if (tid < ntok * VEC) {
+    const int j = tid / VEC, v = tid % VEC;
+    const size_t off = (static_cast<size_t>(t_begin) + p0 + j) * DR + 8 * v;
+    u32x4 pr = *reinterpret_cast<const u32x4 *>(a.k_pe + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = rope_rotate_pair(pr[e], cs[j][4 * v + e], sn[j][4 * v + e]);
+    *reinterpret_cast<u32x4 *>(a.k_rot + off) = pr;
+  }
+  for (int j = 0; j < ntok; ++j) {
+    const int pos = p0 + j;
     const size_t t = static_cast<size_t>(t_begin) + pos;
-    __syncthreads();                       // cs / sn free again
-    if (tid < DR / 2) rope_cos_sin(a.inv_freq, pos, tid, cs[tid], sn[tid]);
-    __syncthreads();
-    for (int idx = tid; idx < a.H * (DR / 2); idx += blockDim.x) {
-      const int h = idx / (DR / 2), i = idx % (DR / 2);
-      const size_t th = t * a.H + h;
-      const uint32_t pr = *reinterpret_cast<const uint32_t *>(a.q_pe + th * DR + 2 * i);
-      *reinterpret_cast<uint32_t *>(a.q_rot + th * DR + 2 * i) = rope_rotate_pair(pr, cs[i], sn[i]);
-    }
-    if (tid < DR / 2) {
-      const uint32_t pr = *reinterpret_cast<const uint32_t *>(a.k_pe + t * DR + 2 * tid);
-      *reinterpret_cast<uint32_t *>(a.k_rot + t * DR + 2 * tid) = rope_rotate_pair(pr, cs[tid], sn[tid]);
-    }
     const int page = a.block_table[static_cast<size_t>(b) * a.max_blocks + pos / PAGE];
     store_cache_row(a.cache, a.kv_fp8, static_cast<size_t>(page) * PAGE + pos % PAGE, a.c + t * DC,
-                    a.k_pe + t * DR, tid, cs, sn);
+                    a.k_pe + t * DR, tid, cs[j], sn[j]);
   }
 }
 
@@ -65,6 +78,109 @@ __global__ __launch_bounds__(256) void transpose_wuk_kernel(const uint16_t *w, u
   for (int r = ty; r < 32; r += 8) tile[r][tx] = src[static_cast<size_t>(n0 + r) * DC + k0 + tx];
   __syncthreads();
   for (int r = ty; r < 32; r += 8) dst[static_cast<size_t>(k0 + r) * DNOPE + n0 + tx] = tile[tx][r];
+}
+
+// ---- per-head up-projection of the shared latent: out[t, h, :] =
+// c[t, :] . W[h] (K = 512, N = 128; W = W_UK^T or W_UV, both [H, 512, 128]).
+//
+// Workgroup: 128 tokens x one head; wave w owns tokens 32 w .. 32 w + 31 and
+// all four 32-column tiles.  K runs in chunks of 32 through a 3-stage LDS
+// ring fed by 16-byte global->LDS copies (two chunks in flight while one is
+// multiplied).  A chunk: 128 rows x 64 bytes, 16-byte piece c of row r at
+// position c ^ ((r >> 2) & 3), so a read of one piece of 16 consecutive rows
+// meets 16 bank quads.  B chunk: 32 rows x 256 bytes, piece c of row k at
+// c ^ 4 (k & 3), read transposed (ds_read_b64_tr_b16) as in the absorption
+// GEMMs.  The output tile goes through the ring to whole-row stores.
+constexpr int PJ_TM = 128;                      // tokens per workgroup
+constexpr int PJ_KC = 32;                       // K per chunk
+constexpr int PJ_NCH = DC / PJ_KC;              // 16 chunks
+constexpr int PJ_ABYTES = PJ_TM * PJ_KC * 2;    // 8 KB
+constexpr int PJ_BBYTES = PJ_KC * DV * 2;       // 8 KB
+constexpr int PJ_STAGE = PJ_ABYTES + PJ_BBYTES;
+constexpr int PJ_CPW = (PJ_ABYTES + PJ_BBYTES) / 1024 / 4;   // copies per wave per chunk: 4
+static_assert(PJ_TM * DV * 2 <= 3 * PJ_STAGE, "the output tile is staged in the ring");
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, int T, int H) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[3 * PJ_STAGE];
+  const int h = blockIdx.y, t0 = blockIdx.x * PJ_TM;
+  const int l = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint8_t *wh = reinterpret_cast<const uint8_t *>(w + static_cast<size_t>(h) * DC * DV);
+  const uint32_t ring_lds = lds_addr(ring);
+  // copy j (0..15) of a chunk: j < 8 -> A rows 16 j .. 16 j + 15; else B rows 4 (j - 8) .. + 3
+  auto issue = [&](int ch) {
+    const uint32_t st = ring_lds + (ch % 3) * PJ_STAGE;
+#pragma unroll
+    for (int k = 0; k < PJ_CPW; ++k) {
+      const int j = wave * PJ_CPW + k;
+      if (j < 8) {
+        const int r = 16 * j + (l >> 2), pos = l & 3;
+        const int c = pos ^ ((r >> 2) & 3);
+        const size_t t = static_cast<size_t>(min(t0 + r, T - 1));
+        dma16(reinterpret_cast<const uint8_t *>(act) + t * (DC * 2) + ch * (PJ_KC * 2) + 16 * c,
+              __builtin_amdgcn_readfirstlane(st + j * 1024));
+      } else {
+        const int kr = 4 * (j - 8) + (l >> 4), pos = l & 15;
+        const int c = pos ^ (4 * (kr & 3));
+        dma16(wh + static_cast<size_t>(ch * PJ_KC + kr) * (DV * 2) + 16 * c,
+              __builtin_amdgcn_readfirstlane(st + PJ_ABYTES + (j - 8) * 1024));
+      }
+    }
+  };
+  f32x16 acc[DV / 32];
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n) acc[n] = f32x16{};
+  // A read: row 32 wave + l % 32, piece 2 s + l / 32 (k-step s of the chunk)
+  const int ar = 32 * wave + (l & 31);
+  // B reads (transposed): lane 16 g + q reads rows 8 (g >> 1) + q / 4 (+ 4) of
+  // a k-step, columns 32 n + 16 (g & 1) + 4 (q & 3) .. + 4
+  const int g = l >> 4, q = l & 15;
+  const int krow = 8 * (g >> 1) + (q >> 2);
+  issue(0);
+  issue(1);
+  for (int ch = 0; ch < PJ_NCH; ++ch) {
+    if (ch + 1 < PJ_NCH) wait_vmcnt<PJ_CPW>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();
+    if (ch + 2 < PJ_NCH) issue(ch + 2);
+    const uint8_t *st = ring + (ch % 3) * PJ_STAGE;
+#pragma unroll
+    for (int s = 0; s < PJ_KC / 16; ++s) {
+      const int piece = 2 * s + (l >> 5);
+      const bf16x8 av = *reinterpret_cast<const bf16x8 *>(st + ar * (PJ_KC * 2) + ((piece ^ ((ar >> 2) & 3)) << 4));
+#pragma unroll
+      for (int n = 0; n < DV / 32; ++n) {
+        const int chunk = 4 * n + 2 * (g & 1) + ((q & 3) >> 1);
+        const int k0 = 16 * s + krow, k1 = k0 + 4;
+        const uint8_t *b0 = st + PJ_ABYTES + k0 * (DV * 2) + ((chunk ^ (4 * (k0 & 3))) << 4) + (q & 1) * 8;
+        const uint8_t *b1 = st + PJ_ABYTES + k1 * (DV * 2) + ((chunk ^ (4 * (k1 & 3))) << 4) + (q & 1) * 8;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)b0);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)b1);
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[n], 0, 0, 0);
+      }
+    }
+  }
+  // stage: row = token, 16-byte piece x at position x ^ (row & 15); then whole rows
+  __syncthreads();
+  const int hb = l >> 5, r = l & 31;
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 32 * wave + (i >> 2) * 8 + hb * 4 + (i & 3), col = 32 * n + r;
+      *reinterpret_cast<uint16_t *>(ring + row * (DV * 2) + (((col >> 3) ^ (row & 15)) << 4) + 2 * (col & 7)) =
+          bf16_bits(to_bf16(acc[n][i]));
+    }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PJ_TM * 16 / 256; ++k) {
+    const int p = threadIdx.x + 256 * k, row = p >> 4, x = p & 15;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(ring + row * (DV * 2) + ((x ^ (row & 15)) << 4));
+    if (t0 + row < T)
+      *reinterpret_cast<u32x4 *>(out + (static_cast<size_t>(t0 + row) * H + h) * DV + 8 * x) = v;
+  }
 }
 
 // ---- causal attention, one head and 128 query rows per workgroup.
@@ -274,8 +390,11 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   transpose_wuk_kernel<<<dim3(DC / 32, DNOPE / 32, a.H), 256, 0, stream>>>(a.w_uk, a.w_ukt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = launch_shared_act_gemm(a.c, a.w_ukt, a.k_nope, a.T, a.H, stream)) != hipSuccess) return e;
-  if ((e = launch_shared_act_gemm(a.c, a.w_uv, a.v, a.T, a.H, stream)) != hipSuccess) return e;
+  const dim3 pgrid((a.T + PJ_TM - 1) / PJ_TM, a.H);
+  prefill_proj_kernel<<<pgrid, 256, 0, stream>>>(a.c, a.w_ukt, a.k_nope, a.T, a.H);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prefill_proj_kernel<<<pgrid, 256, 0, stream>>>(a.c, a.w_uv, a.v, a.T, a.H);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   prefill_attention_kernel<<<dim3((a.max_len + FA_Q - 1) / FA_Q, a.H, a.B), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
