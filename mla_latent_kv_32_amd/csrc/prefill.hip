@@ -229,10 +229,21 @@ __device__ __forceinline__ float fa_sum_xor32(float v) {
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void prefill_attention_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * FA_BUF];
-  const int b = blockIdx.z, h = blockIdx.y;
+  // One workgroup per (prompt, head, query tile), the tiles of a (prompt,
+  // head) numbered consecutively, longest first; workgroups are dealt to the
+  // 8 XCDs round-robin by id, so id -> (XCD id % 8, position id / 8) is
+  // remapped to consecutive items per XCD: the tiles that read the same
+  // head's keys and values share one L2.
+  const int tiles = (a.max_len + FA_Q - 1) / FA_Q;
+  const int G = gridDim.x;
+  int item = blockIdx.x;
+  if ((G & 7) == 0) item = (item & 7) * (G >> 3) + (item >> 3);
+  const int tile = tiles - 1 - item % tiles;
+  const int bh = item / tiles;
+  const int b = bh / a.H, h = bh % a.H;
   const int t_begin = a.cu_seqlens[b];
   const int L = a.cu_seqlens[b + 1] - t_begin;
-  const int q0 = (gridDim.x - 1 - blockIdx.x) * FA_Q;     // longest tiles first
+  const int q0 = tile * FA_Q;
   if (q0 >= L) return;
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -395,7 +406,9 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prefill_proj_kernel<<<pgrid, 256, 0, stream>>>(a.c, a.w_uv, a.v, a.T, a.H);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  prefill_attention_kernel<<<dim3((a.max_len + FA_Q - 1) / FA_Q, a.H, a.B), 256, 0, stream>>>(a);
+  const long items = static_cast<long>((a.max_len + FA_Q - 1) / FA_Q) * a.H * a.B;
+  if (items > 2147483647L) return hipErrorInvalidValue;
+  prefill_attention_kernel<<<dim3(static_cast<unsigned>(items)), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
