@@ -197,22 +197,25 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
 //            of the score accumulator, rounded to bf16, are the B operand of
 //            key step t as they stand (keys stored in natural order, the
 //            MFMA's K-row m reading key pi(m))
-// LDS rows are padded to strides that are odd multiples of 16 bytes (400 for
-// K, 272 for V), so the score reads (row pi(l % 32), one 16-byte chunk) and
-// the transposed value reads (rows 4 apart) spread over all bank quads.
+// A block is three XOR-swizzled regions filled by 16-byte global->LDS copies
+// (20 per block, five per wave) into a ring of three buffers, two blocks in
+// flight while one is used:
+//   K latent part  32 rows x 256 B, piece c of row r at c ^ (r & 15)
+//   K rotary part  32 rows x 128 B, piece c of row r at c ^ ((r >> 1) & 7)
+//   V              32 rows x 256 B, piece c of row r at c ^ 4 ((r >> 2) & 3)
+// so the score reads (rows pi(l % 32), whose residues mod 16 differ within
+// each 16-lane group) and the transposed value reads (four rows 4 apart,
+// four pieces) meet distinct bank quads.
 constexpr int FA_Q = 128;                       // query rows per workgroup
 constexpr int FA_KB = 32;                       // keys per block
 constexpr int FA_KS = (DNOPE + DR) / 16;        // 12 score k-steps
-constexpr int FA_KLROW = (DNOPE + DR) * 2 + 16; // 400
-constexpr int FA_VLROW = DV * 2 + 16;           // 272
-constexpr int FA_KBUF = FA_KB * FA_KLROW;       // 12800
-constexpr int FA_BUF = FA_KBUF + FA_KB * FA_VLROW;   // 21504
-constexpr int FA_KCH = FA_KB * (DNOPE + DR) / 8;     // 768 16-byte chunks of a K block
-constexpr int FA_VCH = FA_KB * DV / 8;               // 512 of a V block
-constexpr int FA_LD = (FA_KCH + FA_VCH) / 256;       // 5 chunk loads per thread per block
-constexpr float FA_SLACK = 16.0f;                    // lazy rescale margin (log2 units)
-static_assert((FA_KCH + FA_VCH) % 256 == 0, "block chunks split evenly over 256 threads");
-static_assert(FA_Q * DV * 2 <= 2 * FA_BUF, "the output tile is staged in the block buffers");
+constexpr int FA_KN = FA_KB * DNOPE * 2;        // 8 KB: latent part of K
+constexpr int FA_KR = FA_KB * DR * 2;           // 4 KB: rotary part of K
+constexpr int FA_VB = FA_KB * DV * 2;           // 8 KB: V
+constexpr int FA_BUF = FA_KN + FA_KR + FA_VB;   // 20 KB per block
+constexpr int FA_CPW = FA_BUF / 1024 / 4;       // 5 copies per wave per block
+constexpr float FA_SLACK = 16.0f;               // lazy rescale margin (log2 units)
+static_assert(FA_Q * DV * 2 <= 3 * FA_BUF, "the output tile is staged in the block ring");
 
 __device__ __forceinline__ int fa_pi(int m) {
   return 16 * ((m >> 2) & 1) + 4 * (m & 3) + 2 * ((m >> 4) & 1) + ((m >> 3) & 1);
@@ -228,7 +231,7 @@ __device__ __forceinline__ float fa_sum_xor32(float v) {
 
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void prefill_attention_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * FA_BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * FA_BUF];
   // One workgroup per (prompt, head, query tile), the tiles of a (prompt,
   // head) numbered consecutively, longest first; workgroups are dealt to the
   // 8 XCDs round-robin by id, so id -> (XCD id % 8, position id / 8) is
@@ -252,6 +255,37 @@ void prefill_attention_kernel(PrefillArgs a) {
   const int H = a.H;
   const int nkb = (min(L, q0 + FA_Q) + FA_KB - 1) / FA_KB;
 
+  // block copies (20 per block, 1 KB each): wave w issues K latent copies
+  // 2 w, 2 w + 1 (rows 4 j + l / 16, piece l % 16), K rotary copy w (rows
+  // 8 w + l / 8, piece l % 8) and V copies 2 w, 2 w + 1 (rows 4 j + l / 16);
+  // rows past the prompt re-read its last row (their scores are masked).
+  const uint32_t lds0 = lds_addr(lds);
+  const uint8_t *kn_src = reinterpret_cast<const uint8_t *>(a.k_nope) + static_cast<size_t>(h) * (DNOPE * 2);
+  const uint8_t *kr_src = reinterpret_cast<const uint8_t *>(a.k_rot);
+  const uint8_t *v_src = reinterpret_cast<const uint8_t *>(a.v) + static_cast<size_t>(h) * (DV * 2);
+  const size_t row_hd = static_cast<size_t>(H) * (DNOPE * 2);    // bytes between tokens, per-head arrays
+  auto issue = [&](int kb) {
+    const uint32_t base = lds0 + (kb % 3) * FA_BUF;
+    const int tok0 = t_begin + kb * FA_KB, last = t_begin + L - 1;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = 2 * wave + k, r = 4 * j + (l >> 4), c = (l & 15) ^ (r & 15);
+      const size_t t = static_cast<size_t>(min(tok0 + r, last));
+      dma16(kn_src + t * row_hd + 16 * c, __builtin_amdgcn_readfirstlane(base + j * 1024));
+    }
+    {
+      const int r = 8 * wave + (l >> 3), c = (l & 7) ^ ((r >> 1) & 7);
+      const size_t t = static_cast<size_t>(min(tok0 + r, last));
+      dma16(kr_src + t * (DR * 2) + 16 * c, __builtin_amdgcn_readfirstlane(base + FA_KN + wave * 1024));
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = 2 * wave + k, r = 4 * j + (l >> 4), c = (l & 15) ^ (4 * ((r >> 2) & 3));
+      const size_t t = static_cast<size_t>(min(tok0 + r, last));
+      dma16(v_src + t * row_hd + 16 * c, __builtin_amdgcn_readfirstlane(base + FA_KN + FA_KR + j * 1024));
+    }
+  };
+
   // query fragments: lane (q row, hb) holds dims 16 ks + 8 hb .. + 8
   bf16x8 qf[FA_KS];
   {
@@ -262,45 +296,26 @@ void prefill_attention_kernel(PrefillArgs a) {
                                             : a.q_rot + th * DR + 16 * (ks - DNOPE / 16) + 8 * hb;
       qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src));
     }
+    // Wait for the query here, before any block copy is issued: the
+    // compiler does not see the copies (inline asm) and would otherwise
+    // place its waits for the query inside the loop, where they also wait
+    // for the copies of the blocks ahead.
+#pragma unroll
+    for (int ks = 0; ks < FA_KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
-  // block loads: thread chunk idx = tid + 256 j; K chunks first, then V
-  u32x4 stg[FA_LD];
-  auto load_block = [&](int kb) {
-#pragma unroll
-    for (int j = 0; j < FA_LD; ++j) {
-      const int idx = tid + 256 * j;
-      if (idx < FA_KCH) {
-        const int n = idx / 24, c = idx % 24;
-        const size_t t = static_cast<size_t>(t_begin) + min(kb * FA_KB + n, L - 1);
-        const uint16_t *src = c < 16 ? a.k_nope + (t * H + h) * DNOPE + 8 * c : a.k_rot + t * DR + 8 * (c - 16);
-        stg[j] = *reinterpret_cast<const u32x4 *>(src);
-      } else {
-        const int v = idx - FA_KCH, n = v / 16, c = v % 16;
-        const size_t t = static_cast<size_t>(t_begin) + min(kb * FA_KB + n, L - 1);
-        stg[j] = *reinterpret_cast<const u32x4 *>(a.v + (t * H + h) * DV + 8 * c);
-      }
-    }
-  };
-  auto store_block = [&](uint8_t *buf) {
-#pragma unroll
-    for (int j = 0; j < FA_LD; ++j) {
-      const int idx = tid + 256 * j;
-      if (idx < FA_KCH) {
-        const int n = idx / 24, c = idx % 24;
-        *reinterpret_cast<u32x4 *>(buf + n * FA_KLROW + 16 * c) = stg[j];
-      } else {
-        const int v = idx - FA_KCH, n = v / 16, c = v % 16;
-        *reinterpret_cast<u32x4 *>(buf + FA_KBUF + n * FA_VLROW + 16 * c) = stg[j];
-      }
-    }
-  };
-
-  // per-lane read bases
-  const int kbase = fa_pi(l & 31) * FA_KLROW + 16 * hb;     // + 32 ks
-  const int vrow = 16 * hb + 4 * ((l & 15) >> 2);
+  // per-lane read offsets within a block buffer
+  const int m = fa_pi(l & 31);
+  // K latent piece 2 ks + hb of row m at ((2 ks + hb) ^ (m & 15)): base ^ 32 ks
+  const int kn_off = m * (DNOPE * 2) + 16 * ((m & 14) | (hb ^ (m & 1)));
+  // K rotary piece 2 (ks - 8) + hb of row m at (... ^ ((m >> 1) & 7)): base ^ 32 (ks - 8)
+  const int fr = (m >> 1) & 7;
+  const int kr_off = FA_KN + m * (DR * 2) + 16 * ((fr & 6) | (hb ^ (fr & 1)));
+  // V (transposed reads): lane supplies row 16 hb + 4 d + 2 t (+ 1 for hi),
+  // piece 4 j + csub at (4 (j ^ d) + csub), byte 8 (l & 1)
+  const int d = (l & 15) >> 2;
   const int csub = 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
-  const int vbase = FA_KBUF + vrow * FA_VLROW + 16 * csub + 8 * (l & 1);   // + 2 t FA_VLROW + 64 j (+ FA_VLROW: hi)
+  const int v_off = FA_KN + FA_KR + (16 * hb + 4 * d) * (DV * 2) + 16 * csub + 8 * (l & 1);
 
   f32x16 o[DV / 32];
 #pragma unroll
@@ -308,17 +323,20 @@ void prefill_attention_kernel(PrefillArgs a) {
   float m_run = -FLT_MAX, l_run = 0.f;
   const float c = a.scale_log2;
 
-  load_block(0);
-  store_block(lds);
-  __syncthreads();
+  issue(0);
+  if (nkb > 1) issue(1);
   for (int kb = 0; kb < nkb; ++kb) {
-    uint8_t *buf = lds + (kb & 1) * FA_BUF;
-    if (kb + 1 < nkb) load_block(kb + 1);
+    if (kb + 1 < nkb) wait_vmcnt<FA_CPW>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();        // block kb visible; every wave is done with block kb - 1
+    if (kb + 2 < nkb) issue(kb + 2);
+    const uint8_t *buf = lds + (kb % 3) * FA_BUF;
     // scores
     f32x16 s = {};
 #pragma unroll
     for (int ks = 0; ks < FA_KS; ++ks) {
-      const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(buf + kbase + 32 * ks);
+      const int off = ks < DNOPE / 16 ? (kn_off ^ (32 * ks)) : (kr_off ^ (32 * (ks - DNOPE / 16)));
+      const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(buf + off);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qf[ks], s, 0, 0, 0);
     }
     // causal mask: key kb * 32 + tok(i) is visible to query qi while <= qi
@@ -355,21 +373,20 @@ void prefill_attention_kernel(PrefillArgs a) {
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int j = 0; j < DV / 32; ++j) {
-        const uint8_t *r0 = buf + vbase + 2 * t * FA_VLROW + 64 * j;
+        const uint8_t *r0 = buf + v_off + 2 * t * (DV * 2) + 64 * (j ^ d);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)r0);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(r0 + FA_VLROW));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(r0 + DV * 2));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[t], o[j], 0, 0, 0);
       }
     }
-    if (kb + 1 < nkb) store_block(lds + ((kb + 1) & 1) * FA_BUF);
-    __syncthreads();
   }
 
-  // normalise; stage rows (query row = 32 wave + l % 32, 16-byte chunk x at
+  // normalise; stage rows (query row = 32 wave + l % 32, 16-byte piece x at
   // position x ^ (row & 15)) and store whole 256-byte rows
   const float inv = 1.0f / fa_sum_xor32(l_run);
   const int row = wave * 32 + (l & 31);
+  barrier_no_fence();          // every wave is done with the ring
 #pragma unroll
   for (int j = 0; j < DV / 32; ++j) {
 #pragma unroll
@@ -377,7 +394,7 @@ void prefill_attention_kernel(PrefillArgs a) {
       bf16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[j][4 * q + e] * inv);
-      // columns 32 j + 8 q + 4 hb .. + 4: half of 16-byte chunk 4 j + q
+      // columns 32 j + 8 q + 4 hb .. + 4: half of 16-byte piece 4 j + q
       const int x = 4 * j + q;
       *reinterpret_cast<bf16x4 *>(lds + row * (DV * 2) + ((x ^ (row & 15)) << 4) + 8 * hb) = v;
     }
