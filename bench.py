@@ -51,10 +51,10 @@ COPIES = 3
 # reported only while that source is unchanged.
 DECODE_TRAFFIC = {
     "sources_sha256": {
-        "mla_latent_kv_32_amd/csrc/decode.hip": "8ceb1adcf7b1c381908b91df38b88c93a0679a126c5f8dde5f903a183c9c8851",
-        "mla_latent_kv_32_amd/csrc/common.h": "9119e84c6a1340e11077a316e161bf93b3bc7e62a88e7300f6ef510da895fad9",
+        "mla_latent_kv_32_amd/csrc/decode.hip": "4f699be56c26f0ac28cb797512bacd9060ecaaf78d90fbae6098b100f7a2e8bd",
+        "mla_latent_kv_32_amd/csrc/common.h": "748cb997b4658e63c1b64bf8032fbb164e6e9bedcf880b094934b6a8c62b4bea",
     },
-    "fetch_kib": 76228.3,
+    "fetch_kib": 76232.3,
     "write_kib": 32896.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
