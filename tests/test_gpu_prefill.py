@@ -95,3 +95,36 @@ def test_prefill_long_prompts_full_heads():
     o, pool = run_prefill(w)
     assert not torch.isnan(o.float()).any().item()
     check_prefill(w, o, pool, [(0, [0, 77]), (3, [127])])
+
+
+@pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8])
+def test_decode_after_prefill(kv_dtype):
+    """The rows a prefill leaves are the cache the decode reads: a decode
+    query against each prompt's prefilled rows matches the oracle's decode
+    over the oracle's rows for that prompt."""
+    lens = [1, 40, 129, 300]
+    H = 16
+    w = synth.prefill_workload(730 + kv_dtype, H, lens, kv_dtype)
+    o, pool = run_prefill(w)
+    fp8 = kv_dtype == synth.KV_FP8
+    q = synth.multi_token_query(731, len(lens), 1, H)[:, 0]
+    sl = np.asarray(lens, np.int32)
+    pool_dev = to_dev(pool) if fp8 else to_dev_bf16(pool)
+    od = torch.full((len(lens), H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((len(lens), H), float("nan"), dtype=torch.float32, device="cuda")
+    mla.mla_decode_paged(to_dev_bf16(q), pool_dev, kv_dtype, to_dev(w["block_table"]), to_dev(sl), max(lens),
+                         w["scale"], od, lse, split_tokens=64)
+    torch.cuda.synchronize()
+    tol = (2e-3, 6e-2) if fp8 else (2e-3, 2e-2)
+    for b, L in enumerate(lens):
+        _, rows = oracle.reference_prefill(w, b, [0])
+        if fp8:   # the cache holds the latent quantised to E4M3 per 128-wide group
+            c = np.stack([(oracle.e4m3_to_f64(cd).reshape(4, 128) * sc.astype(np.float64)[:, None]).reshape(512)
+                          for cd, sc in (oracle.fp8_quantize_latent(w["c"][int(w["cu_seqlens"][b]) + t])
+                                         for t in range(L))])
+        else:
+            c = rows[:, :512]
+        qb = oracle.bf16_to_f64(q[b])
+        ref, ref_l, mag = oracle.decode_absorbed(qb[:, :512], qb[:, 512:], c, rows[:, 512:], w["scale"],
+                                                 with_magnitude=True)
+        assert_close(bf16_tensor_to_f64(od[b]), ref, *tol, extra=P_ROUNDING * mag, what=f"decode after prefill b={b}")
