@@ -151,14 +151,53 @@ __global__ __launch_bounds__(NT * 2) void absorb_kernel(const uint16_t *act, con
   absorb_load_weights<K, N, NT>(w, h, n0, tile, wave, lane);
   wait_vmcnt<0>();
   __syncthreads();
-  for (int b0 = 0; b0 < B; b0 += 32) {
-    u32x4 av[K / 16];
-    absorb_load_act<K>(act, B, H, h, b0, lane, av);
-    absorb_tile<K, N, NT, OUT_ROW>(av, tile, out, B, H, h, n0, b0, wave, lane);
+  if constexpr (K <= 128) {
+    for (int b0 = 0; b0 < B; b0 += 32) {
+      u32x4 av[K / 16];
+      absorb_load_act<K>(act, B, H, h, b0, lane, av);
+      absorb_tile<K, N, NT, OUT_ROW>(av, tile, out, B, H, h, n0, b0, wave, lane);
+    }
+  } else {
+    // long K: the activations stream through a ring of 8 k-steps instead of
+    // being held whole (K / 16 x 4 registers would not fit beside the rest)
+    constexpr int RA = 8;
+    const int g = lane >> 4, q = lane & 15;
+    const int krow = 8 * (g >> 1) + (q >> 2);
+    const int chunk = 4 * wave + 2 * (g & 1) + ((q & 3) >> 1);
+    const int boff0 = krow * (NT * 2) + ((chunk ^ wsw<NT>(krow)) << 4) + (q & 1) * 8;
+    const int boff1 = (krow + 4) * (NT * 2) + ((chunk ^ wsw<NT>(krow + 4)) << 4) + (q & 1) * 8;
+    const int r = lane & 31, hl = lane >> 5;
+    for (int b0 = 0; b0 < B; b0 += 32) {
+      const bool aval = r < B - b0;
+      const uint16_t *ap = act + (static_cast<size_t>(b0 + (aval ? r : 0)) * H + h) * K + hl * 8;
+      u32x4 ring[RA];
+#pragma unroll
+      for (int kb = 0; kb < RA; ++kb) ring[kb] = *reinterpret_cast<const u32x4 *>(ap + kb * 16);
+      f32x16 acc = {};
+#pragma unroll
+      for (int kb = 0; kb < K / 16; ++kb) {
+        u32x4 av = ring[kb % RA];
+        if (kb + RA < K / 16) ring[kb % RA] = *reinterpret_cast<const u32x4 *>(ap + (kb + RA) * 16);
+        if (!aval) av = u32x4{0, 0, 0, 0};
+        const uint8_t *t0 = tile + kb * 16 * (NT * 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t0 + boff0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t0 + boff1));
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bv, acc, 0, 0, 0);
+      }
+      const int rows = B - b0;
+      const size_t ld_out = static_cast<size_t>(H) * OUT_ROW;
+      uint16_t *op = out + static_cast<size_t>(b0) * ld_out + static_cast<size_t>(h) * OUT_ROW + n0 + wave * 32 + r;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = (i >> 2) * 8 + hl * 4 + (i & 3);
+        if (row < rows) op[row * ld_out] = bf16_bits(to_bf16(acc[i]));
+      }
+    }
   }
 }
 
-// The query side of a decode step in one launch// The query side of a decode step in one launch: q[:, :, 0:512] =
+// The query side of a decode step in one launch: q[:, :, 0:512] =
 // q_nope . W_UK (the GEMM of absorb_kernel<128, 512, 128, 576>, grid
 // (4 column tiles, H heads)) and, while the weight tile is in flight, the
 // work of rope_append_kernel: workgroup (x, h) turns the query pairs of head
