@@ -107,6 +107,35 @@ def decode_traffic_bytes():
     return round((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def stream_copy_gbs(torch, nbytes=512 << 20, reps=10):
+    """Second denominator: a plain device copy (read + write) of nbytes, best of reps, in GB/s."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        best = t if best is None else min(best, t)
+    del src, dst
+    return round(2 * nbytes / best / 1e9, 1)
+
+
 def cpu_baseline(w, budget_s):
     """Time the oracle (explicit per-head K/V reconstruction, fp64) on whole sequences."""
     import oracle
@@ -130,6 +159,7 @@ def cpu_baseline(w, budget_s):
         "value": round(w["B"] * S * ROW_BYTES / step_s / 1e9, 4),
         "unit": "GB/s",
         "cores": int(cores),
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": f"{done} of {w['B']} sequences, all {w['H']} heads, full decode step in fp64 "
                   f"(explicit K/V per head), {dt:.1f} s; scaled to the whole batch "
@@ -467,6 +497,7 @@ def main():
         "step_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "decode_kernel": {
             "avg_us": round(avg_us["decode"], 3),
+            "p10_p50_p90_us": [round(float(np.percentile(per["decode"], q)), 3) for q in (10, 50, 90)],
             "latent_gbs": round(achieved, 1),
             "tflops": round(flops / dec_s / 1e12, 1),
             "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -486,6 +517,9 @@ def main():
             "traffic": decode_traffic_bytes(),
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes": cache_bytes,
+            "stream_copy_gbs": stream_copy_gbs(torch),
+            "stream_copy_note": "second denominator: a 512 MiB device copy on this GPU, read + write bytes "
+                                "over its best time of 10; the frac stays against the 8 TB/s peak",
         },
         "parity": parity,
     }
