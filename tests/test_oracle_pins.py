@@ -551,3 +551,32 @@ def test_prefill_explicit_equals_mha_form_workload0():
                                        w["scale"], w["theta"])
     np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(rows[:, w["d_c"]:], kr, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------ merged vs sequential absorption (study)
+def test_merged_and_sequential_query_absorption_precision():
+    """[Su] MLA additional notes 1-2 weigh merging W_UQ W_UK^T into one matrix
+    against applying the two projections in turn.  With bf16 operands and
+    exactly accumulated products (what the MFMA path does), both land within
+    the final bf16 rounding of q_lat of the exact product, and within a few
+    percent of each other; the merged matrix costs d_q/d_n = 12x the weight
+    bytes per head of W_UK (1536 x 512 vs 128 x 512) and 3x the FLOPs of the
+    sequential pair, so the path keeps the sequential form."""
+    rng = np.random.default_rng(11)
+    B, dq, dn, dc, H = 64, 1536, 128, 512, 4
+
+    def bf(x):
+        return oracle.bf16_to_f64(synth.f32_to_bf16_bits(np.asarray(x, np.float64)))
+    x = bf(rng.standard_normal((B, dq)))
+    wuq = bf(rng.standard_normal((H, dq, dn)) / math.sqrt(dq))
+    wuk = bf(rng.standard_normal((H, dn, dc)) / math.sqrt(dc))
+    for h in range(H):
+        exact = x @ wuq[h] @ wuk[h]
+        seq = bf(bf(x @ wuq[h]) @ wuk[h])
+        merged = bf(x @ bf(wuq[h] @ wuk[h]))
+        e_seq = np.sqrt(((seq - exact) ** 2).sum() / (exact ** 2).sum())
+        e_mer = np.sqrt(((merged - exact) ** 2).sum() / (exact ** 2).sum())
+        assert e_seq < 2.0 ** -8 and e_mer < 2.0 ** -8
+        assert abs(e_seq - e_mer) < 0.1 * max(e_seq, e_mer)
+    # cost per token and head (multiply-adds): sequential d_q d_n + d_n d_c, merged d_q d_c
+    assert (dq * dc) / (dq * dn + dn * dc) == 3.0
