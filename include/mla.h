@@ -125,8 +125,8 @@ int mla_rope_append_cache(const void *q_pe, const void *kv_new, const int32_t *s
  * q[:, :, d_c:d_c+d_r] = RoPE(q_pe, p_b) and the cache row of every sequence
  * appended, with exactly the arithmetic of the two calls (results are
  * bit-identical to them).  Arguments, layouts, requirements and errors are
- * those of the two calls.  Reads of q_pe / kv_new and writes of q / kv_cache
- * must not overlap.
+ * those of the two calls, except that H <= 65527 here (MLA_ERR_UNSUPPORTED
+ * above).  Reads of q_pe / kv_new and writes of q / kv_cache must not overlap.
  */
 int mla_absorb_q_rope_append(const void *q_nope, const void *w_uk, const void *q_pe, const void *kv_new,
                              const int32_t *seq_lens, const int32_t *block_table, int max_blocks_per_seq,

@@ -198,12 +198,17 @@ __global__ __launch_bounds__(NT * 2) void absorb_kernel(const uint16_t *act, con
 }
 
 // The query side of a decode step in one launch: q[:, :, 0:512] =
-// q_nope . W_UK (the GEMM of absorb_kernel<128, 512, 128, 576>, grid
-// (4 column tiles, H heads)) and, while the weight tile is in flight, the
-// work of rope_append_kernel: workgroup (x, h) turns the query pairs of head
-// h for the sequences b = x (mod 4), and workgroup h * 4 + x appends the rows
-// of sequences b = h * 4 + x (mod 4 H).  The arithmetic is that of the two
-// separate launches, so the results are bit-identical to them.
+// q_nope . W_UK (the GEMM of absorb_kernel<128, 512, 128, 576>, grid rows
+// 0..H-1: 4 column tiles per head) with the work of rope_append_kernel.
+// Workgroup (x, h < H) turns the query pairs of head h for the sequences
+// b = x (mod 4) while its weight tile is in flight: the first pair's operands
+// (q_pe pair, length, frequency) are requested before the activations and the
+// weight copies, and the vector-memory counter completes in order, so the
+// angle and the rotation wait for those few loads only, not for the copies.
+// The cache rows are appended by extra grid rows h >= H that copy no weights
+// (workgroup (x, H + y) takes the sequences b = 4 y + x modulo their count).
+// The arithmetic is that of the two separate launches, so the results are
+// bit-identical to them.
 __global__ __launch_bounds__(256) void query_kernel(const uint16_t *q_nope, const uint16_t *w_uk, RopeAppendArgs ra) {
   constexpr int K = DNOPE, N = DC, NT = 128;
   __shared__ __attribute__((aligned(16))) uint8_t tile[K * NT * 2];
@@ -214,28 +219,46 @@ __global__ __launch_bounds__(256) void query_kernel(const uint16_t *q_nope, cons
   const int n0 = blockIdx.x * NT;
   const int h = blockIdx.y;
   const int B = ra.B, H = ra.H;
-  absorb_load_weights<K, N, NT>(w_uk, h, n0, tile, wave, lane);
-  u32x4 av[K / 16];
-  absorb_load_act<K>(q_nope, B, H, h, 0, lane, av);
+
+  if (h >= H) {
+    // cache rows
+    const int stride = gridDim.x * (gridDim.y - H);
+    for (int b = (h - H) * gridDim.x + blockIdx.x; b < B; b += stride) {
+      const int S = ra.seq_lens[b];
+      if (S <= 0) continue;
+      __syncthreads();   // cs / sn free again
+      if (tid < DR / 2) rope_cos_sin(ra, rope_position(S), tid, cs[tid], sn[tid]);
+      __syncthreads();
+      append_row(ra, b, S, tid, cs, sn);
+    }
+    return;
+  }
 
   // query rotary pairs: thread (j = tid / 32, pair i = tid % 32), sequences
-  // b = x + 4 j + 32 m
-  // (the q_pe pair is requested with the length, before the angle is formed)
-  for (int b = blockIdx.x + 4 * (tid >> 5); b < B; b += 4 * (256 / 32)) {
-    const uint32_t pr = rope_query_load(ra, b, h, tid & 31);
-    float c, s;
-    rope_cos_sin(ra, rope_position(ra.seq_lens[b]), tid & 31, c, s);
-    rope_query_store(ra, b, h, tid & 31, pr, c, s);
+  // b = x + 4 j + 32 m; the operands of m = 0 go out first
+  const int i = tid & 31, bq = blockIdx.x + 4 * (tid >> 5);
+  const double w = ra.inv_freq[i];
+  uint32_t pr0 = 0;
+  int s0 = 0;
+  if (bq < B) {
+    pr0 = rope_query_load(ra, bq, h, i);
+    s0 = ra.seq_lens[bq];
   }
-  // cache rows
-  const int nwg = gridDim.x * gridDim.y;
-  for (int b = h * gridDim.x + blockIdx.x; b < B; b += nwg) {
-    const int S = ra.seq_lens[b];
-    if (S <= 0) continue;
-    __syncthreads();   // cs / sn free again
-    if (tid < DR / 2) rope_cos_sin(ra, rope_position(S), tid, cs[tid], sn[tid]);
-    __syncthreads();
-    append_row(ra, b, S, tid, cs, sn);
+  u32x4 av[K / 16];
+  absorb_load_act<K>(q_nope, B, H, h, 0, lane, av);
+  absorb_load_weights<K, N, NT>(w_uk, h, n0, tile, wave, lane);
+  // keeps the position arithmetic (and with it the wait for the length)
+  // behind the copies
+  asm volatile("" : "+v"(s0));
+  if (bq < B) {
+    float c, s;
+    rope_cos_sin_at(w, rope_position(s0), c, s);
+    rope_query_store(ra, bq, h, i, pr0, c, s);
+    for (int b = bq + 32; b < B; b += 32) {
+      const uint32_t pr = rope_query_load(ra, b, h, i);
+      rope_cos_sin_at(w, rope_position(ra.seq_lens[b]), c, s);
+      rope_query_store(ra, b, h, i, pr, c, s);
+    }
   }
 
   wait_vmcnt<0>();
@@ -469,7 +492,9 @@ hipError_t launch_absorb_q(const uint16_t *q_nope, const uint16_t *w_uk, uint16_
 }
 
 hipError_t launch_query(const uint16_t *q_nope, const uint16_t *w_uk, const RopeAppendArgs &ra, hipStream_t stream) {
-  query_kernel<<<dim3(DC / 128, ra.H), 256, 0, stream>>>(q_nope, w_uk, ra);
+  // H rows of 4 GEMM workgroups, then 1..8 rows of 4 append workgroups
+  const int append_rows = std::max(1, std::min(8, (ra.B + 3) / 4));
+  query_kernel<<<dim3(DC / 128, ra.H + append_rows), 256, 0, stream>>>(q_nope, w_uk, ra);
   return hipGetLastError();
 }
 

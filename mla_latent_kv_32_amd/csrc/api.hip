@@ -129,7 +129,7 @@ int mla_absorb_q_rope_append(const void *q_nope, const void *w_uk, const void *q
   const int st = rope_args(q_pe, kv_new, seq_lens, block_table, max_blocks_per_seq, kv_cache, kv_dtype, num_blocks,
                            block_size, rope_theta, q, B, H, d_c, d_r, &a);
   if (st != MLA_OK) return st;
-  if (B > 65535 * 32 || H > 65535) return MLA_ERR_UNSUPPORTED;
+  if (B > 65535 * 32 || H > 65535 - 8) return MLA_ERR_UNSUPPORTED;   // grid rows: H + up to 8 append rows
   if (d_nope != MLA_D_NOPE) return MLA_ERR_UNSUPPORTED;
   return status_of(mla::launch_query(static_cast<const uint16_t *>(q_nope), static_cast<const uint16_t *>(w_uk), a,
                                      static_cast<hipStream_t>(stream)));

@@ -46,12 +46,16 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float x) {
 // empty slot rotates at position 0 and appends nothing.
 __device__ __forceinline__ int rope_position(int S) { return S > 0 ? S - 1 : 0; }
 
-// cos and sin of pos * inv_freq[i] (angle formed and reduced in float64).
-__device__ __forceinline__ void rope_cos_sin(const double *inv_freq, int pos, int i, float &c, float &s) {
+// cos and sin of pos * w for the frequency w of one pair (angle formed and
+// reduced in float64).
+__device__ __forceinline__ void rope_cos_sin_at(double w, int pos, float &c, float &s) {
   double sv, cv;
-  sincos(static_cast<double>(pos) * inv_freq[i], &sv, &cv);
+  sincos(static_cast<double>(pos) * w, &sv, &cv);
   c = static_cast<float>(cv);
   s = static_cast<float>(sv);
+}
+__device__ __forceinline__ void rope_cos_sin(const double *inv_freq, int pos, int i, float &c, float &s) {
+  rope_cos_sin_at(inv_freq[i], pos, c, s);
 }
 __device__ __forceinline__ void rope_cos_sin(const RopeAppendArgs &a, int pos, int i, float &c, float &s) {
   rope_cos_sin(a.inv_freq, pos, i, c, s);
