@@ -83,21 +83,25 @@ __global__ __launch_bounds__(256) void transpose_wuk_kernel(const uint16_t *w, u
 // ---- per-head up-projection of the shared latent: out[t, h, :] =
 // c[t, :] . W[h] (K = 512, N = 128; W = W_UK^T or W_UV, both [H, 512, 128]).
 //
-// Workgroup: 128 tokens x one head; wave w owns tokens 32 w .. 32 w + 31 and
-// all four 32-column tiles.  K runs in chunks of 32 through a 3-stage LDS
+// Workgroup: 256 tokens x one head; wave w owns tokens 64 w .. 64 w + 63 (two
+// 32-row tiles) and all four 32-column tiles, so every weight fragment read
+// from LDS feeds two MFMAs.  K runs in chunks of 32 through a 3-stage LDS
 // ring fed by 16-byte global->LDS copies (two chunks in flight while one is
-// multiplied).  A chunk: 128 rows x 64 bytes, 16-byte piece c of row r at
+// multiplied).  A chunk: 256 rows x 64 bytes, 16-byte piece c of row r at
 // position c ^ ((r >> 2) & 3), so a read of one piece of 16 consecutive rows
 // meets 16 bank quads.  B chunk: 32 rows x 256 bytes, piece c of row k at
 // c ^ 4 (k & 3), read transposed (ds_read_b64_tr_b16) as in the absorption
 // GEMMs.  The output tile goes through the ring to whole-row stores.
-constexpr int PJ_TM = 128;                      // tokens per workgroup
+constexpr int PJ_TM = 256;                      // tokens per workgroup
+constexpr int PJ_MT = PJ_TM / 4 / 32;           // 32-row tiles per wave: 2
 constexpr int PJ_KC = 32;                       // K per chunk
 constexpr int PJ_NCH = DC / PJ_KC;              // 16 chunks
-constexpr int PJ_ABYTES = PJ_TM * PJ_KC * 2;    // 8 KB
+constexpr int PJ_ABYTES = PJ_TM * PJ_KC * 2;    // 16 KB
 constexpr int PJ_BBYTES = PJ_KC * DV * 2;       // 8 KB
 constexpr int PJ_STAGE = PJ_ABYTES + PJ_BBYTES;
-constexpr int PJ_CPW = (PJ_ABYTES + PJ_BBYTES) / 1024 / 4;   // copies per wave per chunk: 4
+constexpr int PJ_ACOPIES = PJ_ABYTES / 1024;    // 16 one-KB copies of A per chunk
+constexpr int PJ_CPW = PJ_STAGE / 1024 / 4;     // copies per wave per chunk: 6
+static_assert(PJ_STAGE % 4096 == 0, "a chunk splits evenly over the four waves");
 static_assert(PJ_TM * DV * 2 <= 3 * PJ_STAGE, "the output tile is staged in the ring");
 
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
@@ -108,31 +112,34 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint8_t *wh = reinterpret_cast<const uint8_t *>(w + static_cast<size_t>(h) * DC * DV);
   const uint32_t ring_lds = lds_addr(ring);
-  // copy j (0..15) of a chunk: j < 8 -> A rows 16 j .. 16 j + 15; else B rows 4 (j - 8) .. + 3
+  // copy j (0..23) of a chunk: j < 16 -> A rows 16 j .. 16 j + 15; else B
+  // rows 4 (j - 16) .. + 3 (wave-uniform: j = 6 wave + k)
   auto issue = [&](int ch) {
     const uint32_t st = ring_lds + (ch % 3) * PJ_STAGE;
 #pragma unroll
     for (int k = 0; k < PJ_CPW; ++k) {
       const int j = wave * PJ_CPW + k;
-      if (j < 8) {
+      if (j < PJ_ACOPIES) {
         const int r = 16 * j + (l >> 2), pos = l & 3;
         const int c = pos ^ ((r >> 2) & 3);
         const size_t t = static_cast<size_t>(min(t0 + r, T - 1));
         dma16(reinterpret_cast<const uint8_t *>(act) + t * (DC * 2) + ch * (PJ_KC * 2) + 16 * c,
               __builtin_amdgcn_readfirstlane(st + j * 1024));
       } else {
-        const int kr = 4 * (j - 8) + (l >> 4), pos = l & 15;
+        const int kr = 4 * (j - PJ_ACOPIES) + (l >> 4), pos = l & 15;
         const int c = pos ^ (4 * (kr & 3));
         dma16(wh + static_cast<size_t>(ch * PJ_KC + kr) * (DV * 2) + 16 * c,
-              __builtin_amdgcn_readfirstlane(st + PJ_ABYTES + (j - 8) * 1024));
+              __builtin_amdgcn_readfirstlane(st + PJ_ABYTES + (j - PJ_ACOPIES) * 1024));
       }
     }
   };
-  f32x16 acc[DV / 32];
+  f32x16 acc[PJ_MT][DV / 32];
 #pragma unroll
-  for (int n = 0; n < DV / 32; ++n) acc[n] = f32x16{};
-  // A read: row 32 wave + l % 32, piece 2 s + l / 32 (k-step s of the chunk)
-  const int ar = 32 * wave + (l & 31);
+  for (int m = 0; m < PJ_MT; ++m)
+#pragma unroll
+    for (int n = 0; n < DV / 32; ++n) acc[m][n] = f32x16{};
+  // A read of tile m: row 64 wave + 32 m + l % 32, piece 2 s + l / 32 (k-step s of the chunk)
+  const int ar0 = 32 * PJ_MT * wave + (l & 31);
   // B reads (transposed): lane 16 g + q reads rows 8 (g >> 1) + q / 4 (+ 4) of
   // a k-step, columns 32 n + 16 (g & 1) + 4 (q & 3) .. + 4
   const int g = l >> 4, q = l & 15;
@@ -148,7 +155,12 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
 #pragma unroll
     for (int s = 0; s < PJ_KC / 16; ++s) {
       const int piece = 2 * s + (l >> 5);
-      const bf16x8 av = *reinterpret_cast<const bf16x8 *>(st + ar * (PJ_KC * 2) + ((piece ^ ((ar >> 2) & 3)) << 4));
+      bf16x8 av[PJ_MT];
+#pragma unroll
+      for (int m = 0; m < PJ_MT; ++m) {
+        const int ar = ar0 + 32 * m;
+        av[m] = *reinterpret_cast<const bf16x8 *>(st + ar * (PJ_KC * 2) + ((piece ^ ((ar >> 2) & 3)) << 4));
+      }
 #pragma unroll
       for (int n = 0; n < DV / 32; ++n) {
         const int chunk = 4 * n + 2 * (g & 1) + ((q & 3) >> 1);
@@ -158,7 +170,8 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)b0);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)b1);
         const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[n], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < PJ_MT; ++m) acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bv, acc[m][n], 0, 0, 0);
       }
     }
   }
@@ -166,13 +179,15 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
   __syncthreads();
   const int hb = l >> 5, r = l & 31;
 #pragma unroll
-  for (int n = 0; n < DV / 32; ++n)
+  for (int m = 0; m < PJ_MT; ++m)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 32 * wave + (i >> 2) * 8 + hb * 4 + (i & 3), col = 32 * n + r;
-      *reinterpret_cast<uint16_t *>(ring + row * (DV * 2) + (((col >> 3) ^ (row & 15)) << 4) + 2 * (col & 7)) =
-          bf16_bits(to_bf16(acc[n][i]));
-    }
+    for (int n = 0; n < DV / 32; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = ar0 - (l & 31) + 32 * m + (i >> 2) * 8 + hb * 4 + (i & 3), col = 32 * n + r;
+        *reinterpret_cast<uint16_t *>(ring + row * (DV * 2) + (((col >> 3) ^ (row & 15)) << 4) + 2 * (col & 7)) =
+            bf16_bits(to_bf16(acc[m][n][i]));
+      }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < PJ_TM * 16 / 256; ++k) {
