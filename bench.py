@@ -457,31 +457,34 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole steps.  Each step is replayed from a HIP graph
-    # captured once per rotating cache copy (the eager Python launch path costs
-    # more host time per step than the GPU needs).
-    graphs = []
+    # ---- timed region: K whole steps replayed from one HIP graph that holds
+    # all K of them, one after another with the caches and weights rotating
+    # (a model's decode graph holds one such step per layer, so the launch of
+    # a graph is paid once per token, not once per layer).  The eager Python
+    # launch path costs more host time per step than the GPU needs.
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                step(i)
+        return g
+
     try:
-        for c in range(COPIES):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(c)
-            graphs.append(g)
-        for c in range(COPIES):
-            graphs[c].replay()
+        graph = capture(args.steps)
+        graph.replay()                      # untimed first replay
         torch.cuda.synchronize()
-        mode = "hip-graph replay"
+        mode = f"one hip graph of the {args.steps} steps"
     except Exception as e:  # pragma: no cover - falls back to eager launches
-        graphs = []
+        graph = None
         mode = f"eager launches (graph capture failed: {type(e).__name__})"
     torch.cuda.synchronize()
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     g0.record(stream)
-    for i in range(args.steps):
-        if graphs:
-            graphs[i % COPIES].replay()
-        else:
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
             step(i)
     g1.record(stream)
     torch.cuda.synchronize()
@@ -489,6 +492,27 @@ def main():
     gpu_ms = g0.elapsed_time(g1)
     print(f"timed {args.steps} steps ({mode}) in {wall:.4f} s wall, {gpu_ms:.3f} ms GPU",
           file=sys.stderr, flush=True)
+
+    # the same K steps as one graph per step (3 graphs, one per rotating copy,
+    # replayed in turn): every step then also pays one graph launch
+    one_step_us = None
+    if graph is not None:
+        del graph
+        singles = []
+        for c in range(COPIES):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            singles.append(g)
+        for g in singles:
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            singles[i % COPIES].replay()
+        torch.cuda.synchronize()
+        one_step_us = (time.perf_counter() - t1) / args.steps * 1e6
+        del singles
 
     # ---- per-kernel durations: the same steps launched eagerly behind a GPU
     # sleep, so every launch is queued before the GPU reaches it and the HIP
@@ -544,6 +568,7 @@ def main():
         },
         "kernels_avg_us": {k: round(v, 3) for k, v in avg_us.items()},
         "timing": {"timed_region": mode, "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+                   "one_graph_per_step_us": None if one_step_us is None else round(one_step_us, 3),
                    "eager_step_gpu_us": round(eager_step_us, 3),
                    "kernel_events": "HIP events on the launch stream around each call, launches queued "
                                     "behind a GPU sleep"},
