@@ -147,6 +147,27 @@ size_t mla_decode_workspace_bytes(int B, int H, int max_seq_len, int split_token
 int mla_decode_split_tokens(int B, int H, int max_seq_len);
 
 /*
+ * Checks the device-resident paging values that the other calls trust (a
+ * debugging aid; not part of the decode step).  Sequence b is flagged when
+ * seq_lens[b] < 0, seq_lens[b] > max_seq_len,
+ * seq_lens[b] > max_blocks_per_seq * block_size, or a page it uses,
+ * block_table[b][j] for j < ceil(seq_lens[b] / block_size), lies outside
+ * [0, num_blocks) (the paged layout of Riju, "Interaction with quantisation
+ * and paging": token t of sequence b sits in page block_table[b][t / 64],
+ * slot t % 64).
+ *   bad        device int32: receives the number of flagged sequences
+ *   first_bad  device int32 or NULL: receives the smallest flagged b, -1 if none
+ * Asynchronous like every call (read the results after synchronising the
+ * stream); one small launch, no atomics, no memset.  Errors: a null seq_lens,
+ * block_table or bad, B < 1, max_blocks_per_seq < 1, max_seq_len < 0 or
+ * num_blocks < 1 -> MLA_ERR_INVALID_ARGUMENT; block_size != 64 ->
+ * MLA_ERR_UNSUPPORTED.
+ */
+int mla_validate_paging(const int32_t *seq_lens, const int32_t *block_table, int max_blocks_per_seq,
+                        int max_seq_len, int num_blocks, int block_size, int B, int32_t *bad,
+                        int32_t *first_bad, void *stream);
+
+/*
  * Absorbed decode attention over the paged latent cache (Su, eq:mla-mqa:
  * o^(s) = sum_i exp(q^(s) k_i) c_i / sum_i exp(q^(s) k_i) with the shared key
  * k_i = [c_i | rotated k_R,i]; Riju, absorbed decode sketch):

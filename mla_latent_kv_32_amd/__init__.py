@@ -76,6 +76,8 @@ def lib():
     L.mla_decode_workspace_bytes.restype = c_size
     L.mla_decode_split_tokens.argtypes = [c_int, c_int, c_int]
     L.mla_decode_split_tokens.restype = c_int
+    L.mla_validate_paging.argtypes = [i32p, i32p, c_int, c_int, c_int, c_int, c_int, i32p, i32p, vp]
+    L.mla_validate_paging.restype = c_int
     L.mla_decode_paged.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
                                    vp, c_size, vp, vp, c_int, c_int, vp]
     L.mla_decode_paged.restype = c_int
@@ -174,6 +176,21 @@ def mla_decode_workspace_bytes(B, H, max_seq_len, split_tokens=0) -> int:
 
 def mla_decode_split_tokens(B, H, max_seq_len) -> int:
     return int(lib().mla_decode_split_tokens(B, H, max_seq_len))
+
+
+def mla_validate_paging(seq_lens, block_table, max_seq_len, num_blocks, bad, first_bad=None, stream=None):
+    """Flag sequences whose length or pages in use break the bounds the other calls trust:
+    bad (int32 [1] on the device) receives the count, first_bad (int32 [1] or None) the
+    smallest flagged sequence or -1.  Asynchronous; read the results after synchronising."""
+    _dense(seq_lens, "seq_lens", torch.int32)
+    _dense(block_table, "block_table", torch.int32)
+    _dense(bad, "bad", torch.int32)
+    if first_bad is not None:
+        _dense(first_bad, "first_bad", torch.int32)
+    B = seq_lens.shape[0]
+    _check("mla_validate_paging", lib().mla_validate_paging(
+        _ptr(seq_lens), _ptr(block_table), block_table.shape[1], int(max_seq_len), int(num_blocks), BLOCK_SIZE,
+        B, _ptr(bad), _ptr(first_bad), _stream(stream)))
 
 
 def mla_decode_paged(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, softmax_scale, o_latent,

@@ -135,6 +135,25 @@ int mla_absorb_q_rope_append(const void *q_nope, const void *w_uk, const void *q
                                      static_cast<hipStream_t>(stream)));
 }
 
+int mla_validate_paging(const int32_t *seq_lens, const int32_t *block_table, int max_blocks_per_seq,
+                        int max_seq_len, int num_blocks, int block_size, int B, int32_t *bad,
+                        int32_t *first_bad, void *stream) {
+  if (seq_lens == nullptr || block_table == nullptr || bad == nullptr || B < 1 || max_blocks_per_seq < 1 ||
+      max_seq_len < 0 || num_blocks < 1)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (block_size != MLA_BLOCK_SIZE) return MLA_ERR_UNSUPPORTED;
+  mla::ValidateArgs a;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.num_blocks = num_blocks;
+  a.B = B;
+  a.bad = bad;
+  a.first_bad = first_bad;
+  return status_of(mla::launch_validate_paging(a, static_cast<hipStream_t>(stream)));
+}
+
 int mla_decode_split_tokens(int B, int H, int max_seq_len) {
   if (B < 1 || H < 1 || max_seq_len < 0) return 0;
   return plan_split(B, H, max_seq_len);

@@ -114,4 +114,14 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
+// Check of seq_lens / block_table against the host-side bounds.
+struct ValidateArgs {
+  const int32_t *seq_lens;      // [B]
+  const int32_t *block_table;   // [B, max_blocks]
+  int max_blocks, max_seq_len, num_blocks, B;
+  int32_t *bad;                 // number of sequences breaking a rule
+  int32_t *first_bad;           // smallest such b, -1 if none (or null)
+};
+hipError_t launch_validate_paging(const ValidateArgs &a, hipStream_t stream);
+
 }  // namespace mla

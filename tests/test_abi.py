@@ -186,6 +186,23 @@ def test_prefill_call_validates():
     assert L.mla_prefill_workspace_bytes(100, 16) >= 100 * 16 * (64 + 2 * 128) * 2 + 100 * 64 * 2
 
 
+@needs_lib
+def test_paging_check_validates():
+    L = mla.lib()
+
+    def call(sl=FAKE, bt=FAKE, mb=4, max_len=256, nb=10, bs=64, B=2, bad=FAKE, first=FAKE):
+        return L.mla_validate_paging(sl, bt, mb, max_len, nb, bs, B, bad, first, NULL)
+
+    assert call(sl=NULL) == -1
+    assert call(bt=NULL) == -1
+    assert call(bad=NULL) == -1
+    assert call(B=0) == -1
+    assert call(mb=0) == -1
+    assert call(max_len=-1) == -1
+    assert call(nb=0) == -1
+    assert call(bs=32) == -2
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mla, "_LIB", None)
     monkeypatch.setenv("MLA_LIBRARY", str(tmp_path / "missing.so"))
