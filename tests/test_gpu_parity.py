@@ -244,8 +244,10 @@ def test_decode_workload3_split256():
     check_decode(w, o, lse, [(b, [0, 5, 64, 127]) for b in range(w["B"])])
 
 
-@pytest.mark.parametrize("H", [1, 16, 20, 32, 48, 64, 100, 128])
+@pytest.mark.parametrize("H", [1, 16, 20, 32, 48, 64, 100, 128, 200, 256])
 def test_decode_ragged_lengths_and_heads(H):
+    """Every workgroup shape; above 128 heads, several 128-head groups per
+    chunk (200: the second group partly past H, one wave of it entirely)."""
     lens = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 300, 1000]
     w = synth.gaussian_workload(30 + H, B=len(lens), H=H, seq_lens=lens)
     for split in [0, 64, 128]:
@@ -379,10 +381,11 @@ def test_combine_absorb_out_fused(H, lens, split):
 
 
 # --------------------------------------------------------------------- fp8 cache
-@pytest.mark.parametrize("H", [16, 64, 128])
+@pytest.mark.parametrize("H", [16, 64, 128, 200])
 def test_decode_fp8_ragged_lengths_and_heads(H):
     """Packed E4M3 rows (656 bytes): every workgroup shape (2, 4, 8 waves),
-    partial last blocks, page boundaries, several split sizes."""
+    two head groups (200 heads), partial last blocks, page boundaries,
+    several split sizes."""
     lens = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 300, 1000, 2100]
     w = synth.gaussian_workload(70 + H, B=len(lens), H=H, seq_lens=lens, kv_dtype=synth.KV_FP8)
     for split in [0, 64, 256]:
