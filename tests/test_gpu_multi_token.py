@@ -92,12 +92,13 @@ def check_multi(w, qm, o, lse, pairs):
 LENS = [0, 1, 2, 3, 4, 31, 32, 33, 34, 63, 64, 65, 66, 97, 300, 513, 1000]
 
 
-@pytest.mark.parametrize("H,q_len", [(16, 2), (16, 4), (8, 3), (128, 2), (40, 4)])
+@pytest.mark.parametrize("H,q_len", [(16, 2), (16, 4), (8, 3), (128, 2), (40, 4), (2, 32), (8, 32)])
 @pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8])
 def test_multi_token_matches_oracle(H, q_len, kv_dtype):
     """Ragged lengths around block and chunk edges (and sequences shorter
     than q_len) with query rows on both decoders (q_len * H <= 64: two waves
-    per SIMD; above: one wave per SIMD, 128 rows per workgroup)."""
+    per SIMD; above: one wave per SIMD, 128 rows per workgroup), up to the
+    largest q_len (32)."""
     w = synth.gaussian_workload(200 + H + 10 * q_len + kv_dtype, B=len(LENS), H=H, seq_lens=LENS,
                                 kv_dtype=kv_dtype)
     qm = synth.multi_token_query(300 + H + q_len, len(LENS), q_len, H)
