@@ -97,6 +97,16 @@ def test_prefill_long_prompts_full_heads():
     check_prefill(w, o, pool, [(0, [0, 77]), (3, [127])])
 
 
+def test_prefill_long_ragged_prompt():
+    """One 4001-token prompt (126 key blocks, a ragged last query tile and
+    page) beside a short one: every token of two heads against the oracle,
+    and every cache row of the long prompt."""
+    w = synth.prefill_workload(740, 8, [4001, 37])
+    o, pool = run_prefill(w)
+    assert not torch.isnan(o.float()).any().item()
+    check_prefill(w, o, pool, [(0, [0, 7]), (1, [3])], rows_for=[0])
+
+
 @pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8])
 def test_decode_after_prefill(kv_dtype):
     """The rows a prefill leaves are the cache the decode reads: a decode
