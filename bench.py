@@ -78,6 +78,8 @@ def parse():
                     help="> 1: time the multi-token decode (q_len new tokens per sequence) on the same cache")
     ap.add_argument("--prefill", action="store_true",
                     help="time the explicit-form prefill of 4 prompts of 1024 tokens, 128 heads")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the decode over the fp8 latent cache: B=128 sequences of 8192 tokens, 128 heads")
     ap.add_argument("--heads", type=int, default=128,
                     help="with --q-len: heads per token (128: the DeepSeek-V3-shaped workload; other values: "
                          "the same shape with N(0,1) entries, e.g. 16 = one GPU's share under 8-way head "
@@ -396,6 +398,118 @@ def cpu_baseline_prefill(w, o):
             "parity": _check(got, ref, 2.0 ** -8 * mag, "o of every token of prompt 1, heads 0 and 127")}
 
 
+def main_fp8(args):
+    """--fp8: the decode over the fp8 latent cache (packed E4M3 rows of 656 bytes: 512 codes,
+    the bf16 rotary key, 4 group scales) of B=128 sequences of 8192 tokens with 128 heads
+    (688 MB of rows; synth.workload(4)), as mla_decode_partial + mla_decode_combine in the
+    planner's chunking.  value = packed row bytes / decode-kernel time; the products run on
+    bf16 MFMAs over the expanded rows, so the roofline is the bf16 MFMA peak."""
+    import torch
+    import mla_latent_kv_32_amd as mla
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    mla.lib()
+    w = synth.workload(4)
+    B, H = w["B"], w["H"]
+    S = int(w["seq_lens"].max())
+    row_bytes = 656
+    caches = [torch.from_numpy(w["cache_full"]).cuda() for _ in range(COPIES)]
+    q = torch.from_numpy(np.ascontiguousarray(w["q_decode"]).view(np.int16)).view(torch.bfloat16).cuda()
+    sl = torch.from_numpy(w["seq_lens"]).cuda()
+    bt = torch.from_numpy(w["block_table"]).cuda()
+    split = args.split_tokens or mla.mla_decode_split_tokens(B, H, S)
+    ws = torch.empty(mla.mla_decode_workspace_bytes(B, H, S, split), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_decode_partial(q, caches[i % COPIES], mla.KV_FP8_E4M3, bt, sl, S, w["scale"], ws, split_tokens=split)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.mla_decode_combine(ws, sl, S, o, lse, split_tokens=split)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)      # every launch below is queued before the GPU reaches it
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+    comb = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    dec_us, comb_us = float(np.mean(dec)), float(np.mean(comb))
+    cache_bytes = B * S * row_bytes
+    flops = 2.0 * B * H * S * (576 + 512)
+    gbs = cache_bytes / (dec_us * 1e-6) / 1e9
+    tflops = flops / (dec_us * 1e-6) / 1e12
+    out = {
+        "metric": "MLA fp8-cache decode packed-latent GB/s + TFLOP/s (% roofline), H=128 B=128 ctx=8K, 1 GPU",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((dec_us + comb_us) * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "MLA absorbed decode over an fp8 E4M3 latent cache (one fp32 scale per token and "
+                               "128-group, bf16 rotary key): B=128, H=128, context 8192, 656-byte rows in "
+                               "[16384 pages, 64, 656]", "B": B, "H": H, "seq_len": S, "split_tokens": split,
+                   "parallelism": "single GPU"},
+        "decode_kernel": {"avg_us": round(dec_us, 3),
+                          "p10_p50_p90_us": [round(float(np.percentile(dec, p)), 3) for p in (10, 50, 90)],
+                          "packed_gbs": round(gbs, 1), "tflops": round(tflops, 1),
+                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "kernels_avg_us": {"decode": round(dec_us, 3), "combine": round(comb_us, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "scope": "decode kernel alone (HIP events on the launch stream); the expanded rows feed "
+                              "bf16 MFMAs, 424.6 FLOP per packed byte"},
+        "timing": {"timed_region": "eager launches behind a GPU sleep, HIP events around each call",
+                   "wall_s": round(wall, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_fp8(w, o)
+        out["parity"] = out["cpu_baseline"]["parity"]
+        assert out["parity"]["ok"], "benchmarked output differs from the oracle"
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_fp8(w, o):
+    """The CPU leg of --fp8: the oracle's decode (rows dequantised to fp64) for (b, h) in
+    (0, 0), (0, 127), (127, 64), timed and scaled per (sequence, head) pair to the whole
+    batch, and its o_latent compared with the benchmarked one under the fp8 bound
+    2e-3 + 6e-2 |ref| (+ 2^-8 sum_t p_t |c_t| for the bf16 rounding of the weights)."""
+    import oracle
+    B, H = w["B"], w["H"]
+    S = int(w["seq_lens"].max())
+    pairs = [(0, [0, 127]), (127, [64])]
+    got, ref, extra = [], [], []
+    t0 = time.perf_counter()
+    for b, heads in pairs:
+        r, _, mag = oracle.reference_decode(w, b, heads, with_magnitude=True)
+        ref.append(r)
+        extra.append(2.0 ** -8 * mag)           # sum_t p_t |c_t|, per element
+    dt = time.perf_counter() - t0
+    for b, heads in pairs:
+        got.append(o[b, heads].float().cpu().numpy().astype(np.float64))
+    got, ref, extra = np.concatenate(got), np.concatenate(ref), np.concatenate(extra)
+    err = np.abs(got - ref)
+    ok = bool((err <= 2e-3 + 6e-2 * np.abs(ref) + extra).all())
+    n = sum(len(h) for _, h in pairs)
+    job_s = dt / n * B * H
+    return {"value": round(B * S * 656 / job_s / 1e9, 6), "unit": "GB/s", "cores": _oracle_cores(),
+            "cpu_model": _cpu_model(), "kind": "oracle",
+            "sample": f"{n} (sequence, head) pairs of {B * H}, rows dequantised to fp64, {dt:.2f} s; scaled to "
+                      f"the whole batch ({job_s:.0f} s)",
+            "parity": {"checked": "o_latent for (b,h) in (0,0),(0,127),(127,64)", "max_abs_err": float(err.max()),
+                       "ok": ok}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -412,6 +526,9 @@ def main():
         return
     if args.prefill:
         main_prefill(args)
+        return
+    if args.fp8:
+        main_fp8(args)
         return
 
     import mla_latent_kv_32_amd as mla
