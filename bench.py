@@ -53,10 +53,10 @@ COPIES = 3
 # reported only while that source is unchanged.
 DECODE_TRAFFIC = {
     "sources_sha256": {
-        "mla_latent_kv_32_amd/csrc/decode.hip": "4f699be56c26f0ac28cb797512bacd9060ecaaf78d90fbae6098b100f7a2e8bd",
+        "mla_latent_kv_32_amd/csrc/decode.hip": "0ac224724df606869c824ae2c937ae7c480791d714b4b6d049c8c0d71d6a5cf9",
         "mla_latent_kv_32_amd/csrc/common.h": "748cb997b4658e63c1b64bf8032fbb164e6e9bedcf880b094934b6a8c62b4bea",
     },
-    "fetch_kib": 76232.3,
+    "fetch_kib": 76216.3,
     "write_kib": 32896.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
@@ -78,6 +78,8 @@ def parse():
                     help="> 1: time the multi-token decode (q_len new tokens per sequence) on the same cache")
     ap.add_argument("--prefill", action="store_true",
                     help="time the explicit-form prefill of 4 prompts of 1024 tokens, 128 heads")
+    ap.add_argument("--long", action="store_true",
+                    help="time the split-KV decode of 4 long sequences (1K-32K tokens), 128 heads, 256-token chunks")
     ap.add_argument("--fp8", action="store_true",
                     help="time the decode over the fp8 latent cache: B=128 sequences of 8192 tokens, 128 heads")
     ap.add_argument("--heads", type=int, default=128,
@@ -398,27 +400,37 @@ def cpu_baseline_prefill(w, o):
             "parity": _check(got, ref, 2.0 ** -8 * mag, "o of every token of prompt 1, heads 0 and 127")}
 
 
-def main_fp8(args):
-    """--fp8: the decode over the fp8 latent cache (packed E4M3 rows of 656 bytes: 512 codes,
-    the bf16 rotary key, 4 group scales) of B=128 sequences of 8192 tokens with 128 heads
-    (688 MB of rows; synth.workload(4)), as mla_decode_partial + mla_decode_combine in the
-    planner's chunking.  value = packed row bytes / decode-kernel time; the products run on
-    bf16 MFMAs over the expanded rows, so the roofline is the bf16 MFMA peak."""
+def main_cache_workload(args, cfg):
+    """--long (workload 3) and --fp8 (workload 4): the decode alone, as
+    mla_decode_partial + mla_decode_combine, on a split-KV workload.
+      3: B=4 sequences of U{1024..32768} tokens, H=128, bf16 cache, 256-token chunks;
+         bound by HBM (241.8 FLOP per cached byte), value = cached bytes / decode time.
+      4: B=128 sequences of 8192 tokens, H=128, fp8 E4M3 rows of 656 bytes (512 codes,
+         the bf16 rotary key, 4 group scales; 688 MB), the planner's chunking; the rows
+         are expanded to bf16 for bf16 MFMAs, so the roofline is the bf16 MFMA peak.
+    """
     import torch
     import mla_latent_kv_32_amd as mla
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     mla.lib()
-    w = synth.workload(4)
+    w = synth.workload(cfg)
     B, H = w["B"], w["H"]
     S = int(w["seq_lens"].max())
-    row_bytes = 656
-    caches = [torch.from_numpy(w["cache_full"]).cuda() for _ in range(COPIES)]
+    fp8 = w["kv_dtype"] == synth.KV_FP8
+    row_bytes = 656 if fp8 else ROW_BYTES
+    kv_dtype = mla.KV_FP8_E4M3 if fp8 else mla.KV_BF16
+
+    def dev_pool(pool):
+        t = torch.from_numpy(np.ascontiguousarray(pool))
+        return (t.view(torch.int16).view(torch.bfloat16) if not fp8 else t).cuda()
+
+    caches = [dev_pool(w["cache_full"]) for _ in range(COPIES)]
     q = torch.from_numpy(np.ascontiguousarray(w["q_decode"]).view(np.int16)).view(torch.bfloat16).cuda()
     sl = torch.from_numpy(w["seq_lens"]).cuda()
     bt = torch.from_numpy(w["block_table"]).cuda()
-    split = args.split_tokens or mla.mla_decode_split_tokens(B, H, S)
+    split = args.split_tokens or (256 if cfg == 3 else mla.mla_decode_split_tokens(B, H, S))
     ws = torch.empty(mla.mla_decode_workspace_bytes(B, H, S, split), dtype=torch.uint8, device="cuda")
     o = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
@@ -427,7 +439,7 @@ def main_fp8(args):
     def step(i, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        mla.mla_decode_partial(q, caches[i % COPIES], mla.KV_FP8_E4M3, bt, sl, S, w["scale"], ws, split_tokens=split)
+        mla.mla_decode_partial(q, caches[i % COPIES], kv_dtype, bt, sl, S, w["scale"], ws, split_tokens=split)
         if ev is not None:
             ev[1].record(stream)
         mla.mla_decode_combine(ws, sl, S, o, lse, split_tokens=split)
@@ -447,67 +459,81 @@ def main_fp8(args):
     dec = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
     comb = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
     dec_us, comb_us = float(np.mean(dec)), float(np.mean(comb))
-    cache_bytes = B * S * row_bytes
-    flops = 2.0 * B * H * S * (576 + 512)
+    tokens = int(w["seq_lens"].sum())
+    cache_bytes = tokens * row_bytes
+    flops = 2.0 * H * tokens * (576 + 512)
     gbs = cache_bytes / (dec_us * 1e-6) / 1e9
     tflops = flops / (dec_us * 1e-6) / 1e12
+    if fp8:
+        metric = "MLA fp8-cache decode packed-latent GB/s + TFLOP/s (% roofline), H=128 B=128 ctx=8K, 1 GPU"
+        workload = ("MLA absorbed decode over an fp8 E4M3 latent cache (one fp32 scale per token and 128-group, "
+                    "bf16 rotary key): B=128, H=128, context 8192, 656-byte rows in [16384 pages, 64, 656]")
+        roofline = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "scope": "decode kernel alone (HIP events on the launch stream); the expanded rows feed "
+                             "bf16 MFMAs, 424.6 FLOP per packed byte"}
+    else:
+        metric = "MLA long-context split-KV decode latent-KV GB/s + TFLOP/s (% roofline), H=128 B=4, 1 GPU"
+        workload = (f"MLA absorbed decode, variable long contexts: B=4, H=128, seq_lens "
+                    f"{[int(x) for x in w['seq_lens']]}, bf16 paged cache, {split}-token chunks + combine")
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "scope": "decode kernel alone (HIP events on the launch stream)"}
     out = {
-        "metric": "MLA fp8-cache decode packed-latent GB/s + TFLOP/s (% roofline), H=128 B=128 ctx=8K, 1 GPU",
+        "metric": metric,
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round((dec_us + comb_us) * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "MLA absorbed decode over an fp8 E4M3 latent cache (one fp32 scale per token and "
-                               "128-group, bf16 rotary key): B=128, H=128, context 8192, 656-byte rows in "
-                               "[16384 pages, 64, 656]", "B": B, "H": H, "seq_len": S, "split_tokens": split,
-                   "parallelism": "single GPU"},
+        "config": {"workload": workload, "B": B, "H": H, "max_seq_len": S, "tokens": tokens,
+                   "split_tokens": split, "parallelism": "single GPU"},
         "decode_kernel": {"avg_us": round(dec_us, 3),
                           "p10_p50_p90_us": [round(float(np.percentile(dec, p)), 3) for p in (10, 50, 90)],
-                          "packed_gbs": round(gbs, 1), "tflops": round(tflops, 1),
-                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+                          "cache_gbs": round(gbs, 1), "tflops": round(tflops, 1),
+                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         "kernels_avg_us": {"decode": round(dec_us, 3), "combine": round(comb_us, 3)},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "scope": "decode kernel alone (HIP events on the launch stream); the expanded rows feed "
-                              "bf16 MFMAs, 424.6 FLOP per packed byte"},
+        "roofline": roofline,
         "timing": {"timed_region": "eager launches behind a GPU sleep, HIP events around each call",
                    "wall_s": round(wall, 4)},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_fp8(w, o)
+        out["cpu_baseline"] = cpu_baseline_decode(w, o, row_bytes)
         out["parity"] = out["cpu_baseline"]["parity"]
         assert out["parity"]["ok"], "benchmarked output differs from the oracle"
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_fp8(w, o):
-    """The CPU leg of --fp8: the oracle's decode (rows dequantised to fp64) for (b, h) in
-    (0, 0), (0, 127), (127, 64), timed and scaled per (sequence, head) pair to the whole
-    batch, and its o_latent compared with the benchmarked one under the fp8 bound
-    2e-3 + 6e-2 |ref| (+ 2^-8 sum_t p_t |c_t| for the bf16 rounding of the weights)."""
+def cpu_baseline_decode(w, o, row_bytes):
+    """The CPU leg of --long / --fp8: the oracle's decode (fp8 rows dequantised to fp64)
+    for (first sequence, heads 0 and 127) and (last sequence, head 64), timed and scaled
+    per (sequence, head) pair to the whole batch, and its o_latent compared with the
+    benchmarked one: bf16 cache 2e-3 + 2e-2 |ref|; fp8 cache 2e-3 + 6e-2 |ref| + 2^-8
+    sum_t p_t |c_t| (the bf16 rounding of the weights, as in the fp8 tests)."""
     import oracle
     B, H = w["B"], w["H"]
-    S = int(w["seq_lens"].max())
-    pairs = [(0, [0, 127]), (127, [64])]
+    fp8 = w["kv_dtype"] == 1
+    pairs = [(0, [0, 127]), (B - 1, [64])]
     got, ref, extra = [], [], []
     t0 = time.perf_counter()
     for b, heads in pairs:
         r, _, mag = oracle.reference_decode(w, b, heads, with_magnitude=True)
         ref.append(r)
-        extra.append(2.0 ** -8 * mag)           # sum_t p_t |c_t|, per element
+        extra.append(2.0 ** -8 * mag if fp8 else np.zeros_like(r))
     dt = time.perf_counter() - t0
     for b, heads in pairs:
         got.append(o[b, heads].float().cpu().numpy().astype(np.float64))
     got, ref, extra = np.concatenate(got), np.concatenate(ref), np.concatenate(extra)
     err = np.abs(got - ref)
-    ok = bool((err <= 2e-3 + 6e-2 * np.abs(ref) + extra).all())
+    rtol = 6e-2 if fp8 else 2e-2
+    ok = bool((err <= 2e-3 + rtol * np.abs(ref) + extra).all())
     n = sum(len(h) for _, h in pairs)
     job_s = dt / n * B * H
-    return {"value": round(B * S * 656 / job_s / 1e9, 6), "unit": "GB/s", "cores": _oracle_cores(),
-            "cpu_model": _cpu_model(), "kind": "oracle",
-            "sample": f"{n} (sequence, head) pairs of {B * H}, rows dequantised to fp64, {dt:.2f} s; scaled to "
-                      f"the whole batch ({job_s:.0f} s)",
-            "parity": {"checked": "o_latent for (b,h) in (0,0),(0,127),(127,64)", "max_abs_err": float(err.max()),
-                       "ok": ok}}
+    return {"value": round(int(w["seq_lens"].sum()) * row_bytes / job_s / 1e9, 6), "unit": "GB/s",
+            "cores": _oracle_cores(), "cpu_model": _cpu_model(), "kind": "oracle",
+            "sample": f"{n} (sequence, head) pairs of {B * H}, fp64, {dt:.2f} s; scaled to the whole batch "
+                      f"({job_s:.0f} s)",
+            "parity": {"checked": f"o_latent for (b,h) in (0,0),(0,127),({B - 1},64)",
+                       "max_abs_err": float(err.max()), "ok": ok}}
 
 
 def main():
@@ -527,8 +553,8 @@ def main():
     if args.prefill:
         main_prefill(args)
         return
-    if args.fp8:
-        main_fp8(args)
+    if args.fp8 or args.long:
+        main_cache_workload(args, 4 if args.fp8 else 3)
         return
 
     import mla_latent_kv_32_amd as mla

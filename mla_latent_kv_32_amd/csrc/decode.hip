@@ -1546,7 +1546,7 @@ void decode_fp8_kernel(DecodeArgs a) {
 // multi-token row merges the chunks that hold tokens it sees.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int b = blockIdx.x;
-  const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int head = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int t = threadIdx.x & 63;
   if (head >= a.H) return;
   int S = a.seq_lens[b];
@@ -1628,7 +1628,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
-  combine_kernel<<<dim3(a.B, (a.H + 3) / 4), 256, 0, stream>>>(a);
+  // one wave per (b, head): the heads of a long sequence, whose rows each
+  // stream every chunk of it, are spread over as many compute units as there
+  // are heads
+  combine_kernel<<<dim3(a.B, a.H), 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
