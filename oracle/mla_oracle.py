@@ -16,8 +16,9 @@ Sources (cited by title and section):
          the Part 2 decoupled-RoPE equation, and the Part 3 MHA form
          (eq:mla-mha) and decoding-stage MQA form (eq:mla-mqa).
   [Riju] "Multi-Head Latent Attention vs GQA vs MQA: KV-Cache Compression
-         Explained" -- "A latent KV projection in PyTorch" (rope function,
-         non-absorbed module, absorbed decode sketch, the equivalence test),
+         Explained" -- "A latent KV projection in PyTorch" (the RoPE pair
+         convention, non-absorbed module, absorbed decode sketch, the
+         equivalence test),
          "Worked numbers from real configs", "Interaction with quantisation
          and paging".
   [DL0107] "DL0107 Multi-head Latent Attention MLA" -- the cache holds the
@@ -126,28 +127,30 @@ def fp8_row_decode(rec):
 
 
 # --------------------------------------------------------------------------
-# rotary position embedding  ([Riju] rope function; [Su] Part 2, R_m)
+# rotary position embedding  ([Su] Part 2, the rotation R_m)
 # --------------------------------------------------------------------------
 
 
 def rope(v, pos, theta=10000.0) -> np.ndarray:
-    """Rotate interleaved pairs (v[2i], v[2i+1]) by angle pos * theta^(-2i/d).
+    """Apply R_pos to v: the block-diagonal rotation of [Su] Part 2.
+
+    Block i of R_m acts on the interleaved pair (v[2i], v[2i+1]) and turns it
+    by the angle m * w_i, w_i = theta^(-2i/d).  Written here in complex form:
+    the pair is z_i = v[2i] + 1j v[2i+1], R_m multiplies it by the unit phasor
+    e^(1j m w_i), and the real and imaginary parts go back to slots 2i and
+    2i+1.  R_m R_n^T = R_(m-n) holds because the phasors multiply.
 
     v: [..., d] (d even); pos: scalar or array broadcastable to v[..., 0].
-    The pair convention and frequencies are those of the rope function in
-    [Riju], section "A latent KV projection in PyTorch"; R_m R_n^T = R_{m-n}
-    ([Su], Part 2) holds for this block-diagonal rotation.
     """
     v = np.asarray(v, dtype=F64)
     d = v.shape[-1]
-    inv = 1.0 / (F64(theta) ** (np.arange(0, d, 2, dtype=F64) / d))
-    ang = np.asarray(pos, dtype=F64)[..., None] * inv
-    cos, sin = np.cos(ang), np.sin(ang)
-    x1, x2 = v[..., 0::2], v[..., 1::2]
-    out = np.empty(np.broadcast_shapes(v.shape, ang.shape[:-1] + (d,)), dtype=F64)
-    out[..., 0::2] = x1 * cos - x2 * sin
-    out[..., 1::2] = x1 * sin + x2 * cos
-    return out
+    half = d // 2
+    omega = np.power(F64(theta), -2.0 * np.arange(half, dtype=F64) / d)
+    pairs = v.reshape(v.shape[:-1] + (half, 2))
+    z = pairs[..., 0] + 1j * pairs[..., 1]
+    phasor = np.exp(1j * (np.asarray(pos, dtype=F64)[..., None] * omega))
+    w = z * phasor
+    return np.stack([w.real, w.imag], axis=-1).reshape(w.shape[:-1] + (d,))
 
 
 # --------------------------------------------------------------------------
@@ -360,27 +363,53 @@ def reference_decode_multi(inp, q_multi, b, heads=None):
     return decode_multi_token(q[..., :512], q[..., 512:], c, kr, inp["scale"])
 
 
-def reference_step(inp, b, heads=None):
-    """Full decode step for sequence b from the step inputs (explicit K/V form).
+def decode_step(q_nope, q_pe, new_c, new_k_pe, c_prefix, kr_prefix, w_uk, w_uv, scale, theta=10000.0,
+                heads=None):
+    """One decode step of one sequence from values (explicit K/V form).
 
-    The new token (position S_b - 1) contributes [c_new | RoPE(kr_new, S_b-1)]
-    (fp8 caches: c_new quantised and dequantised by this module's quantiser);
-    the query is [q_nope | RoPE(q_pe, S_b-1)].  Returns a dict with
-    q_lat, q_rot, new_c, new_kr (and fp8 codes/scales), o_lat, lse and o
-    for the requested heads.
+    The sequence holds S = len(c_prefix) + 1 tokens after the step; the new
+    token is the last, at position S - 1 ([Su] MHA equation: token t attends
+    to i <= t, itself included; [Riju] absorbed decode sketch: the new latent
+    and rotated key are appended before attending).  Its key row is
+    [new_c | RoPE(new_k_pe, S - 1)] and its query [q_nope | RoPE(q_pe, S - 1)];
+    prefix row t (rotated at position t when it was cached) is
+    [c_prefix[t] | kr_prefix[t]].
+        q_nope [H, d_nope], q_pe [H, d_r] (unrotated), new_c [d_c],
+        new_k_pe [d_r] (unrotated), c_prefix [S-1, d_c], kr_prefix [S-1, d_r]
+    Returns a dict with q_rot, new_kr, q_lat, o_lat, lse and o for the heads.
+    """
+    c_prefix = np.asarray(c_prefix, F64)
+    pos = c_prefix.shape[0]
+    H = np.asarray(q_nope).shape[0]
+    heads = list(range(H)) if heads is None else list(heads)
+    q_nope = np.asarray(q_nope, F64)
+    q_rot = rope(np.asarray(q_pe, F64), pos, theta)
+    new_kr = rope(np.asarray(new_k_pe, F64), pos, theta)
+    c = np.concatenate([c_prefix, np.asarray(new_c, F64)[None]], 0)
+    kr = np.concatenate([np.asarray(kr_prefix, F64).reshape(pos, new_kr.shape[0]), new_kr[None]], 0)
+    o, o_lat, lse = decode_explicit(q_nope, q_rot, c, kr, w_uk, w_uv, scale, heads)
+    w_uk_h = np.asarray(w_uk, F64)[heads]
+    return dict(q_rot=q_rot[heads], new_kr=new_kr, q_lat=absorb_q(q_nope[heads], w_uk_h),
+                o_lat=o_lat, lse=lse, o=o)
+
+
+def reference_step(inp, b, heads=None):
+    """Full decode step for sequence b from the stored step inputs.
+
+    Decodes the storage formats and runs decode_step on sequence b's S_b - 1
+    cached prefix rows (inp["cache_step"]) and its new token inp["kv_new"][b]
+    (fp8 caches: the new latent quantised and dequantised by this module's
+    quantiser, as the append stores it).  Returns decode_step's dict plus
+    new_c (and new_codes / new_scales for fp8).  S_b = 0 is an empty slot:
+    zero outputs and lse = -inf, the query rotated at position 0.
     """
     S = int(inp["seq_lens"][b])
     H = inp["H"]
     heads = list(range(H)) if heads is None else list(heads)
     fp8 = inp["kv_dtype"] == 1
     theta = inp["theta"]
-    pos = max(S - 1, 0)
-    q_nope = bf16_to_f64(inp["q_nope"][b])
-    q_rot = rope(bf16_to_f64(inp["q_pe"][b]), pos, theta)
     new = inp["kv_new"][b]
-    new_kr = rope(bf16_to_f64(new[512:]), pos, theta)
-    w_uk_h = bf16_to_f64(np.asarray(inp["w_uk"])[heads])
-    out = dict(q_rot=q_rot[heads], q_lat=absorb_q(q_nope[heads], w_uk_h), new_kr=new_kr)
+    out = {}
     if fp8:
         codes, scales = fp8_quantize_latent(new[:512])
         out["new_codes"], out["new_scales"] = codes, scales
@@ -388,18 +417,19 @@ def reference_step(inp, b, heads=None):
     else:
         new_c = bf16_to_f64(new[:512])
     out["new_c"] = new_c
+    q_nope = bf16_to_f64(inp["q_nope"][b])
+    q_pe = bf16_to_f64(inp["q_pe"][b])
+    w_uk = bf16_to_f64(inp["w_uk"])
     if S == 0:
         n = len(heads)
-        out.update(o_lat=np.zeros((n, 512)), lse=np.full(n, -np.inf), o=np.zeros((n, 128)))
+        out.update(q_rot=rope(q_pe[heads], 0, theta), new_kr=rope(bf16_to_f64(new[512:]), 0, theta),
+                   q_lat=absorb_q(q_nope[heads], w_uk[heads]),
+                   o_lat=np.zeros((n, 512)), lse=np.full(n, -np.inf), o=np.zeros((n, 128)))
         return out
     rows = gather_rows(inp["cache_step"], inp["block_table"], b, S - 1, inp["block_size"])
     c, kr = rows_to_latent_rope(rows, fp8)
-    c = np.concatenate([c, new_c[None]], 0)
-    kr = np.concatenate([kr, new_kr[None]], 0)
-    w_uk = bf16_to_f64(inp["w_uk"])
-    w_uv = bf16_to_f64(inp["w_uv"])
-    o, o_lat, lse = decode_explicit(q_nope, q_rot, c, kr, w_uk, w_uv, inp["scale"], heads)
-    out.update(o=o, o_lat=o_lat, lse=lse)
+    out.update(decode_step(q_nope, q_pe, new_c, bf16_to_f64(new[512:]), c, kr, w_uk, bf16_to_f64(inp["w_uv"]),
+                           inp["scale"], theta, heads))
     return out
 
 

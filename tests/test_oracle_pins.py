@@ -391,6 +391,47 @@ def test_reference_step_consistent_forms_workload1():
         np.testing.assert_allclose(oracle.absorb_out(o_lat, w_uv), r["o"], rtol=1e-9, atol=1e-12)
 
 
+@pytest.mark.parametrize("S", [1, 2, 37, 64])
+def test_decode_step_is_the_last_row_of_the_mha_prefill(S):
+    """The step's composition, pinned to the MHA form from hidden states
+    ([Su] MHA equation with i <= t; Part 2 decoupled RoPE): decoding token
+    S - 1 of workload 0 -- prefix rows [c | RoPE(x W_KR, t)] for t < S - 1,
+    the new token's latent, unrotated rope key and query projected from
+    x[S - 1] -- reproduces row S - 1 of the causal MHA-form prefill.  A query
+    or appended key rotated at any other position, or a new row left out of
+    the softmax, fails this."""
+    w = synth.workload(0)
+    o, c, kr, _, _ = oracle.prefill_mha_form(
+        w["x"], w["w_dkv"], w["w_kr"], w["w_q"], w["w_uk"], w["w_uv"], w["d_nope"], w["d_r"], w["scale"], w["theta"])
+    x = np.asarray(w["x"], np.float64)[S - 1]
+    q = (x @ np.asarray(w["w_q"], np.float64)).reshape(w["H"], -1)
+    r = oracle.decode_step(q[:, :w["d_nope"]], q[:, w["d_nope"]:], x @ np.asarray(w["w_dkv"], np.float64),
+                           x @ np.asarray(w["w_kr"], np.float64), c[:S - 1], kr[:S - 1], w["w_uk"], w["w_uv"],
+                           w["scale"], w["theta"])
+    np.testing.assert_allclose(r["o"], o[S - 1], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["new_kr"], kr[S - 1], rtol=1e-12, atol=1e-14)
+
+
+def test_reference_step_passes_the_stored_prefix_and_new_token():
+    """reference_step reads exactly the S_b - 1 prefix rows of the step cache
+    (the slot of the new row holds poison) in logical order through the page
+    table, and the new token from kv_new: equal to decode_step on rows
+    gathered here one token at a time."""
+    w = synth.gaussian_workload(3, B=3, H=4, seq_lens=[1, 70, 130])
+    w_uk, w_uv = oracle.bf16_to_f64(w["w_uk"]), oracle.bf16_to_f64(w["w_uv"])
+    for b in range(3):
+        S = int(w["seq_lens"][b])
+        rows = np.array([w["cache_step"][w["block_table"][b][t // 64], t % 64] for t in range(S - 1)],
+                        dtype=np.uint16).reshape(S - 1, 576)
+        vals = oracle.bf16_to_f64(rows)
+        new = oracle.bf16_to_f64(w["kv_new"][b])
+        ref = oracle.decode_step(oracle.bf16_to_f64(w["q_nope"][b]), oracle.bf16_to_f64(w["q_pe"][b]), new[:512],
+                                 new[512:], vals[:, :512], vals[:, 512:], w_uk, w_uv, w["scale"], w["theta"])
+        r = oracle.reference_step(w, b)
+        for k in ("o", "o_lat", "lse", "q_rot", "new_kr", "q_lat"):
+            np.testing.assert_array_equal(r[k], ref[k])
+
+
 def test_reference_decode_empty_sequence():
     w = synth.gaussian_workload(1, B=3, H=2, seq_lens=[0, 1, 65])
     o, l = oracle.reference_decode(w, 0)
