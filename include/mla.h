@@ -324,6 +324,10 @@ int mla_decode_combine_absorb_out(const void *workspace, size_t workspace_bytes,
  *   workspace   device buffer of mla_prefill_workspace_bytes(T, H) bytes
  *               (rotated queries and keys, per-head K and V, W_UK transposed)
  * Empty prompts write nothing.  Errors as for the decode calls.
+ * Precision: the attention runs on IEEE-half operands with fp32
+ * accumulation (rotated query and key, K_nope, V and the softmax weights),
+ * so per-head queries, keys and values must stay below 65504 in magnitude;
+ * larger values overflow to infinity.
  */
 size_t mla_prefill_workspace_bytes(int total_tokens, int H);
 

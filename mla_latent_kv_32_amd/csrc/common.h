@@ -11,6 +11,8 @@ namespace mla {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -43,6 +45,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ __bf16 to_bf16(float f) { return static_cast<__bf16>(f); }
 
 __device__ __forceinline__ uint16_t bf16_bits(__bf16 v) { return __builtin_bit_cast(uint16_t, v); }
+
+// Round-to-nearest-even float -> IEEE half (bits).  Finite only below 65520.
+__device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f)); }
 
 __device__ __forceinline__ float bf16_round_f32(float f) {
   return static_cast<float>(static_cast<__bf16>(f));

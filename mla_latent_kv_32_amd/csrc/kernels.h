@@ -105,11 +105,11 @@ struct PrefillArgs {
   float scale_log2;             // softmax_scale * log2(e)
   int B, H, T, max_len;
   uint16_t *o;                  // [T, H, 128]
-  // workspace
-  uint16_t *q_rot;              // [T, H, 64]
-  uint16_t *k_rot;              // [T, 64]
-  uint16_t *k_nope;             // [T, H, 128]
-  uint16_t *v;                  // [T, H, 128]
+  // workspace (attention operands in IEEE half)
+  uint16_t *q_rot;              // [T, H, 64] fp16
+  uint16_t *k_rot;              // [T, 64] fp16
+  uint16_t *k_nope;             // [T, H, 128] fp16
+  uint16_t *v;                  // [T, H, 128] fp16
   uint16_t *w_ukt;              // [H, 512, 128] = W_UK transposed per head
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);

@@ -12,6 +12,16 @@
 // and the prompt's rows [c_t | RoPE(k_pe_t, t)] go to the paged latent cache
 // for the decode steps that follow.  Token t of a prompt sits at position t.
 //
+// Precision.  The attention's operands -- the rotated query and key, the
+// materialised K_nope and V, and the softmax weights P -- are IEEE half
+// (fp16 MFMAs, fp32 accumulation): each is one rounding away from its fp32
+// value, and half's 11-bit significand keeps the sum of those roundings
+// inside 2e-3 + 2e-2 |o| where bf16's 8 bits do not (a row of a short
+// prefix is a sum of a few O(1) terms).  q_nope arrives in bf16 and converts
+// to half exactly.  Half is finite below 65520: per-head keys, values and
+// queries must stay below that magnitude (unit-scale activations are five
+// orders of magnitude inside it); P stays at most 2^8 by the lazy rescale.
+//
 // Launches: RoPE + cache rows; W_UK transposed per head; the two
 // up-projections; causal attention.
 #include "common.h"
@@ -24,8 +34,9 @@ namespace {
 // ---- RoPE of the prompt tokens and their cache rows.  Workgroup (b, y)
 // handles positions 8 y .. 8 y + 7 of prompt b: the angles of all eight
 // tokens first (one thread per token and pair), then the query pairs of
-// every head in 16-byte pieces (to the workspace), the shared rotary key (to
-// the workspace, for the attention) and the cache rows.
+// every head in 16-byte pieces (to the workspace, in fp16), the shared rotary
+// key (to the workspace in fp16, for the attention) and the cache rows (bf16
+// or fp8, as every cache row).
 constexpr int ROPE_TOK = 8;
 
 __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
@@ -48,7 +59,7 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
     const size_t off = ((static_cast<size_t>(t_begin) + p0 + j) * H + h) * DR + 8 * v;
     u32x4 pr = *reinterpret_cast<const u32x4 *>(a.q_pe + off);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pr[e] = rope_rotate_pair(pr[e], cs[j][4 * v + e], sn[j][4 * v + e]);
+    for (int e = 0; e < 4; ++e) pr[e] = rope_rotate_pair_f16(pr[e], cs[j][4 * v + e], sn[j][4 * v + e]);
     *reinterpret_cast<u32x4 *>(a.q_rot + off) = pr;
   }
   if (tid < ntok * VEC) {
@@ -56,7 +67,7 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
     const size_t off = (static_cast<size_t>(t_begin) + p0 + j) * DR + 8 * v;
     u32x4 pr = *reinterpret_cast<const u32x4 *>(a.k_pe + off);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pr[e] = rope_rotate_pair(pr[e], cs[j][4 * v + e], sn[j][4 * v + e]);
+    for (int e = 0; e < 4; ++e) pr[e] = rope_rotate_pair_f16(pr[e], cs[j][4 * v + e], sn[j][4 * v + e]);
     *reinterpret_cast<u32x4 *>(a.k_rot + off) = pr;
   }
   for (int j = 0; j < ntok; ++j) {
@@ -81,7 +92,8 @@ __global__ __launch_bounds__(256) void transpose_wuk_kernel(const uint16_t *w, u
 }
 
 // ---- per-head up-projection of the shared latent: out[t, h, :] =
-// c[t, :] . W[h] (K = 512, N = 128; W = W_UK^T or W_UV, both [H, 512, 128]).
+// c[t, :] . W[h] (K = 512, N = 128; W = W_UK^T or W_UV, both [H, 512, 128]),
+// bf16 operands, fp32 accumulation, written in fp16.
 //
 // Workgroup: 256 tokens x one head; wave w owns tokens 64 w .. 64 w + 63 (two
 // 32-row tiles) and all four 32-column tiles, so every weight fragment read
@@ -186,7 +198,7 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
       for (int i = 0; i < 16; ++i) {
         const int row = ar0 - (l & 31) + 32 * m + (i >> 2) * 8 + hb * 4 + (i & 3), col = 32 * n + r;
         *reinterpret_cast<uint16_t *>(ring + row * (DV * 2) + (((col >> 3) ^ (row & 15)) << 4) + 2 * (col & 7)) =
-            bf16_bits(to_bf16(acc[m][n][i]));
+            f16_bits(acc[m][n][i]);
       }
   __syncthreads();
 #pragma unroll
@@ -201,7 +213,7 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
 // ---- causal attention, one head and 128 query rows per workgroup.
 //
 // Four waves of 32 query rows each; keys in blocks of 32, staged in LDS and
-// shared by the four waves.  Both products are v_mfma_f32_32x32x16_bf16 with
+// shared by the four waves.  Both products are v_mfma_f32_32x32x16_f16 with
 // the query rows as the 32-wide N dimension, the layout of the decode's
 // one-wave-per-SIMD kernel:
 //   scores   S^T[key, q] = K[key, 0:192] . Q^T over 12 k-steps; the query
@@ -209,7 +221,7 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
 //   softmax  on the score accumulator: lane (q row l % 32, hb = l / 32) holds
 //            keys pi(8 (i / 4) + 4 hb + i % 4) of register i
 //   values   O^T[d, q] += V^T[d, key] . P^T[key, q]; registers 8 t .. 8 t + 7
-//            of the score accumulator, rounded to bf16, are the B operand of
+//            of the score accumulator, rounded to fp16, are the B operand of
 //            key step t as they stand (keys stored in natural order, the
 //            MFMA's K-row m reading key pi(m))
 // A block is three XOR-swizzled regions filled by 16-byte global->LDS copies
@@ -229,7 +241,7 @@ constexpr int FA_KR = FA_KB * DR * 2;           // 4 KB: rotary part of K
 constexpr int FA_VB = FA_KB * DV * 2;           // 8 KB: V
 constexpr int FA_BUF = FA_KN + FA_KR + FA_VB;   // 20 KB per block
 constexpr int FA_CPW = FA_BUF / 1024 / 4;       // 5 copies per wave per block
-constexpr float FA_SLACK = 16.0f;               // lazy rescale margin (log2 units)
+constexpr float FA_SLACK = 8.0f;                // lazy rescale margin (log2 units): P <= 2^8 in fp16
 static_assert(FA_Q * DV * 2 <= 3 * FA_BUF, "the output tile is staged in the block ring");
 
 __device__ __forceinline__ int fa_pi(int m) {
@@ -301,15 +313,28 @@ void prefill_attention_kernel(PrefillArgs a) {
     }
   };
 
-  // query fragments: lane (q row, hb) holds dims 16 ks + 8 hb .. + 8
-  bf16x8 qf[FA_KS];
+  // query fragments: lane (q row, hb) holds dims 16 ks + 8 hb .. + 8; the
+  // bf16 q_nope converts to half (exact inside half's range), the rotated
+  // part is already half
+  f16x8 qf[FA_KS];
   {
     const size_t th = (static_cast<size_t>(t_begin) + min(qi, L - 1)) * H + h;
 #pragma unroll
     for (int ks = 0; ks < FA_KS; ++ks) {
       const uint16_t *src = ks < DNOPE / 16 ? a.q_nope + th * DNOPE + 16 * ks + 8 * hb
                                             : a.q_rot + th * DR + 16 * (ks - DNOPE / 16) + 8 * hb;
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src));
+      const u32x4 raw = *reinterpret_cast<const u32x4 *>(src);
+      if (ks < DNOPE / 16) {
+        f16x8 h8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h8[2 * e] = static_cast<_Float16>(__uint_as_float(raw[e] << 16));
+          h8[2 * e + 1] = static_cast<_Float16>(__uint_as_float(raw[e] & 0xFFFF0000u));
+        }
+        qf[ks] = h8;
+      } else {
+        qf[ks] = __builtin_bit_cast(f16x8, raw);
+      }
     }
     // Wait for the query here, before any block copy is issued: the
     // compiler does not see the copies (inline asm) and would otherwise
@@ -351,8 +376,8 @@ void prefill_attention_kernel(PrefillArgs a) {
 #pragma unroll
     for (int ks = 0; ks < FA_KS; ++ks) {
       const int off = ks < DNOPE / 16 ? (kn_off ^ (32 * ks)) : (kr_off ^ (32 * (ks - DNOPE / 16)));
-      const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(buf + off);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qf[ks], s, 0, 0, 0);
+      const f16x8 kr = *reinterpret_cast<const f16x8 *>(buf + off);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kr, qf[ks], s, 0, 0, 0);
     }
     // causal mask: key kb * 32 + tok(i) is visible to query qi while <= qi
     const int lim = qi - kb * FA_KB - 16 * hb;                // visible while tok - 16 hb <= lim
@@ -375,14 +400,14 @@ void prefill_attention_kernel(PrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < DV / 32; ++j) o[j] *= alpha;
     }
-    bf16x8 p[2];
+    f16x8 p[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i >> 3][i & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m_run)));
-    const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    for (int i = 0; i < 16; ++i)
+      p[i >> 3][i & 7] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m_run)));
+    const f16x2 one2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[i >> 2][2 * (i & 3)], p[i >> 2][2 * (i & 3) + 1]}, one2,
-                                              l_run, false);
+      l_run = __builtin_amdgcn_fdot2(f16x2{p[i >> 2][2 * (i & 3)], p[i >> 2][2 * (i & 3) + 1]}, one2, l_run, false);
     // values
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -391,8 +416,8 @@ void prefill_attention_kernel(PrefillArgs a) {
         const uint8_t *r0 = buf + v_off + 2 * t * (DV * 2) + 64 * (j ^ d);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)r0);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(r0 + DV * 2));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[t], o[j], 0, 0, 0);
+        const f16x8 vf = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, p[t], o[j], 0, 0, 0);
       }
     }
   }

@@ -69,6 +69,15 @@ __device__ __forceinline__ uint32_t rope_rotate_pair(uint32_t pr, float c, float
   return static_cast<uint32_t>(bf16_bits(to_bf16(y1))) | (static_cast<uint32_t>(bf16_bits(to_bf16(y2))) << 16);
 }
 
+// The same rotation with the result rounded to IEEE half instead (the
+// explicit-form prefill keeps its attention operands in fp16).
+__device__ __forceinline__ uint32_t rope_rotate_pair_f16(uint32_t pr, float c, float s) {
+  const float x1 = bf16_to_f32(pr & 0xFFFFu), x2 = bf16_to_f32(pr >> 16);
+  const float y1 = x1 * c - x2 * s;
+  const float y2 = x1 * s + x2 * c;
+  return static_cast<uint32_t>(f16_bits(y1)) | (static_cast<uint32_t>(f16_bits(y2)) << 16);
+}
+
 // Query pair i of (b, h): q[b, h, 512 + 2i .. 512 + 2i + 1] = RoPE(q_pe[b, h]).
 __device__ __forceinline__ uint32_t rope_query_load(const RopeAppendArgs &a, int b, int h, int i) {
   return *reinterpret_cast<const uint32_t *>(a.q_pe + (static_cast<size_t>(b) * a.H + h) * DR + 2 * i);

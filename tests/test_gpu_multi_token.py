@@ -3,9 +3,10 @@ among themselves) against the fp64 oracle, and against single-token decodes
 of the matching virtual sequences.
 
 Tolerances are those of the single-token decode: |gpu - ref| <= 2e-3 +
-2e-2 |ref| (bf16 cache) or 2e-3 + 6e-2 |ref| (fp8 cache), widened by the
-bf16 rounding of the softmax weights (2^-8 sum_t p_t |c_t|) for the
-synthetic edge cases whose outputs can cancel to tiny values.
+2e-2 |ref| (bf16 cache) or 2e-3 + 6e-2 |ref| (fp8 cache).  The full-size
+workload is held to that bound as stated; the synthetic ragged edge cases
+(a few N(0,1) rows whose weighted sums can cancel to tiny values) add the
+bf16 rounding of the softmax weights, 2^-8 sum_t p_t |c_t|.
 """
 import numpy as np
 import pytest
@@ -60,8 +61,9 @@ def run_virtual(w, qm, split_tokens):
     return o.view(B, q_len, H, 512), lse.view(B, q_len, H)
 
 
-def check_multi(w, qm, o, lse, pairs):
-    """pairs: (b, heads); every query token j of the sequence is checked."""
+def check_multi(w, qm, o, lse, pairs, widen=True):
+    """pairs: (b, heads); every query token j of the sequence is checked.
+    widen=False holds o_latent to the stated bound with nothing added."""
     fp8 = w["kv_dtype"] == synth.KV_FP8
     tol = (FP8_ATOL, FP8_RTOL) if fp8 else (BF16_ATOL, BF16_RTOL)
     q_len = qm.shape[1]
@@ -82,7 +84,8 @@ def check_multi(w, qm, o, lse, pairs):
             q = oracle.bf16_to_f64(qm[b, j])[heads]
             _, _, mag = oracle.decode_absorbed(q[:, :512], q[:, 512:], c[:n], kr[:n], w["scale"],
                                                with_magnitude=True)
-            assert_close(got[j], ref_o[j], *tol, extra=P_ROUNDING * mag, what=f"o_latent b={b} j={j} S={S}")
+            extra = P_ROUNDING * mag if widen else 0.0
+            assert_close(got[j], ref_o[j], *tol, extra=extra, what=f"o_latent b={b} j={j} S={S}")
             lse_extra = 0.0
             if fp8:   # expansion to bf16 moves each score by at most scale 2^-9 sum |q||c|
                 lse_extra = 1.01 * w["scale"] * 2.0 ** -9 * (np.abs(q[:, :512]) @ np.abs(c[:n]).T).max(axis=1)
@@ -143,14 +146,15 @@ def test_multi_token_single_is_the_decode():
 
 def test_multi_token_full_size():
     """Two new tokens per sequence on the 32 x 4096-token, 128-head workload
-    in the planner's launch configuration: sampled rows against the oracle,
+    in the planner's launch configuration: every head of both tokens of four
+    sequences against the oracle at the stated bf16 bound (nothing added),
     and every row against the virtual-sequence decodes for the same chunking."""
     w = synth.workload(2)
     B, H = w["B"], w["H"]
     qm = synth.multi_token_query(600, B, 2, H)
     o, lse = run_multi(w, qm)
     assert not torch.isnan(o.float()).any().item()
-    check_multi(w, qm, o, lse, [(0, [0, 127]), (17, [64]), (31, [5, 90])])
+    check_multi(w, qm, o, lse, [(b, range(H)) for b in (0, 9, 17, 31)], widen=False)
     split = mla.mla_decode_split_tokens(B, 2 * H, int(w["seq_lens"].max()))
     o2, l2 = run_virtual(w, qm, split_tokens=split)
     assert torch.equal(o.float(), o2.float()) and torch.equal(lse, l2)

@@ -231,11 +231,14 @@ def test_decode_workload1_all_heads():
         check_decode(w, o, lse, [(b, range(w["H"])) for b in range(w["B"])])
 
 
-def test_decode_workload2_sampled():
+def test_decode_workload2_all_pairs():
+    """The DeepSeek-V3-shaped decode (32 sequences x 4096 tokens, 128 heads) in
+    the benchmark's launch configuration: every (sequence, head) pair against
+    the oracle at the stated bf16 bound, nothing added to it."""
     w = synth.workload(2)
-    o, lse = run_decode(w, split_tokens=0)          # the benchmark's launch configuration
+    o, lse = run_decode(w, split_tokens=0)
     assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
-    check_decode(w, o, lse, [(0, [0, 1, 15, 16, 77, 127]), (13, [3, 64, 100]), (31, [31, 32, 126])])
+    check_decode(w, o, lse, [(b, range(w["H"])) for b in range(w["B"])])
 
 
 def test_decode_workload3_split256():
@@ -287,7 +290,7 @@ def test_decode_without_lse_and_all_empty():
 def test_decode_long_sequence_many_splits():
     w = synth.gaussian_workload(41, B=1, H=128, seq_lens=[140000])
     o, lse = run_decode(w, split_tokens=0)
-    check_decode(w, o, lse, [(0, [0, 9, 127])], p_rounding_term=True)
+    check_decode(w, o, lse, [(0, range(128))])
 
 
 def test_decode_page_permutation_bit_identical():
@@ -424,11 +427,12 @@ def test_decode_ignores_rows_past_the_end(kv_dtype):
 
 def test_decode_fp8_full_size():
     """Workload 4 (B=128, 8192 tokens, fp8 cache, 688 MB) in the planner's
-    launch configuration; sampled sequences against the oracle."""
+    launch configuration: every head of 12 sequences spread over the batch
+    against the oracle at the fp8 bound 2e-3 + 6e-2 |ref|, nothing added."""
     w = synth.workload(4)
     o, lse = run_decode(w, split_tokens=0)
     assert not torch.isnan(o.float()).any().item()
-    check_decode(w, o, lse, [(0, [0, 1, 127]), (63, [64]), (127, [5, 126])], p_rounding_term=True)
+    check_decode(w, o, lse, [(b, range(w["H"])) for b in (0, 1, 15, 31, 32, 63, 64, 77, 95, 100, 126, 127)])
 
 
 def test_decode_repeatable():
@@ -458,7 +462,7 @@ def run_step(w):
 
 @pytest.mark.parametrize("cfg,pairs", [
     (1, [(b, range(16)) for b in range(8)]),
-    (2, [(0, [0, 127]), (17, [5, 64]), (31, [100])]),
+    (2, [(0, range(128)), (17, [5, 64]), (31, range(128))]),
 ])
 def test_full_step(cfg, pairs):
     w = synth.workload(cfg)

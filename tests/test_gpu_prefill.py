@@ -1,7 +1,8 @@
 """GPU parity of the explicit-form prefill (mla_prefill) against the fp64
-oracle: outputs within the bf16 bound |gpu - ref| <= 2e-3 + 2e-2 |ref|,
-widened by 2^-8 sum_i p_i |V_i| (the bf16 rounding of the softmax weights
-and of the materialised per-head values, 2^-9 each); the cache rows the
+oracle: outputs within the bf16 bound |gpu - ref| <= 2e-3 + 2e-2 |ref|
+(the 4 x 1024-token, 128-head shape exactly so; the ragged synthetic prompts
+add 2^-8 sum_i p_i |V_i|, the bf16 rounding of the softmax weights and of
+the materialised per-head values, 2^-9 each); the cache rows the
 prompts leave: latent copies and fp8 codes/scales bit for bit, rotated keys
 within the bf16 bound."""
 import numpy as np
@@ -37,7 +38,7 @@ def run_prefill(w):
     return o, pool
 
 
-def check_prefill(w, o, pool, pairs, rows_for=()):
+def check_prefill(w, o, pool, pairs, rows_for=(), widen=True):
     fp8 = w["kv_dtype"] == synth.KV_FP8
     for b, heads in pairs:
         heads = list(heads)
@@ -46,7 +47,7 @@ def check_prefill(w, o, pool, pairs, rows_for=()):
             continue
         ref, rows, mag = oracle.reference_prefill(w, b, heads, with_magnitude=True)
         got = bf16_tensor_to_f64(o[t0:t1][:, heads])
-        assert_close(got, ref, extra=P_ROUNDING * mag, what=f"o prompt b={b} L={t1 - t0}")
+        assert_close(got, ref, extra=P_ROUNDING * mag if widen else 0.0, what=f"o prompt b={b} L={t1 - t0}")
         if b not in rows_for:
             continue
         for pos in range(t1 - t0):
@@ -90,11 +91,12 @@ def test_prefill_rows_untouched_elsewhere():
 
 def test_prefill_long_prompts_full_heads():
     """Four 1024-token prompts with DeepSeek-V3's 128 heads (the benchmark's
-    prefill shape): sampled heads and every token of two prompts."""
+    prefill shape): every token of 16 heads of two prompts at the stated bf16
+    bound, nothing added."""
     w = synth.prefill_workload(720, 128, [1024] * 4)
     o, pool = run_prefill(w)
     assert not torch.isnan(o.float()).any().item()
-    check_prefill(w, o, pool, [(0, [0, 77]), (3, [127])])
+    check_prefill(w, o, pool, [(0, range(0, 128, 9)), (3, range(4, 128, 8))], widen=False)
 
 
 def test_prefill_long_ragged_prompt():
