@@ -53,7 +53,8 @@ enum {
   MLA_ERR_INVALID_ARGUMENT = -1,  /* null/misaligned pointer, non-positive or inconsistent size */
   MLA_ERR_UNSUPPORTED = -2,       /* a size the kernels are not built for (d_c != 512, ...) */
   MLA_ERR_WORKSPACE_TOO_SMALL = -3,
-  MLA_ERR_LAUNCH = -4             /* the HIP runtime rejected a kernel launch */
+  MLA_ERR_LAUNCH = -4,            /* the HIP runtime rejected a kernel launch */
+  MLA_ERR_SCRATCH_TOO_SMALL = -5  /* request exceeds the library's fixed scratch buffer */
 };
 
 /* Latent-cache storage formats. */
@@ -203,6 +204,32 @@ int mla_decode_paged(const void *q, const void *kv_cache, int kv_dtype,
                      int block_size, float softmax_scale, int split_tokens,
                      void *workspace, size_t workspace_bytes,
                      void *o_latent, float *lse, int B, int H, void *stream);
+
+/* Bytes of the fixed device scratch buffer behind mla_decode_paged_noalloc. */
+#define MLA_NOALLOC_SCRATCH_BYTES (72u << 20)
+
+/*
+ * mla_decode_paged without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, arithmetic, kernels and
+ * results as mla_decode_paged; the split-KV partials go to a file-scope
+ * device array of MLA_NOALLOC_SCRATCH_BYTES (72 MiB; holds the partials of
+ * 128 heads x 128 chunks x 4 sequences or 8 chunks x 32 sequences) that
+ * each GPU the library runs on keeps until the process ends.  The call
+ * allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ * Every call on one GPU shares that GPU's buffer and leaves its partials
+ * there; nothing in it needs to start at zero.  Calls that overlap on one
+ * GPU (concurrent streams, or host threads) race on it: order them on one
+ * stream.  Errors: as mla_decode_paged, plus MLA_ERR_SCRATCH_TOO_SMALL when
+ * the partials, mla_decode_workspace_bytes(B, H, max_seq_len,
+ * split_tokens), exceed the buffer (nothing is launched); MLA_ERR_LAUNCH if
+ * the buffer's device address cannot be obtained.
+ */
+int mla_decode_paged_noalloc(const void *q, const void *kv_cache, int kv_dtype,
+                             const int32_t *block_table, int max_blocks_per_seq,
+                             const int32_t *seq_lens, int max_seq_len, int num_blocks,
+                             int block_size, float softmax_scale, int split_tokens,
+                             void *o_latent, float *lse, int B, int H, void *stream);
 
 /* Most new tokens per sequence that mla_decode_paged_multi takes. */
 #define MLA_MAX_Q_LEN 32

@@ -22,7 +22,7 @@ __all__ = [
     "mla_absorb_q", "mla_rope_append_cache", "mla_decode_paged", "mla_absorb_out",
     "mla_decode_workspace_bytes", "mla_decode_split_tokens", "mla_decode_partial", "mla_decode_combine",
     "mla_decode_combine_absorb_out", "mla_absorb_q_rope_append", "mla_decode_paged_multi", "MAX_Q_LEN",
-    "mla_prefill", "mla_prefill_workspace_bytes",
+    "mla_prefill", "mla_prefill_workspace_bytes", "mla_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 KV_BF16 = 0
@@ -30,12 +30,14 @@ KV_FP8_E4M3 = 1
 D_C, D_R, D_NOPE, D_V, BLOCK_SIZE = 512, 64, 128, 128, 64
 FP8_ROW_BYTES = 656
 MAX_Q_LEN = 32
+NOALLOC_SCRATCH_BYTES = 72 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size or format",
-           -3: "workspace too small", -4: "kernel launch failed"}
+           -3: "workspace too small", -4: "kernel launch failed",
+           -5: "request exceeds the fixed scratch buffer"}
 
 
 class MLAError(RuntimeError):
@@ -81,6 +83,9 @@ def lib():
     L.mla_decode_paged.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
                                    vp, c_size, vp, vp, c_int, c_int, vp]
     L.mla_decode_paged.restype = c_int
+    L.mla_decode_paged_noalloc.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
+                                           vp, vp, c_int, c_int, vp]
+    L.mla_decode_paged_noalloc.restype = c_int
     L.mla_decode_paged_multi.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
                                          vp, c_size, vp, vp, c_int, c_int, c_int, vp]
     L.mla_decode_paged_multi.restype = c_int
@@ -219,6 +224,25 @@ def mla_decode_paged(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, 
         _ptr(q), _ptr(kv_cache), int(kv_dtype), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
         int(max_seq_len), kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(split_tokens),
         _ptr(workspace), ws_bytes, _ptr(o_latent), _ptr(lse), B, H, _stream(stream)))
+
+
+def mla_decode_paged_noalloc(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, softmax_scale, o_latent,
+                             lse=None, split_tokens=0, stream=None):
+    """mla_decode_paged with the split-KV partials in the library's fixed device
+    scratch buffer (NOALLOC_SCRATCH_BYTES per GPU): nothing is allocated, here
+    or in the library.  Calls that overlap on one GPU race on that buffer."""
+    B, H, _ = q.shape
+    _dense(q, "q", torch.bfloat16)
+    _dense(o_latent, "o_latent", torch.bfloat16)
+    _dense(kv_cache, "kv_cache")
+    _dense(block_table, "block_table", torch.int32)
+    _dense(seq_lens, "seq_lens", torch.int32)
+    if lse is not None:
+        _dense(lse, "lse", torch.float32)
+    _check("mla_decode_paged_noalloc", lib().mla_decode_paged_noalloc(
+        _ptr(q), _ptr(kv_cache), int(kv_dtype), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+        int(max_seq_len), kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(split_tokens),
+        _ptr(o_latent), _ptr(lse), B, H, _stream(stream)))
 
 
 def mla_decode_paged_multi(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, softmax_scale, o_latent,

@@ -7,8 +7,14 @@
 #include "mla.h"
 
 #include <cmath>
+#include <mutex>
 #include "common.h"
 #include "kernels.h"
+
+// Fixed split-KV scratch of mla_decode_paged_noalloc (one copy per GPU).
+// Host code never uses this name as an address: it is a host-side stand-in;
+// the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -63,6 +69,7 @@ const char *mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "unsupported size or format";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MLA_ERR_LAUNCH: return "kernel launch failed";
+    case MLA_ERR_SCRATCH_TOO_SMALL: return "request exceeds the fixed scratch buffer";
     default: return "unknown status";
   }
 }
@@ -238,6 +245,53 @@ int mla_decode_paged(const void *q, const void *kv_cache, int kv_dtype, const in
   const hipError_t e = mla::launch_decode(a, s);
   if (e != hipSuccess || a.direct) return status_of(e);
   return status_of(mla::launch_combine(a, s));
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device with that device current.
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MLA_ERR_LAUNCH;
+  if (dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MLA_ERR_LAUNCH;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_paged_noalloc(const void *q, const void *kv_cache, int kv_dtype, const int32_t *block_table,
+                             int max_blocks_per_seq, const int32_t *seq_lens, int max_seq_len, int num_blocks,
+                             int block_size, float softmax_scale, int split_tokens, void *o_latent, float *lse,
+                             int B, int H, void *stream) {
+  // The partials this request needs, against the fixed buffer (host arithmetic only).
+  if (B >= 1 && H >= 1 && max_seq_len > 0 && split_tokens >= 0 && split_tokens % MLA_BLOCK_SIZE == 0 &&
+      split_tokens <= MLA_MAX_SPLIT_TOKENS) {
+    const int split = split_tokens ? split_tokens : plan_split(B, H, max_seq_len);
+    const int n_splits = (max_seq_len + split - 1) / split;
+    if (n_splits > 1 && workspace_for(B, H, n_splits) > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_SCRATCH_TOO_SMALL;
+  }
+  void *ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != MLA_OK) return st;
+  return mla_decode_paged(q, kv_cache, kv_dtype, block_table, max_blocks_per_seq, seq_lens, max_seq_len, num_blocks,
+                          block_size, softmax_scale, split_tokens, ws, MLA_NOALLOC_SCRATCH_BYTES, o_latent, lse, B, H,
+                          stream);
 }
 
 int mla_decode_paged_multi(const void *q, const void *kv_cache, int kv_dtype, const int32_t *block_table,
