@@ -648,19 +648,44 @@ struct DecoderSolo {
     for (int j = 0; j < NT; ++j) o[j] = f32x16{};
   }
 
-  // Query fragments (32x32x16 B operand): lane (head l % 32, hb = l / 32)
-  // holds dims 16 ks + 8 hb + [0, 8).
-  __device__ __forceinline__ void load_q() {
-    const int l = threadIdx.x & 63, head = head_of(l);
-    const bool ok = head < a.H;
-    const uint16_t *qp = a.q + (static_cast<size_t>(b) * a.H + (ok ? head : 0)) * DROW + (l >> 5) * 8;
+  // Query through LDS.  Read straight into the MFMA layout, every query load
+  // would touch 32 head rows (32 bytes of each), and the 36 loads of a wave
+  // would fetch each 128-byte line four times.  Instead each wave copies its
+  // 32 heads' rows (36 KB, contiguous in q) into LDS with whole-1 KB copies,
+  // then reads its fragments from there.  Staging layout: 16-byte chunk c of
+  // row r (head of the workgroup) at chunk position 72 (r - row0) +
+  // (c ^ qs(r)), qs(r) = (r >> 1) & 7, so a fragment read (16 rows at one
+  // chunk index) meets 16 distinct bank quads.  Rows past H re-read row
+  // H - 1.  row0 is the first row the staging area holds (waves stage in two
+  // halves of 64 rows, 73,728 bytes).
+  static constexpr int Q_CHUNKS = DROW / 8;                     // 72 chunks of 16 bytes per row
+  static constexpr int Q_WAVE_BYTES = 32 * DROW * 2;            // 36,864: one wave's heads
+  static constexpr int Q_COPIES = Q_WAVE_BYTES / 1024;          // 36 copies per wave
+  __device__ __forceinline__ static int qs(int r) { return (r >> 1) & 7; }
+  __device__ __forceinline__ void load_q_lds(uint8_t *stage, int row0) {
+    const int l = threadIdx.x & 63;
+    const uint8_t *rows = reinterpret_cast<const uint8_t *>(a.q + (static_cast<size_t>(b) * a.H + grp * HEADS) * DROW);
+    const int last = min(HEADS, a.H - grp * HEADS) - 1;
+    const uint32_t dst = lds_addr(stage) + (wave * 32 - row0) * (DROW * 2);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = *reinterpret_cast<const u32x4 *>(qp + ks * 16);
-      if (!ok) v = u32x4{0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    for (int k = 0; k < Q_COPIES; ++k) {
+      const int pos = wave * (Q_WAVE_BYTES / 16) + 64 * k + l;   // chunk position of row 0-based staging
+      const int r = pos / Q_CHUNKS, c = (pos - r * Q_CHUNKS) ^ qs(r);
+      dma16_s(static_cast<uint32_t>(min(r, last) * (DROW * 2) + c * 16), rows,
+              __builtin_amdgcn_readfirstlane(dst + 1024 * k));
     }
   }
+  // Fragments from the staging area (after this wave's copies have landed).
+  __device__ __forceinline__ void read_q_lds(const uint8_t *stage, int row0) {
+    const int l = threadIdx.x & 63;
+    const int r = wave * 32 + (l & 31), hb = l >> 5;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = 2 * ks + hb;
+      qf[ks] = *reinterpret_cast<const bf16x8 *>(stage + 16 * ((r - row0) * Q_CHUNKS + (c ^ qs(r))));
+    }
+  }
+
 
   __device__ __forceinline__ int page_of(int blk) const {
     return ((const_i32 *)bt_row)[(t_begin + blk * TB) >> 6];
@@ -1244,15 +1269,20 @@ void decode_bf16_kernel(DecodeArgs a) {
 #undef MLA_STEP_Y
 #undef MLA_WAIT_BLOCK
 
-// One-wave-per-SIMD decoder.  Iteration i (scores of block i already in s):
-// [wait own copies of i + 1] barrier [copy i + 3 into the slot of i - 1]
-// [softmax i] [scores i + 1] [values i]; the last block is peeled off the
+// One-wave-per-SIMD decoder.
+// Prologue: the query rows go through the slot ring (whole-row copies, then
+// the fragments) in two halves while blocks 0 and 1 are copied into the
+// other half of the ring; then block 2.
+// Iteration i (scores of block i already in s): [wait own copies of i + 1]
+// barrier [scores i + 1 with the softmax of i] [rescale] [values i with the
+// copies of i + 3 into the slot of i - 1]; the last block is peeled off the
 // loop.  The barrier makes block i + 1 visible and certifies that every wave
-// is done with block i - 1.  Slot of block i: i % 4.
+// is done with block i - 1.  Slot of block i: (i + 2) % 4.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void decode_solo_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSLOT * S_SLOT];
   static_assert(DecoderSolo::HEADS * LAT_BYTES <= NSLOT * S_SLOT, "the output tile is staged in the slot ring");
+  static_assert(DecoderSolo::HEADS * DROW * 2 <= NSLOT * S_SLOT, "the query is staged in the slot ring");
 
   // One workgroup per (sequence, chunk, head group), the head groups of a
   // chunk numbered consecutively; workgroups are dealt to the 8 XCDs
@@ -1283,35 +1313,45 @@ void decode_solo_kernel(DecodeArgs a) {
     return;
   }
 
+  constexpr int NI = DecoderSolo::NI;
   DecoderSolo dec(a, b, split, grp, S, t_begin, t_end);
   dec.begin();
   const int nblk = (t_end - t_begin + TB - 1) / TB;
   const bool ragged = (t_end - t_begin) % TB != 0 || a.q_len > 1;
-  auto slot = [&](int i) { return ring + (i & (NSLOT - 1)) * S_SLOT; };
-  // Block 0's copies, the query and blocks 1 and 2 all go out at once; the
-  // first wait covers block 0 and the query only.
+  // Slot of block i: (i + 2) % 4, so that blocks 0 and 1 land in slots 2
+  // and 3 while the query rows are staged in the first 73,728 bytes (slots
+  // 0 and 1), in two halves: waves 0 and 1, then waves 2 and 3.
+  auto slot = [&](int i) { return ring + ((i + 2) & (NSLOT - 1)) * S_SLOT; };
+  const bool first_half = dec.wave < 2;
+  if (first_half) dec.load_q_lds(ring, 0);
   dec.issue(0, dec.page_of(0), slot(0));
-  dec.load_q();
   if (nblk > 1) dec.issue(1, dec.page_of(1), slot(1));
+  if (first_half) {
+    if (nblk > 1) wait_vmcnt<2 * NI>();       // the query rows (copied before blocks 0, 1)
+    else wait_vmcnt<NI>();
+    dec.read_q_lds(ring, 0);
+  }
+  barrier_lds();              // waves 0 and 1 are done with the staging area
+  if (!first_half) {
+    dec.load_q_lds(ring, 2 * 32);
+    wait_vmcnt<0>();          // the query rows, and blocks 0 and 1 (copied before them)
+    dec.read_q_lds(ring, 2 * 32);
+  }
+  barrier_lds();              // the staging area (slots 0 and 1) is free
   if (nblk > 2) dec.issue(2, dec.page_of(2), slot(2));
-  if (nblk > 2) wait_vmcnt<2 * DecoderSolo::NI>();
-  else if (nblk > 1) wait_vmcnt<DecoderSolo::NI>();
+  if (nblk > 2) wait_vmcnt<NI>();             // blocks 0 and 1
   else wait_vmcnt<0>();
-  barrier_no_fence();         // block 0 visible
+  barrier_no_fence();         // blocks 0 and 1 visible
   f32x16 s = dec.scores(slot(0));
-  // Iteration i: [wait own copies of i + 1] barrier [scores i + 1 with the
-  // softmax of i] [rescale] [values i with the copies of i + 3 into the slot
-  // of i - 1].  The barrier makes block i + 1 visible and certifies that
-  // every wave is done with block i - 1.
   int i = 0;
   for (; i + 3 < nblk; ++i) {
     const int phys = dec.page_of(i + 3);
-    wait_vmcnt<DecoderSolo::NI>();
+    wait_vmcnt<NI>();
     barrier_no_fence();
     dec.phase<true>(slot(i + 1), slot(i), s, i == 0, dec.copy_of(i + 3, phys, slot(i + 3)));
   }
   for (; i + 1 < nblk; ++i) {
-    if (i + 2 < nblk) wait_vmcnt<DecoderSolo::NI>();
+    if (i + 2 < nblk) wait_vmcnt<NI>();
     else wait_vmcnt<0>();
     barrier_no_fence();
     dec.mask_scores(s, dec.mask_limit(DecoderSolo::lane_id(), i));
@@ -1377,16 +1417,25 @@ void decode_solo_fp8_kernel(DecodeArgs a) {
   auto slot = [&](int i) { return lds + (i % 3) * S_SLOT; };
   auto stage = [&](int i) { return stage0 + (i & 1) * STAGE_BYTES; };
   constexpr int NI8 = DecoderSolo::NI8;
-  // Blocks 0 and 1 and the query go out together; block 0 is expanded first,
-  // then block 2 is requested into its stage and block 1 expanded.
+  static_assert(2 * 32 * DROW * 2 <= 2 * S_SLOT, "half of the query rows fit the first two slots");
+  // Blocks 0 and 1 go to their stages while the query rows are staged in the
+  // first 73,728 bytes (slots 0 and 1) in two halves, as in the bf16 kernel;
+  // then block 0 is expanded, block 2 requested into its stage and block 1
+  // expanded.
   dec.issue8(0, dec.page_of(0), stage(0));
-  dec.load_q();
-  if (nblk > 1) {
-    dec.issue8(1, dec.page_of(1), stage(1));
-    wait_vmcnt<NI8>();
-  } else {
-    wait_vmcnt<0>();
+  if (nblk > 1) dec.issue8(1, dec.page_of(1), stage(1));
+  if (dec.wave < 2) {
+    dec.load_q_lds(lds, 0);
+    wait_vmcnt<0>();          // the query rows, and blocks 0 and 1 (copied before them)
+    dec.read_q_lds(lds, 0);
   }
+  barrier_lds();              // waves 0 and 1 are done with the staging area
+  if (dec.wave >= 2) {
+    dec.load_q_lds(lds, 2 * 32);
+    wait_vmcnt<0>();
+    dec.read_q_lds(lds, 2 * 32);
+  }
+  barrier_lds();              // the staging area (slots 0 and 1) is free
   dec.expand8(0, stage(0), slot(0));
   if (nblk > 1) {
     if (nblk > 2) {
