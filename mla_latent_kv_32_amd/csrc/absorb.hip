@@ -377,10 +377,29 @@ void combine_absorb_out_kernel(CombineOutArgs a) {
       ncmax = max(ncmax, nv[j]);
     }
 
-    // ---- weighted sums in chunk order, VB chunks of every row per batch
-    // (the batching of combine_kernel, so the sums are the same)
+    // ---- weighted sums in the order of combine_kernel: VB chunks of every
+    // row per batch, each range of combine_range(n_splits) chunks summed in
+    // chunk order from zero (accr, zr), the range sums added in range order
+    // (acc, z) -- so the sums are the same
     float acc[RPW][8] = {};
     float z[RPW] = {};
+    float accr[RPW][8] = {};
+    float zr[RPW] = {};
+    const int R = combine_range(a.n_splits);
+    // add the range that started at chunk c (rows that have chunks there)
+    auto flush = [&](int c) {
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+        if (c < nv[j]) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[j][e] += accr[j][e];
+          z[j] += zr[j];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) accr[j][e] = 0.f;
+        zr[j] = 0.f;
+      }
+    };
     // lane LPR j + k: weight of chunk cb + k of row j
     float w_l = kl < nv_l ? expf(l0 - mx) : 0.f;
     auto accumulate = [&](const u32x4 (&v)[RPW][VB], int part) {
@@ -390,11 +409,11 @@ void combine_absorb_out_kernel(CombineOutArgs a) {
         for (int k = 0; k < VB; ++k) {
           const float wk = __builtin_bit_cast(
               float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), LPR * j + part + k));
-          z[j] += wk;
+          zr[j] += wk;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            acc[j][2 * e] += wk * __uint_as_float(v[j][k][e] << 16);
-            acc[j][2 * e + 1] += wk * __uint_as_float(v[j][k][e] & 0xFFFF0000u);
+            accr[j][2 * e] += wk * __uint_as_float(v[j][k][e] << 16);
+            accr[j][2 * e + 1] += wk * __uint_as_float(v[j][k][e] & 0xFFFF0000u);
           }
         }
       }
@@ -408,6 +427,7 @@ void combine_absorb_out_kernel(CombineOutArgs a) {
       accumulate(v0, 0);
     }
     for (int c0 = VB; c0 < ncmax; c0 += VB) {
+      if (c0 % R == 0) flush(c0 - R);
       const int part = c0 & (LPR - 1);
       if (part == 0) {
         w_l = 0.f;
@@ -424,6 +444,7 @@ void combine_absorb_out_kernel(CombineOutArgs a) {
       }
       accumulate(v, part);
     }
+    if (ncmax > 0) flush((ncmax - 1) / R * R);
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
       const int row = wave + NWAVE * j;

@@ -1589,55 +1589,76 @@ void decode_fp8_kernel(DecodeArgs a) {
 #undef MLA_STEP_Y8
 
 // Merge split-KV partials: o = sum_c w_c o_c / sum_c w_c, w_c = exp(lse_c - L),
-// L = max_c lse_c.  One 64-lane group per (sequence, head), 8 columns per
-// lane; the chunks' lse are reduced across the lanes first, then the partial
-// rows stream in groups of 8 so that 8 loads per lane are in flight.  A
-// multi-token row merges the chunks that hold tokens it sees.
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-  const int b = blockIdx.x;
-  const int head = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6);
+// L = max_c lse_c (the softmax regrouped over the chunks).  One workgroup
+// per (sequence, head) with one wave per range of combine_range(n_splits)
+// chunks: lanes hold 8 columns each, every wave requests its range's partial
+// rows 16 at a time before the maximum lse is known (fp32 sums in chunk
+// order), and wave 0 adds the range sums in order.  A long sequence's rows
+// are thus read by up to 8 waves at once.
+// A multi-token row merges the chunks that hold tokens it sees.
+__global__ __launch_bounds__(512) void combine_kernel(DecodeArgs a) {
+  __shared__ float red[7][9][64];            // range sums of waves 1..7: 8 columns and z per lane
+  const int b = blockIdx.x, head = blockIdx.y;
   const int t = threadIdx.x & 63;
-  if (head >= a.H) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
   int S = a.seq_lens[b];
   if (a.q_len > 1) S = max(0, S - (a.q_len - 1) + head / a.heads);
   const int nv = (S + a.split_tokens - 1) / a.split_tokens;
   uint16_t *dst = a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC + t * 8;
   if (nv <= 0) {
-    *reinterpret_cast<u32x4 *>(dst) = u32x4{0, 0, 0, 0};
-    if (t == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = -INFINITY;
+    if (wave == 0) {
+      *reinterpret_cast<u32x4 *>(dst) = u32x4{0, 0, 0, 0};
+      if (t == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.H + head] = -INFINITY;
+    }
     return;
   }
   const size_t stride = static_cast<size_t>(a.H);
   const float *lp = a.lse_part + static_cast<size_t>(b) * a.n_splits * stride + head;
+  const uint16_t *op = a.o_part + (static_cast<size_t>(b) * a.n_splits * stride + head) * DC + t * 8;
+  const int R = combine_range(a.n_splits);
+  const int c_begin = wave * R, c_end = min(nv, c_begin + R);
+  // The partial rows of this wave's range (16 at a time) are requested
+  // before the maximum, which only the weights need: one round trip.
+  constexpr int BATCH = 16;
   float L = -INFINITY;
-  for (int c = t; c < nv; c += 64) L = fmaxf(L, lp[c * stride]);
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) L = fmaxf(L, __shfl_xor(L, m));
   float acc[8] = {};
   float z = 0.f;
-  const uint16_t *op = a.o_part + (static_cast<size_t>(b) * a.n_splits * stride + head) * DC + t * 8;
-  for (int c0 = 0; c0 < nv; c0 += 8) {
-    u32x4 v[8];
-    float w[8];
+  for (int c0 = c_begin; c0 < c_end; c0 += BATCH) {
+    u32x4 v[BATCH];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = c0 + k;
-      if (c < nv) {
-        v[k] = *reinterpret_cast<const u32x4 *>(op + c * stride * DC);
-        w[k] = expf(lp[c * stride] - L);
-      } else {
-        v[k] = u32x4{0, 0, 0, 0};
-        w[k] = 0.f;
-      }
+    for (int k = 0; k < BATCH; ++k)
+      v[k] = c0 + k < c_end ? *reinterpret_cast<const u32x4 *>(op + (c0 + k) * stride * DC) : u32x4{0, 0, 0, 0};
+    const float lw = t < BATCH && c0 + t < c_end ? lp[(c0 + t) * stride] : -INFINITY;   // lane k: chunk c0 + k
+    if (c0 == c_begin) {
+      for (int c = t; c < nv; c += 64) L = fmaxf(L, lp[c * stride]);
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) L = fmaxf(L, __shfl_xor(L, m));
     }
+    const float wl = t < BATCH && c0 + t < c_end ? expf(lw - L) : 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      z += w[k];
+    for (int k = 0; k < BATCH; ++k) {
+      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k));
+      z += w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += w[k] * __uint_as_float(v[k][e] << 16);
-        acc[2 * e + 1] += w[k] * __uint_as_float(v[k][e] & 0xFFFF0000u);
+        acc[2 * e] += w * __uint_as_float(v[k][e] << 16);
+        acc[2 * e + 1] += w * __uint_as_float(v[k][e] & 0xFFFF0000u);
       }
+    }
+  }
+  if (W > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave - 1][e][t] = acc[e];
+      red[wave - 1][8][t] = z;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 1; w < W && w * R < nv; ++w) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += red[w - 1][e][t];
+      z += red[w - 1][8][t];
     }
   }
   const float inv = 1.0f / z;
@@ -1677,10 +1698,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
-  // one wave per (b, head): the heads of a long sequence, whose rows each
-  // stream every chunk of it, are spread over as many compute units as there
-  // are heads
-  combine_kernel<<<dim3(a.B, a.H), 64, 0, stream>>>(a);
+  // one workgroup per (b, head), one wave per range of chunks
+  const int R = combine_range(a.n_splits);
+  const int waves = (a.n_splits + R - 1) / R;
+  combine_kernel<<<dim3(a.B, a.H), 64 * waves, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -32,6 +32,18 @@ struct DecodeArgs {
   float *lse_part;              // [B, n_splits, H] fp32
 };
 
+// Split-KV combine order.  A row's partials are summed in ranges of
+// combine_range(n_splits) consecutive chunks -- each range in chunk order
+// from zero, then the range sums in range order -- so that up to 8 waves can
+// stream one row's chunks at once.  A multiple of 8 (the load batch), at
+// least 16, and at most 8 ranges.  Every combine kernel follows this order,
+// so the separate and the fused merges agree bit for bit.
+__host__ __device__ inline int combine_range(int n_splits) {
+  int r = (n_splits + 7) / 8;
+  r = (r + 7) & ~7;
+  return r < 16 ? 16 : r;
+}
+
 // Attention over each chunk; direct mode writes o_latent/lse, else partials.
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // Log-sum-exp merge of the partials into o_latent/lse.
