@@ -169,6 +169,30 @@ def absorb_q(q_nope, w_uk) -> np.ndarray:
     return np.einsum("...hn,hnc->...hc", q, w)
 
 
+def query_from_latent(c_q, w_uq, w_uk, pos, theta=10000.0, d_nope=128):
+    """Absorbed decode query from the low-rank query latent, sequential order.
+
+    [Su] Part 3 (queries pass through their own low-rank latent c'_i) and MLA
+    additional notes 1-2 (the up-projection and W_UK are applied one after the
+    other, never merged); [Riju] "Query compression is separate".  For each
+    head h, with W_UQ's output split head-major into [nope | rope] (the
+    layout reading of the configs):
+        q_h   = c_q W_UQ[:, h (d_nope + d_r) : (h + 1) (d_nope + d_r)]
+        q_lat = q_h[:d_nope] W_UK[h]            (absorb_q)
+        q_rot = RoPE(q_h[d_nope:], pos)         (rope, the query's position)
+    c_q [B, d_q], w_uq [d_q, H (d_nope + d_r)], w_uk [H, d_nope, d_c],
+    pos [B] (or scalar).  Returns (q_lat [B, H, d_c], q_rot [B, H, d_r]).
+    """
+    c_q = np.asarray(c_q, F64)
+    w_uq = np.asarray(w_uq, F64)
+    w_uk = np.asarray(w_uk, F64)
+    H = w_uk.shape[0]
+    q = (c_q @ w_uq).reshape(c_q.shape[0], H, -1)
+    q_lat = absorb_q(q[..., :d_nope], w_uk)
+    q_rot = rope(q[..., d_nope:], np.asarray(pos, F64).reshape(-1, 1), theta)
+    return q_lat, q_rot
+
+
 def absorb_out(o_lat, w_uv) -> np.ndarray:
     """o[..., h, :] = o_lat[..., h, :] W_UV[h]   (W_UV: [H, d_c, d_v]); [Su] eq:mla-mqa first line."""
     o = np.asarray(o_lat, dtype=F64)

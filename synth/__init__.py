@@ -224,20 +224,31 @@ def _projected_workload(seed, B, H, d, S, q_latent_dim=None):
         w_uq = _normal(rng, (q_latent_dim, H * (D_NOPE + D_R)), 1 / math.sqrt(q_latent_dim))
     w_uk = f32_to_bf16_bits(_normal(rng, (H, D_NOPE, D_C), 1 / math.sqrt(D_C)))
     w_uv = f32_to_bf16_bits(_normal(rng, (H, D_C, D_V), 1 / math.sqrt(D_C)))
-    prefix, new, qs = [], [], []
+    prefix, new, qs, cqs = [], [], [], []
     for b in range(B):
         x = _normal(rng, (S, d))
         rows = f32_to_bf16_bits(x @ w_kv)
         prefix.append(rows[:-1])
         new.append(rows[-1])
         xq = x[-1:]
-        q = (xq @ w_q) if q_latent_dim is None else ((xq @ w_dq) @ w_uq)
+        if q_latent_dim is None:
+            q = xq @ w_q
+        else:
+            cq = xq @ w_dq
+            cqs.append(cq[0])
+            q = cq @ w_uq
         qs.append(q.reshape(H, D_NOPE + D_R))
         del x
     q = np.stack(qs)
     q_nope = f32_to_bf16_bits(q[..., :D_NOPE])
     q_pe = f32_to_bf16_bits(q[..., D_NOPE:])
-    return _finish(rng, B, H, [S] * B, prefix, new, q_nope, q_pe, w_uk, w_uv, KV_BF16)
+    out = _finish(rng, B, H, [S] * B, prefix, new, q_nope, q_pe, w_uk, w_uv, KV_BF16)
+    if q_latent_dim is not None:
+        # the query latent c' = x W_DQ of the new token and W_UQ, rounded to
+        # bf16, for the path that starts from the query latent
+        out["c_q"] = f32_to_bf16_bits(np.stack(cqs))
+        out["w_uq"] = f32_to_bf16_bits(w_uq)
+    return out
 
 
 def gaussian_workload(seed, B, H, seq_lens, kv_dtype=KV_BF16, spare_pages=0):
@@ -324,6 +335,19 @@ def prefill_workload(seed, H, lens, kv_dtype=KV_BF16):
                 q_nope=q_nope, q_pe=q_pe, c=c, k_pe=k_pe, w_uk=w_uk, w_uv=w_uv,
                 block_table=table, num_blocks=nblocks, block_size=BLOCK, kv_dtype=kv_dtype,
                 theta=ROPE_THETA, scale=1 / math.sqrt(D_NOPE + D_R))
+
+
+def query_latent_inputs(seed, B, H, d_q=1536):
+    """Query latent c' [B, d_q] ~ N(0, 1) and W_UQ [d_q, H (d_nope + d_r)] ~
+    N(0, 1/d_q) (the 1/fan_in law of the configs), W_UK as in every builder,
+    sequence lengths U{0..40000}, all rounded to bf16: the inputs of the path
+    that starts from the query latent, at any batch and head count."""
+    rng = np.random.default_rng(seed)
+    c_q = f32_to_bf16_bits(_normal(rng, (B, d_q)))
+    w_uq = f32_to_bf16_bits(_normal(rng, (d_q, H * (D_NOPE + D_R)), 1 / math.sqrt(d_q)))
+    w_uk = f32_to_bf16_bits(_normal(rng, (H, D_NOPE, D_C), 1 / math.sqrt(D_C)))
+    seq_lens = rng.integers(0, 40000, size=B, endpoint=True).astype(np.int32)
+    return dict(B=B, H=H, c_q=c_q, w_uq=w_uq, w_uk=w_uk, seq_lens=seq_lens, theta=ROPE_THETA)
 
 
 def random_bf16(seed, shape, std=1.0):

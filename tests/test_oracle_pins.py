@@ -594,6 +594,42 @@ def test_prefill_explicit_equals_mha_form_workload0():
     np.testing.assert_allclose(rows[:, w["d_c"]:], kr, rtol=1e-13, atol=1e-15)
 
 
+# ------------------------------------- query from its low-rank latent (NEXT-4)
+def test_query_from_latent_brute_force():
+    """Loops over the definition: q_h = c' W_UQ[:, head h's columns], the
+    first d_nope entries times W_UK[h], the last d_r turned pair by pair."""
+    rng = np.random.default_rng(21)
+    B, dq, H, dn, dr, dc = 3, 5, 2, 3, 4, 6
+    c_q = _rand(B, dq, rng=rng)
+    w_uq = _rand(dq, H * (dn + dr), rng=rng)
+    w_uk = _rand(H, dn, dc, rng=rng)
+    pos = np.array([0, 7, 123])
+    theta = 100.0
+    q_lat, q_rot = oracle.query_from_latent(c_q, w_uq, w_uk, pos, theta, d_nope=dn)
+    for b in range(B):
+        for h in range(H):
+            q = [sum(c_q[b][k] * w_uq[k][h * (dn + dr) + j] for k in range(dq)) for j in range(dn + dr)]
+            lat = [sum(q[n] * w_uk[h][n][c] for n in range(dn)) for c in range(dc)]
+            np.testing.assert_allclose(q_lat[b, h], lat, rtol=1e-12, atol=1e-13)
+            for i in range(dr // 2):
+                ang = pos[b] * theta ** (-2.0 * i / dr)
+                x1, x2 = q[dn + 2 * i], q[dn + 2 * i + 1]
+                assert abs(q_rot[b, h, 2 * i] - (x1 * math.cos(ang) - x2 * math.sin(ang))) < 1e-12
+                assert abs(q_rot[b, h, 2 * i + 1] - (x1 * math.sin(ang) + x2 * math.cos(ang))) < 1e-12
+
+
+def test_query_from_latent_equals_merged_product():
+    """Sequential and merged orders reach the same q_lat in exact arithmetic
+    ([Su] MLA additional notes): c' (W_UQ_nope W_UK) to 1e-12."""
+    rng = np.random.default_rng(22)
+    B, dq, H, dn, dr, dc = 4, 24, 3, 8, 4, 16
+    c_q, w_uq, w_uk = _rand(B, dq, rng=rng), _rand(dq, H * (dn + dr), rng=rng), _rand(H, dn, dc, rng=rng)
+    q_lat, _ = oracle.query_from_latent(c_q, w_uq, w_uk, 0, d_nope=dn)
+    for h in range(H):
+        merged = w_uq[:, h * (dn + dr):h * (dn + dr) + dn] @ w_uk[h]
+        np.testing.assert_allclose(q_lat[:, h], c_q @ merged, rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------ merged vs sequential absorption (study)
 def test_merged_and_sequential_query_absorption_precision():
     """[Su] MLA additional notes 1-2 weigh merging W_UQ W_UK^T into one matrix
