@@ -74,6 +74,7 @@ enum {
 #define MLA_D_R 64         /* qk_rope_head_dim */
 #define MLA_D_NOPE 128     /* qk_nope_head_dim */
 #define MLA_D_V 128        /* v_head_dim */
+#define MLA_D_Q 1536       /* q_lora_rank: width of the query latent */
 #define MLA_BLOCK_SIZE 64  /* tokens per cache page */
 
 /* Human-readable text for a status code (static storage). */
@@ -204,6 +205,36 @@ int mla_decode_paged(const void *q, const void *kv_cache, int kv_dtype,
                      int block_size, float softmax_scale, int split_tokens,
                      void *workspace, size_t workspace_bytes,
                      void *o_latent, float *lse, int B, int H, void *stream);
+
+/*
+ * The decode query from the low-rank query latent, in one launch: the query
+ * path of Su, "The Ultimate Tug-of-War Between Cache and Performance", MLA
+ * Part 3 (queries through their own latent c'_i = x_i W_c'), with W_UK
+ * absorbed in the sequential order of MLA additional notes 1-2 (never a
+ * merged W_UQ W_UK); Riju, "Multi-Head Latent Attention vs GQA vs MQA",
+ * "Query compression is separate".  For every sequence b and head h:
+ *   q_h            = c_q[b] . w_uq[:, h (d_nope + d_r) : (h + 1) (d_nope + d_r)]
+ *   q[b,h,0:d_c]   = q_h[0:d_nope] . w_uk[h]   (fp32 accumulation; q_h enters as the
+ *                    sum of two bf16 terms, about 2^-17 relative)
+ *   q[b,h,d_c:]    = RoPE(q_h[d_nope:], seq_lens[b] - 1)    (rotated in fp32)
+ * and, when kv_new is not NULL, the new token's cache row exactly as
+ * mla_rope_append_cache writes it.
+ *   c_q         [B, d_q] bf16 query latents (d_q = 1536)
+ *   w_uq        [d_q, H (d_nope + d_r)] bf16; head h's columns are
+ *               [nope (d_nope) | rope (d_r)]
+ *   w_uk        [H, d_nope, d_c] bf16
+ *   kv_new      [B, d_c + d_r] bf16 or NULL; with NULL the block_table,
+ *               kv_cache, kv_dtype, num_blocks and max_blocks_per_seq
+ *               arguments are ignored (may be NULL / 0)
+ *   seq_lens    [B] int32, counts the new token (seq_lens[b] = 0: position 0,
+ *               no row appended)
+ *   q           [B, H, d_c + d_r] bf16 output (all 576 columns written)
+ * Errors: as mla_absorb_q_rope_append; d_q != 1536 -> MLA_ERR_UNSUPPORTED.
+ */
+int mla_query_from_latent(const void *c_q, const void *w_uq, const void *w_uk, const void *kv_new,
+                          const int32_t *seq_lens, const int32_t *block_table, int max_blocks_per_seq,
+                          void *kv_cache, int kv_dtype, int num_blocks, int block_size, float rope_theta,
+                          void *q, int B, int H, int d_q, int d_nope, int d_c, int d_r, void *stream);
 
 /* Bytes of the fixed device scratch buffer behind mla_decode_paged_noalloc. */
 #define MLA_NOALLOC_SCRATCH_BYTES (72u << 20)

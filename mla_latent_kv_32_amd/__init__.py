@@ -23,11 +23,13 @@ __all__ = [
     "mla_decode_workspace_bytes", "mla_decode_split_tokens", "mla_decode_partial", "mla_decode_combine",
     "mla_decode_combine_absorb_out", "mla_absorb_q_rope_append", "mla_decode_paged_multi", "MAX_Q_LEN",
     "mla_prefill", "mla_prefill_workspace_bytes", "mla_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "mla_query_from_latent", "D_Q",
 ]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
 D_C, D_R, D_NOPE, D_V, BLOCK_SIZE = 512, 64, 128, 128, 64
+D_Q = 1536
 FP8_ROW_BYTES = 656
 MAX_Q_LEN = 32
 NOALLOC_SCRATCH_BYTES = 72 << 20
@@ -74,6 +76,9 @@ def lib():
     L.mla_absorb_q_rope_append.argtypes = [vp, vp, vp, vp, i32p, i32p, c_int, vp, c_int, c_int, c_int, c_float,
                                            vp, c_int, c_int, c_int, c_int, c_int, vp]
     L.mla_absorb_q_rope_append.restype = c_int
+    L.mla_query_from_latent.argtypes = [vp, vp, vp, vp, i32p, i32p, c_int, vp, c_int, c_int, c_int, c_float,
+                                        vp, c_int, c_int, c_int, c_int, c_int, c_int, vp]
+    L.mla_query_from_latent.restype = c_int
     L.mla_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
     L.mla_decode_workspace_bytes.restype = c_size
     L.mla_decode_split_tokens.argtypes = [c_int, c_int, c_int]
@@ -174,6 +179,30 @@ def mla_absorb_q_rope_append(q_nope, w_uk, q_pe, kv_new, seq_lens, block_table, 
         _ptr(kv_cache), int(kv_dtype), kv_cache.shape[0], kv_cache.shape[1], float(rope_theta),
         _ptr(q), B, H, dn, w_uk.shape[2], dr, _stream(stream)))
 
+
+
+def mla_query_from_latent(c_q, w_uq, w_uk, seq_lens, rope_theta, q, kv_new=None, block_table=None, kv_cache=None,
+                          kv_dtype=KV_BF16, stream=None):
+    """q[:, :, 0:512] = bf16(c_q W_UQ_nope) . W_UK and q[:, :, 512:] = RoPE(c_q W_UQ_rope) at
+    seq_lens - 1, in one launch; with kv_new, the new tokens' cache rows as mla_rope_append_cache.
+
+    c_q [B, 1536] bf16; w_uq [1536, H*192] bf16 (per head [nope 128 | rope 64]); w_uk [H,128,512];
+    q [B,H,576] bf16 output."""
+    B, dq = c_q.shape
+    H = w_uk.shape[0]
+    for t, n in ((c_q, "c_q"), (w_uq, "w_uq"), (w_uk, "w_uk"), (q, "q")):
+        _dense(t, n, torch.bfloat16)
+    _dense(seq_lens, "seq_lens", torch.int32)
+    if kv_new is not None:
+        _dense(kv_new, "kv_new", torch.bfloat16)
+        _dense(block_table, "block_table", torch.int32)
+        _dense(kv_cache, "kv_cache")
+    _check("mla_query_from_latent", lib().mla_query_from_latent(
+        _ptr(c_q), _ptr(w_uq), _ptr(w_uk), _ptr(kv_new), _ptr(seq_lens), _ptr(block_table),
+        block_table.shape[1] if block_table is not None else 0, _ptr(kv_cache), int(kv_dtype),
+        kv_cache.shape[0] if kv_cache is not None else 0, kv_cache.shape[1] if kv_cache is not None else 0,
+        float(rope_theta), _ptr(q), B, H, dq, w_uk.shape[1], w_uk.shape[2], q.shape[2] - w_uk.shape[2],
+        _stream(stream)))
 
 def mla_decode_workspace_bytes(B, H, max_seq_len, split_tokens=0) -> int:
     return int(lib().mla_decode_workspace_bytes(B, H, max_seq_len, split_tokens))

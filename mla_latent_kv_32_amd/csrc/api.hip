@@ -142,6 +142,36 @@ int mla_absorb_q_rope_append(const void *q_nope, const void *w_uk, const void *q
                                      static_cast<hipStream_t>(stream)));
 }
 
+int mla_query_from_latent(const void *c_q, const void *w_uq, const void *w_uk, const void *kv_new,
+                          const int32_t *seq_lens, const int32_t *block_table, int max_blocks_per_seq,
+                          void *kv_cache, int kv_dtype, int num_blocks, int block_size, float rope_theta,
+                          void *q, int B, int H, int d_q, int d_nope, int d_c, int d_r, void *stream) {
+  if (!aligned16(c_q) || !aligned16(w_uq) || !aligned16(w_uk) || !aligned16(seq_lens) || !aligned16(q) || B < 1 ||
+      H < 1 || !(rope_theta > 0.0f) || !isfinite(rope_theta))
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (d_q != MLA_D_Q || d_nope != MLA_D_NOPE || d_c != MLA_D_C || d_r != MLA_D_R) return MLA_ERR_UNSUPPORTED;
+  if (H > 65535 - 8 || (B + 63) / 64 > 65535) return MLA_ERR_UNSUPPORTED;
+  mla::QueryLatentArgs qa = {};
+  if (kv_new != nullptr) {
+    // rope_args validates the append's arguments; its q_pe slot is unused here (q stands in)
+    const int st = rope_args(q, kv_new, seq_lens, block_table, max_blocks_per_seq, kv_cache, kv_dtype, num_blocks,
+                             block_size, rope_theta, q, B, H, d_c, d_r, &qa.ra);
+    if (st != MLA_OK) return st;
+  } else {
+    qa.ra.seq_lens = seq_lens;
+    for (int i = 0; i < MLA_D_R / 2; ++i)
+      qa.ra.inv_freq[i] = std::pow(static_cast<double>(rope_theta), -(2.0 * i) / static_cast<double>(MLA_D_R));
+    qa.ra.q = static_cast<uint16_t *>(q);
+    qa.ra.B = B;
+    qa.ra.H = H;
+  }
+  qa.ra.q_pe = nullptr;
+  qa.c_q = static_cast<const uint16_t *>(c_q);
+  qa.w_uq = static_cast<const uint16_t *>(w_uq);
+  qa.w_uk = static_cast<const uint16_t *>(w_uk);
+  return status_of(mla::launch_query_latent(qa, static_cast<hipStream_t>(stream)));
+}
+
 int mla_validate_paging(const int32_t *seq_lens, const int32_t *block_table, int max_blocks_per_seq,
                         int max_seq_len, int num_blocks, int block_size, int B, int32_t *bad,
                         int32_t *first_bad, void *stream) {

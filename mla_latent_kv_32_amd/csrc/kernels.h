@@ -96,6 +96,17 @@ struct RopeAppendArgs {
 };
 
 hipError_t launch_rope_append(const RopeAppendArgs &a, hipStream_t stream);
+
+// The decode query from the query latent: q[:, :, 0:512] = (c' W_UQ_nope) . W_UK,
+// q[:, :, 512:576] = RoPE(c' W_UQ_rope); ra.q_pe is unused, ra.kv_new null =
+// no cache append.
+struct QueryLatentArgs {
+  const uint16_t *c_q;          // [B, 1536]
+  const uint16_t *w_uq;         // [1536, H * 192], per head [nope 128 | rope 64]
+  const uint16_t *w_uk;         // [H, 128, 512]
+  RopeAppendArgs ra;
+};
+hipError_t launch_query_latent(const QueryLatentArgs &qa, hipStream_t stream);
 // mla_absorb_q and mla_rope_append_cache in one launch (ra.q receives both parts).
 hipError_t launch_query(const uint16_t *q_nope, const uint16_t *w_uk, const RopeAppendArgs &ra, hipStream_t stream);
 
