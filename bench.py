@@ -53,10 +53,10 @@ COPIES = 3
 # reported only while that source is unchanged.
 DECODE_TRAFFIC = {
     "sources_sha256": {
-        "mla_latent_kv_32_amd/csrc/decode.hip": "0ac224724df606869c824ae2c937ae7c480791d714b4b6d049c8c0d71d6a5cf9",
-        "mla_latent_kv_32_amd/csrc/common.h": "748cb997b4658e63c1b64bf8032fbb164e6e9bedcf880b094934b6a8c62b4bea",
+        "mla_latent_kv_32_amd/csrc/decode.hip": "8c1a4207af77eac335021e4377d5752f06d60e51212ebe8e9c3376d933cb1a5e",
+        "mla_latent_kv_32_amd/csrc/common.h": "d18c3c18be49dc19eb359d77318930af1591e7ce2c3c3d6aa6fd5fd26f9de349",
     },
-    "fetch_kib": 76216.3,
+    "fetch_kib": 76278.4,
     "write_kib": 32896.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
