@@ -82,6 +82,9 @@ def parse():
                     help="time the split-KV decode of 4 long sequences (1K-32K tokens), 128 heads, 256-token chunks")
     ap.add_argument("--fp8", action="store_true",
                     help="time the decode over the fp8 latent cache: B=128 sequences of 8192 tokens, 128 heads")
+    ap.add_argument("--fp8-mfma", action="store_true",
+                    help="with --fp8: time mla_decode_paged_fp8_mfma (both products on fp8 MFMAs over the "
+                         "stored codes) instead of the expanding decoder")
     ap.add_argument("--heads", type=int, default=128,
                     help="with --q-len: heads per token (128: the DeepSeek-V3-shaped workload; other values: "
                          "the same shape with N(0,1) entries, e.g. 16 = one GPU's share under 8-way head "
@@ -439,7 +442,19 @@ def main_cache_workload(args, cfg):
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
+    fp8_mfma = fp8 and args.fp8_mfma
+
     def step(i, ev=None):
+        if fp8_mfma:
+            # one call (decode + combine); the combine share is timed on its own below
+            if ev is not None:
+                ev[0].record(stream)
+            mla.mla_decode_paged_fp8_mfma(q, caches[i % COPIES], bt, sl, S, w["scale"], o, lse, split_tokens=split,
+                                          workspace=ws)
+            if ev is not None:
+                ev[1].record(stream)
+                ev[2].record(stream)
+            return
         if ev is not None:
             ev[0].record(stream)
         mla.mla_decode_partial(q, caches[i % COPIES], kv_dtype, bt, sl, S, w["scale"], ws, split_tokens=split)
@@ -461,6 +476,20 @@ def main_cache_workload(args, cfg):
     wall = time.perf_counter() - t0
     dec = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
     comb = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    if fp8_mfma:
+        # the same combine on the partials the last call left, timed alone;
+        # decode = call - combine
+        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda._sleep(200_000_000)
+        for e in ce:
+            e[0].record(stream)
+            mla.mla_decode_combine(ws, sl, S, o, lse, split_tokens=split)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        comb = [e[0].elapsed_time(e[1]) * 1e3 for e in ce]
+        dec = [d - c for d, c in zip(dec, comb)]
+        mla.mla_decode_paged_fp8_mfma(q, caches[0], bt, sl, S, w["scale"], o, lse, split_tokens=split, workspace=ws)
+        torch.cuda.synchronize()
     dec_us, comb_us = float(np.mean(dec)), float(np.mean(comb))
     tokens = int(w["seq_lens"].sum())
     cache_bytes = tokens * row_bytes
@@ -468,7 +497,22 @@ def main_cache_workload(args, cfg):
     gbs = cache_bytes / (dec_us * 1e-6) / 1e9                  # the decode kernel alone
     call_gbs = cache_bytes / ((dec_us + comb_us) * 1e-6) / 1e9  # decode + combine
     tflops = flops / (dec_us * 1e-6) / 1e12
-    if fp8:
+    if fp8_mfma:
+        metric = "MLA fp8-cache decode packed-latent GB/s + TFLOP/s (% roofline), H=128 B=128 ctx=8K, 1 GPU"
+        workload = ("MLA absorbed decode over an fp8 E4M3 latent cache (one fp32 scale per token and 128-group, "
+                    "bf16 rotary key), both products on fp8 MFMAs over the stored codes (two-term E4M3 query and "
+                    "weights): B=128, H=128, context 8192, 656-byte rows in [16384 pages, 64, 656]")
+        # two E4M3 terms per query and weight: 2 x 2 x 512 fp8 MACs + the 64 bf16 rotary MACs per
+        # (head, token); the fp8 MFMA time equals that of the bf16 products it replaces
+        roofline = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "hbm_achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "scope": "decode kernel = call minus the separately timed combine (HIP events on the launch "
+                             "stream); algorithmic FLOPs as for the bf16 products (2 x 1088 per head and token): "
+                             "two-term fp8 operands take as many MFMA cycles as bf16 ones, so the bf16 MFMA peak "
+                             "binds (116.8 us) before HBM (86.0 us)"}
+        dtype = "fp8_e4m3"
+    elif fp8:
         metric = "MLA fp8-cache decode packed-latent GB/s + TFLOP/s (% roofline), H=128 B=128 ctx=8K, 1 GPU"
         workload = ("MLA absorbed decode over an fp8 E4M3 latent cache (one fp32 scale per token and 128-group, "
                     "bf16 rotary key): B=128, H=128, context 8192, 656-byte rows in [16384 pages, 64, 656]")

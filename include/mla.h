@@ -262,6 +262,27 @@ int mla_decode_paged_noalloc(const void *q, const void *kv_cache, int kv_dtype,
                              int block_size, float softmax_scale, int split_tokens,
                              void *o_latent, float *lse, int B, int H, void *stream);
 
+/*
+ * mla_decode_paged for the fp8 cache (kv_dtype MLA_KV_FP8_E4M3) with both
+ * products on fp8 matrix instructions over the stored E4M3 codes, which are
+ * never expanded to bf16.  The scores and the weighted sum regroup by scale
+ * group (Riju, "Interaction with quantisation and paging", the per-group
+ * scales of the fp8 cache; Su, MLA Part 3, eq:mla-mqa):
+ *   q . k_t = sum_g sc[t,g] (q_g . code[t,g]) + q_R . kr_t,
+ *   o[g]    = sum_t (p_t sc[t,g]) code[t,g] / sum_t p_t,
+ * with the query and the weights p_t sc[t,g] each carried as two E4M3 terms
+ * (hi + lo, about bf16 precision), products accumulated in fp32.  Same
+ * arguments, outputs, split choice, workspace and errors as
+ * mla_decode_paged; results agree with it to the fp8-cache tolerance, not
+ * bit for bit.  MLA_ERR_UNSUPPORTED for a bf16 cache.
+ */
+int mla_decode_paged_fp8_mfma(const void *q, const void *kv_cache, int kv_dtype,
+                              const int32_t *block_table, int max_blocks_per_seq,
+                              const int32_t *seq_lens, int max_seq_len, int num_blocks,
+                              int block_size, float softmax_scale, int split_tokens,
+                              void *workspace, size_t workspace_bytes, void *o_latent,
+                              float *lse, int B, int H, void *stream);
+
 /* Most new tokens per sequence that mla_decode_paged_multi takes. */
 #define MLA_MAX_Q_LEN 32
 

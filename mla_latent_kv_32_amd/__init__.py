@@ -23,7 +23,7 @@ __all__ = [
     "mla_decode_workspace_bytes", "mla_decode_split_tokens", "mla_decode_partial", "mla_decode_combine",
     "mla_decode_combine_absorb_out", "mla_absorb_q_rope_append", "mla_decode_paged_multi", "MAX_Q_LEN",
     "mla_prefill", "mla_prefill_workspace_bytes", "mla_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
-    "mla_query_from_latent", "D_Q",
+    "mla_query_from_latent", "D_Q", "mla_decode_paged_fp8_mfma",
 ]
 
 KV_BF16 = 0
@@ -88,6 +88,8 @@ def lib():
     L.mla_decode_paged.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
                                    vp, c_size, vp, vp, c_int, c_int, vp]
     L.mla_decode_paged.restype = c_int
+    L.mla_decode_paged_fp8_mfma.argtypes = L.mla_decode_paged.argtypes
+    L.mla_decode_paged_fp8_mfma.restype = c_int
     L.mla_decode_paged_noalloc.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
                                            vp, vp, c_int, c_int, vp]
     L.mla_decode_paged_noalloc.restype = c_int
@@ -251,6 +253,29 @@ def mla_decode_paged(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("mla_decode_paged", lib().mla_decode_paged(
         _ptr(q), _ptr(kv_cache), int(kv_dtype), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+        int(max_seq_len), kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(split_tokens),
+        _ptr(workspace), ws_bytes, _ptr(o_latent), _ptr(lse), B, H, _stream(stream)))
+
+
+def mla_decode_paged_fp8_mfma(q, kv_cache, block_table, seq_lens, max_seq_len, softmax_scale, o_latent,
+                              lse=None, split_tokens=0, workspace=None, stream=None):
+    """mla_decode_paged over an fp8 cache ([num_blocks, 64, 656] uint8) with both
+    products on fp8 MFMAs over the stored codes (two-term E4M3 query and weights)."""
+    B, H, _ = q.shape
+    _dense(q, "q", torch.bfloat16)
+    _dense(o_latent, "o_latent", torch.bfloat16)
+    _dense(kv_cache, "kv_cache")
+    _dense(block_table, "block_table", torch.int32)
+    _dense(seq_lens, "seq_lens", torch.int32)
+    if lse is not None:
+        _dense(lse, "lse", torch.float32)
+    sp = split_tokens or mla_decode_split_tokens(B, H, max_seq_len)
+    need = mla_decode_workspace_bytes(B, H, max_seq_len, split_tokens) if max_seq_len > sp else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_decode_paged_fp8_mfma", lib().mla_decode_paged_fp8_mfma(
+        _ptr(q), _ptr(kv_cache), KV_FP8_E4M3, _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
         int(max_seq_len), kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(split_tokens),
         _ptr(workspace), ws_bytes, _ptr(o_latent), _ptr(lse), B, H, _stream(stream)))
 

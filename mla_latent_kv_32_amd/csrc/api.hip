@@ -324,6 +324,22 @@ int mla_decode_paged_noalloc(const void *q, const void *kv_cache, int kv_dtype, 
                           stream);
 }
 
+int mla_decode_paged_fp8_mfma(const void *q, const void *kv_cache, int kv_dtype, const int32_t *block_table,
+                              int max_blocks_per_seq, const int32_t *seq_lens, int max_seq_len, int num_blocks,
+                              int block_size, float softmax_scale, int split_tokens, void *workspace,
+                              size_t workspace_bytes, void *o_latent, float *lse, int B, int H, void *stream) {
+  mla::DecodeArgs a;
+  const int st = prepare_decode(DecodeMode::Paged, q, kv_cache, kv_dtype, block_table, max_blocks_per_seq,
+                                seq_lens, max_seq_len, num_blocks, block_size, softmax_scale, split_tokens,
+                                workspace, workspace_bytes, o_latent, lse, B, H, &a);
+  if (st != MLA_OK) return st;
+  if (!a.kv_fp8) return MLA_ERR_UNSUPPORTED;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = mla::launch_decode_fp8_mfma(a, s);
+  if (e != hipSuccess || a.direct) return status_of(e);
+  return status_of(mla::launch_combine(a, s));
+}
+
 int mla_decode_paged_multi(const void *q, const void *kv_cache, int kv_dtype, const int32_t *block_table,
                            int max_blocks_per_seq, const int32_t *seq_lens, int max_seq_len, int num_blocks,
                            int block_size, float softmax_scale, int split_tokens, void *workspace,

@@ -48,6 +48,9 @@ __host__ __device__ inline int combine_range(int n_splits) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // Log-sum-exp merge of the partials into o_latent/lse.
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);
+// fp8 cache only, single new token: the same chunks and partials as
+// launch_decode, with both products on fp8 MFMAs over the stored codes.
+hipError_t launch_decode_fp8_mfma(const DecodeArgs &a, hipStream_t stream);
 
 // Decode workgroup shape: 16 heads per wave (MFMA 16x16x32) and 2, 4 or 8
 // waves per workgroup.  At least two waves share a block's copies so that

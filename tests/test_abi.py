@@ -142,6 +142,22 @@ def test_fused_query_call_validates_like_its_parts():
 
 
 @needs_lib
+def test_fp8_mfma_call_validates():
+    L = mla.lib()
+    dec = L.mla_decode_paged_fp8_mfma
+
+    def call(kv=1, split=0, ws=NULL, ws_bytes=0, max_seq=256, block=64):
+        return dec(FAKE, FAKE, kv, FAKE, 4, FAKE, max_seq, 16, block, ctypes.c_float(0.07), split,
+                   ws, ws_bytes, FAKE, NULL, 2, 128, NULL)
+    assert call(kv=0, split=256) == -2        # a bf16 cache: the call is for the fp8 cache only
+    assert call(kv=5) == -1
+    assert call(split=100) == -1
+    assert call(block=32) == -2
+    assert call(max_seq=257) == -1
+    assert call(split=64, ws=FAKE, ws_bytes=1024) == -3
+
+
+@needs_lib
 def test_multi_token_call_validates():
     L = mla.lib()
     dec = L.mla_decode_paged_multi
