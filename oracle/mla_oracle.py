@@ -530,6 +530,49 @@ def prefill_explicit(q_nope, q_pe, c, k_pe, w_uk, w_uv, scale, theta=10000.0, wi
     return (o, rows, mag) if with_magnitude else (o, rows)
 
 
+def prefill_chunk_explicit(q_nope, q_pe, c, k_pe, c_prefix, kr_prefix, w_uk, w_uv, scale, theta=10000.0,
+                           with_magnitude=False):
+    """A prompt chunk that continues a cached prefix, in the explicit (MHA) form.
+
+    [Su] Part 3 MHA form (eq:mla-mha) and the causal MHA equation (query t
+    attends to keys i <= t); [Riju] "Prefill versus decode" (the prefill and
+    the decode share one cache).  The prefix's P rows are already cached:
+    c_prefix [P, d_c] and kr_prefix [P, d_r], the latter rotated at positions
+    0..P-1.  Chunk token j (q_nope [n,H,d_nope], q_pe [n,H,d_r], c [n,d_c],
+    k_pe [n,d_r], unrotated) sits at position P + j and attends to the keys at
+    positions 0..P + j:
+        K^(h) = [[c_prefix; c] W_UK[h]^T | [kr_prefix; RoPE(k_pe, P + j)]]
+        V^(h) = [c_prefix; c] W_UV[h]
+        o_j^(h) = sum_{i <= P+j} softmax_i(scale [q_nope | RoPE(q_pe, P+j)]_j . K_i^(h)) V_i^(h)
+    Returns (o [n,H,d_v], rows [n, d_c + d_r]) with the chunk's cache rows
+    [c_j | RoPE(k_pe_j, P + j)]; with_magnitude also returns sum_i p_i |V_i|.
+    """
+    q_nope = np.asarray(q_nope, F64)
+    c = np.asarray(c, F64)
+    c_prefix = np.asarray(c_prefix, F64).reshape(-1, c.shape[1])
+    P = c_prefix.shape[0]
+    n, H = q_nope.shape[:2]
+    pos = P + np.arange(n, dtype=F64)
+    kr = rope(np.asarray(k_pe, F64), pos, theta)
+    q_rot = rope(np.asarray(q_pe, F64), pos[:, None], theta)
+    c_all = np.concatenate([c_prefix, c], 0)
+    kr_all = np.concatenate([np.asarray(kr_prefix, F64).reshape(P, kr.shape[1]), kr], 0)
+    # key i is visible to chunk token j while i <= P + j
+    visible = np.arange(P + n)[None, :] <= (P + np.arange(n))[:, None]
+    o = np.zeros((n, H, np.asarray(w_uv).shape[2]))
+    mag = np.zeros_like(o)
+    for h in range(H):
+        k_h = np.concatenate([c_all @ np.asarray(w_uk[h], F64).T, kr_all], 1)
+        v_h = c_all @ np.asarray(w_uv[h], F64)
+        q_h = np.concatenate([q_nope[:, h], q_rot[:, h]], 1)
+        p, _ = softmax_lse(np.where(visible, scale * (q_h @ k_h.T), -np.inf))
+        o[:, h] = p @ v_h
+        if with_magnitude:
+            mag[:, h] = p @ np.abs(v_h)
+    rows = np.concatenate([c, kr], 1)
+    return (o, rows, mag) if with_magnitude else (o, rows)
+
+
 def reference_prefill(inp, b, heads=None, with_magnitude=False):
     """Prefill reference for prompt b of a batch from synth.prefill_workload:
     (o [T_b, h, d_v], rows [T_b, d_c + d_r][, magnitude]) by prefill_explicit

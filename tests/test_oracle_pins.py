@@ -594,6 +594,70 @@ def test_prefill_explicit_equals_mha_form_workload0():
     np.testing.assert_allclose(rows[:, w["d_c"]:], kr, rtol=1e-13, atol=1e-15)
 
 
+# ------------------------------------------ chunked prefill over a cached prefix
+def test_prefill_chunk_continues_the_whole_prompt():
+    """A prompt cut at P: its first P cache rows as the prefix and the rest as
+    the chunk give the whole prompt's outputs and rows for tokens P.. ."""
+    rng = np.random.default_rng(31)
+    T, H = 23, 2
+    qn, qp, c, kp, wuk, wuv = _tiny_prefill(rng, T, H)
+    o, rows = oracle.prefill_explicit(qn, qp, c, kp, wuk, wuv, 0.4, theta=100.0)
+    for P in [0, 1, 7, 22]:
+        oc, rc = oracle.prefill_chunk_explicit(qn[P:], qp[P:], c[P:], kp[P:], rows[:P, :10], rows[:P, 10:], wuk, wuv,
+                                               0.4, theta=100.0)
+        np.testing.assert_allclose(oc, o[P:], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(rc, rows[P:], rtol=1e-13, atol=1e-15)
+
+
+def test_prefill_chunk_brute_force():
+    """Loops over the definition with an arbitrary cached prefix: chunk token
+    j sits at position P + j (its query and key rotated there) and sees the
+    P prefix rows and chunk tokens 0..j."""
+    rng = np.random.default_rng(32)
+    P, n, H = 5, 4, 2
+    qn, qp, c, kp, wuk, wuv = _tiny_prefill(rng, n, H)
+    c_pre, kr_pre = rng.standard_normal((P, 10)), rng.standard_normal((P, 4))
+    o, rows = oracle.prefill_chunk_explicit(qn, qp, c, kp, c_pre, kr_pre, wuk, wuv, 0.3, theta=50.0)
+
+    def turn(v, pos):   # pairs (2i, 2i+1) turned by pos * 50^(-2i/d)
+        d = len(v)
+        out = []
+        for i in range(d // 2):
+            a = pos * 50.0 ** (-2.0 * i / d)
+            out += [v[2 * i] * math.cos(a) - v[2 * i + 1] * math.sin(a), v[2 * i] * math.sin(a) + v[2 * i + 1] * math.cos(a)]
+        return out
+    keys_c = list(c_pre) + list(c)
+    keys_r = [list(r) for r in kr_pre] + [turn(kp[j], P + j) for j in range(n)]
+    for j in range(n):
+        for h in range(H):
+            q = list(qn[j, h]) + turn(qp[j, h], P + j)
+            sc = []
+            for i in range(P + j + 1):
+                k = [sum(keys_c[i][m] * wuk[h, d, m] for m in range(10)) for d in range(6)] + keys_r[i]
+                sc.append(0.3 * sum(a * b for a, b in zip(q, k)))
+            z = sum(math.exp(v) for v in sc)
+            want = [sum(math.exp(sc[i]) / z * sum(keys_c[i][m] * wuv[h, m, e] for m in range(10)) for i in range(P + j + 1))
+                    for e in range(5)]
+            np.testing.assert_allclose(o[j, h], want, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(rows[j], list(c[j]) + keys_r[P + j], rtol=1e-13, atol=1e-15)
+
+
+def test_prefill_chunk_equals_mha_form_workload0():
+    """Workload 0 cut at position 40: the prefix rows of the MHA form and the
+    remaining tokens' projections reproduce the MHA form's last 24 outputs."""
+    w = synth.workload(0)
+    o, c, kr, q_nope, q_rot = oracle.prefill_mha_form(
+        w["x"], w["w_dkv"], w["w_kr"], w["w_q"], w["w_uk"], w["w_uv"], w["d_nope"], w["d_r"], w["scale"], w["theta"])
+    x = np.asarray(w["x"], np.float64)
+    q = (x @ np.asarray(w["w_q"], np.float64)).reshape(w["S"], w["H"], -1)
+    P = 40
+    oc, rows = oracle.prefill_chunk_explicit(q[P:, :, :w["d_nope"]], q[P:, :, w["d_nope"]:], c[P:],
+                                             (x @ np.asarray(w["w_kr"], np.float64))[P:], c[:P], kr[:P],
+                                             w["w_uk"], w["w_uv"], w["scale"], w["theta"])
+    np.testing.assert_allclose(oc, o[P:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(rows[:, w["d_c"]:], kr[P:], rtol=1e-13, atol=1e-15)
+
+
 # ------------------------------------- query from its low-rank latent (NEXT-4)
 def test_query_from_latent_brute_force():
     """Loops over the definition: q_h = c' W_UQ[:, head h's columns], the
