@@ -417,6 +417,49 @@ int mla_prefill(const void *q_nope, const void *q_pe, const void *c_kv, const vo
                 int num_blocks, int block_size, void *o, void *workspace, size_t workspace_bytes,
                 void *stream);
 
+/*
+ * A prefill chunk that continues a cached prefix (chunked prefill; the
+ * prefill and the decode share one cache: Riju, "Prefill versus decode"
+ * and "Interaction with quantisation and paging").  Prompt b already has
+ * P_b = prefix_lens[b] rows in the paged cache (positions 0 .. P_b - 1 of
+ * block-table row b, written by mla_prefill, mla_prefill_chunk or the
+ * decode's appends); its chunk is tokens cu_seqlens[b] .. cu_seqlens[b+1]-1
+ * of the packed inputs, token j at position P_b + j.  In the explicit form
+ * of mla_prefill (Su, Part 3, eq:mla-mha, with the causal rule of the MHA
+ * equation), for every head h
+ *   K^(h) = [[c_prefix; c] W_UK[h]^T | [kr_prefix; RoPE(k_pe, P_b + j)]],
+ *   V^(h) = [c_prefix; c] W_UV[h]
+ *   o[j,h] = sum_{i <= P_b + j} softmax_i(softmax_scale [q_nope | RoPE(q_pe, P_b + j)]_j . K_i^(h)) V_i^(h)
+ * where c_prefix, kr_prefix are the cached rows (fp8 rows dequantised as
+ * code * group scale and carried into the up-projection as two bf16 terms,
+ * within 2^-17 of the exact value), and the chunk's rows
+ * [c_j | RoPE(k_pe_j, P_b + j)] are written at positions P_b + j.
+ * Arguments as for mla_prefill, plus:
+ *   prefix_lens  [B] int32 device: cached rows per prompt
+ *   total_keys   host: sum_b (prefix_lens[b] + chunk length b), the keys the
+ *                attention materialises per head (the workspace is sized for
+ *                it; a wrong value gives unspecified results, while every
+ *                access stays inside the workspace)
+ *   max_prefix   host bound >= every prefix_lens[b], <= max_blocks_per_seq *
+ *                block_size; each prompt's prefix plus chunk must fit its
+ *                block-table row (prefix_lens[b] + chunk length b <=
+ *                max_blocks_per_seq * block_size)
+ *   workspace    mla_prefill_chunk_workspace_bytes(T, total_keys, B, H)
+ *                bytes (per-head K and V of every key: 512 bytes per key
+ *                and head)
+ * With every prefix_lens[b] = 0 the results equal mla_prefill's.  Errors as
+ * for mla_prefill.
+ */
+size_t mla_prefill_chunk_workspace_bytes(int total_tokens, int total_keys, int B, int H);
+
+int mla_prefill_chunk(const void *q_nope, const void *q_pe, const void *c_kv, const void *k_pe,
+                      const void *w_uk, const void *w_uv, const int32_t *cu_seqlens,
+                      const int32_t *prefix_lens, int B, int total_tokens, int max_seqlen,
+                      int total_keys, int max_prefix, int H, float softmax_scale, float rope_theta,
+                      const int32_t *block_table, int max_blocks_per_seq, void *kv_cache,
+                      int kv_dtype, int num_blocks, int block_size, void *o, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

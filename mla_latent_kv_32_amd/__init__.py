@@ -23,7 +23,8 @@ __all__ = [
     "mla_decode_workspace_bytes", "mla_decode_split_tokens", "mla_decode_partial", "mla_decode_combine",
     "mla_decode_combine_absorb_out", "mla_absorb_q_rope_append", "mla_decode_paged_multi", "MAX_Q_LEN",
     "mla_prefill", "mla_prefill_workspace_bytes", "mla_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
-    "mla_query_from_latent", "D_Q", "mla_decode_paged_fp8_mfma",
+    "mla_query_from_latent", "D_Q", "mla_decode_paged_fp8_mfma", "mla_prefill_chunk",
+    "mla_prefill_chunk_workspace_bytes",
 ]
 
 KV_BF16 = 0
@@ -101,6 +102,11 @@ def lib():
     L.mla_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32p, c_int, c_int, c_int, c_int, c_float, c_float,
                               i32p, c_int, vp, c_int, c_int, c_int, vp, vp, c_size, vp]
     L.mla_prefill.restype = c_int
+    L.mla_prefill_chunk_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
+    L.mla_prefill_chunk_workspace_bytes.restype = c_size
+    L.mla_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, i32p, i32p, c_int, c_int, c_int, c_int, c_int, c_int,
+                                    c_float, c_float, i32p, c_int, vp, c_int, c_int, c_int, vp, vp, c_size, vp]
+    L.mla_prefill_chunk.restype = c_int
     L.mla_decode_partial.argtypes = [vp, vp, c_int, i32p, c_int, i32p, c_int, c_int, c_int, c_float, c_int,
                                      vp, c_size, c_int, c_int, vp]
     L.mla_decode_partial.restype = c_int
@@ -356,6 +362,39 @@ def mla_prefill(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, cu_seqlens, max_seqlen, so
         int(max_seqlen), H, float(softmax_scale), float(rope_theta), _ptr(block_table), block_table.shape[1],
         _ptr(kv_cache), int(kv_dtype), kv_cache.shape[0], kv_cache.shape[1], _ptr(o), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def mla_prefill_chunk_workspace_bytes(total_tokens, total_keys, B, H) -> int:
+    return int(lib().mla_prefill_chunk_workspace_bytes(total_tokens, total_keys, B, H))
+
+
+def mla_prefill_chunk(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, cu_seqlens, prefix_lens, max_seqlen, total_keys,
+                      max_prefix, softmax_scale, rope_theta, block_table, kv_cache, kv_dtype, o, workspace=None,
+                      stream=None):
+    """Prompt chunks that continue cached prefixes (prefix_lens [B] int32 rows already cached):
+    chunk token j of prompt b at position prefix_lens[b] + j, attending to the cached rows
+    and to the chunk's tokens up to itself; writes the chunk's cache rows.  Shapes as for
+    mla_prefill; total_keys = sum_b (prefix_lens[b] + chunk length b) and max_prefix are
+    host values.  A workspace of mla_prefill_chunk_workspace_bytes(...) bytes is allocated
+    with torch when not given."""
+    T, H, _ = q_nope.shape
+    for t, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (c_kv, "c_kv"), (k_pe, "k_pe"), (w_uk, "w_uk"),
+                 (w_uv, "w_uv"), (o, "o")):
+        _dense(t, n, torch.bfloat16)
+    _dense(cu_seqlens, "cu_seqlens", torch.int32)
+    _dense(prefix_lens, "prefix_lens", torch.int32)
+    _dense(block_table, "block_table", torch.int32)
+    _dense(kv_cache, "kv_cache")
+    B = cu_seqlens.shape[0] - 1
+    if workspace is None and T > 0:
+        workspace = torch.empty(mla_prefill_chunk_workspace_bytes(T, total_keys, B, H), dtype=torch.uint8,
+                                device=q_nope.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_prefill_chunk", lib().mla_prefill_chunk(
+        _ptr(q_nope), _ptr(q_pe), _ptr(c_kv), _ptr(k_pe), _ptr(w_uk), _ptr(w_uv), _ptr(cu_seqlens),
+        _ptr(prefix_lens), B, T, int(max_seqlen), int(total_keys), int(max_prefix), H, float(softmax_scale),
+        float(rope_theta), _ptr(block_table), block_table.shape[1], _ptr(kv_cache), int(kv_dtype),
+        kv_cache.shape[0], kv_cache.shape[1], _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def mla_decode_partial(q, kv_cache, kv_dtype, block_table, seq_lens, max_seq_len, softmax_scale, workspace,

@@ -491,6 +491,77 @@ int mla_prefill(const void *q_nope, const void *q_pe, const void *c_kv, const vo
   return status_of(mla::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t mla_prefill_chunk_workspace_bytes(int total_tokens, int total_keys, int B, int H) {
+  if (total_tokens < 1 || total_keys < total_tokens || B < 1 || H < 1) return 0;
+  const size_t T = static_cast<size_t>(total_tokens), K = static_cast<size_t>(total_keys),
+               h = static_cast<size_t>(H);
+  return align256(T * h * MLA_D_R * 2) + align256(K * MLA_D_R * 2) + 2 * align256(K * h * MLA_D_NOPE * 2) +
+         align256(h * MLA_D_C * MLA_D_NOPE * 2) + align256(K * 2 * MLA_D_C * 2) +
+         align256((static_cast<size_t>(B) + 1) * sizeof(int32_t));
+}
+
+int mla_prefill_chunk(const void *q_nope, const void *q_pe, const void *c_kv, const void *k_pe, const void *w_uk,
+                      const void *w_uv, const int32_t *cu_seqlens, const int32_t *prefix_lens, int B,
+                      int total_tokens, int max_seqlen, int total_keys, int max_prefix, int H, float softmax_scale,
+                      float rope_theta, const int32_t *block_table, int max_blocks_per_seq, void *kv_cache,
+                      int kv_dtype, int num_blocks, int block_size, void *o, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(c_kv) || !aligned16(k_pe) || !aligned16(w_uk) ||
+      !aligned16(w_uv) || !aligned16(cu_seqlens) || !aligned16(prefix_lens) || !aligned16(block_table) ||
+      !aligned16(kv_cache) || !aligned16(o) || B < 1 || H < 1 || total_tokens < 0 || max_seqlen < 0 ||
+      max_prefix < 0 || total_keys < total_tokens || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      !isfinite(softmax_scale) || !(rope_theta > 0.0f) || !isfinite(rope_theta))
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_INVALID_ARGUMENT;
+  if (block_size != MLA_BLOCK_SIZE) return MLA_ERR_UNSUPPORTED;
+  const long cap = static_cast<long>(max_blocks_per_seq) * block_size;
+  if (max_prefix > cap || max_seqlen > cap) return MLA_ERR_INVALID_ARGUMENT;
+  if (B > 65535 || H > 65535 || total_keys > 2147483647 / MLA_D_C) return MLA_ERR_UNSUPPORTED;
+  if (total_tokens == 0 || max_seqlen == 0) return MLA_OK;
+  const size_t need = mla_prefill_chunk_workspace_bytes(total_tokens, total_keys, B, H);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  mla::PrefillArgs a = {};
+  a.q_nope = static_cast<const uint16_t *>(q_nope);
+  a.q_pe = static_cast<const uint16_t *>(q_pe);
+  a.c = static_cast<const uint16_t *>(c_kv);
+  a.k_pe = static_cast<const uint16_t *>(k_pe);
+  a.w_uk = static_cast<const uint16_t *>(w_uk);
+  a.w_uv = static_cast<const uint16_t *>(w_uv);
+  a.cu_seqlens = cu_seqlens;
+  a.prefix_lens = prefix_lens;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.cache = static_cast<uint8_t *>(kv_cache);
+  a.kv_fp8 = kv_dtype == MLA_KV_FP8_E4M3;
+  for (int i = 0; i < MLA_D_R / 2; ++i)
+    a.inv_freq[i] = std::pow(static_cast<double>(rope_theta), -(2.0 * i) / static_cast<double>(MLA_D_R));
+  a.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  a.B = B;
+  a.H = H;
+  a.T = total_tokens;
+  a.max_len = max_seqlen;
+  a.T_keys = total_keys;
+  a.max_prefix = max_prefix;
+  a.o = static_cast<uint16_t *>(o);
+  const size_t T = static_cast<size_t>(total_tokens), K = static_cast<size_t>(total_keys),
+               h = static_cast<size_t>(H);
+  uint8_t *p = static_cast<uint8_t *>(workspace);
+  a.q_rot = reinterpret_cast<uint16_t *>(p);
+  p += align256(T * h * MLA_D_R * 2);
+  a.k_rot = reinterpret_cast<uint16_t *>(p);
+  p += align256(K * MLA_D_R * 2);
+  a.k_nope = reinterpret_cast<uint16_t *>(p);
+  p += align256(K * h * MLA_D_NOPE * 2);
+  a.v = reinterpret_cast<uint16_t *>(p);
+  p += align256(K * h * MLA_D_NOPE * 2);
+  a.w_ukt = reinterpret_cast<uint16_t *>(p);
+  p += align256(h * MLA_D_C * MLA_D_NOPE * 2);
+  a.c_gather = reinterpret_cast<uint16_t *>(p);
+  p += align256(K * 2 * MLA_D_C * 2);
+  a.cu_keys_ws = reinterpret_cast<int32_t *>(p);
+  return status_of(mla::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
 int mla_absorb_out(const void *o_latent, const void *w_uv, void *o, int B, int H, int d_c, int d_v,
                    void *stream) {
   if (!aligned16(o_latent) || !aligned16(w_uv) || !aligned16(o) || B < 1 || H < 1)

@@ -131,12 +131,24 @@ struct PrefillArgs {
   float scale_log2;             // softmax_scale * log2(e)
   int B, H, T, max_len;
   uint16_t *o;                  // [T, H, 128]
+  // Chunks that continue a cached prefix: prompt b's P_b = prefix_lens[b]
+  // rows are already in the cache and its tokens sit at positions P_b + j.
+  // Keys (the prefix's and the prompt's own) are packed per prompt at
+  // cu_keys[b] .. cu_keys[b + 1] - 1 of the key arrays.  Without a prefix
+  // (prefix_lens null) cu_keys = cu_seqlens, c_keys = c and T_keys = T.
+  const int32_t *prefix_lens;   // [B] or null
+  const int32_t *cu_keys;       // [B + 1]
+  const uint16_t *c_keys;       // [T_keys, c_keys_w] latents of every key (bf16)
+  int c_keys_w;                 // 512, or 1024 = [hi | lo] bf16 terms (fp8 prefix rows)
+  int T_keys, max_prefix;
   // workspace (attention operands in IEEE half)
   uint16_t *q_rot;              // [T, H, 64] fp16
-  uint16_t *k_rot;              // [T, 64] fp16
-  uint16_t *k_nope;             // [T, H, 128] fp16
-  uint16_t *v;                  // [T, H, 128] fp16
+  uint16_t *k_rot;              // [T_keys, 64] fp16
+  uint16_t *k_nope;             // [T_keys, H, 128] fp16
+  uint16_t *v;                  // [T_keys, H, 128] fp16
   uint16_t *w_ukt;              // [H, 512, 128] = W_UK transposed per head
+  uint16_t *c_gather;           // [T_keys, c_keys_w] bf16 (chunks only: c_keys points here)
+  int32_t *cu_keys_ws;          // [B + 1] (chunks only: cu_keys points here)
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 

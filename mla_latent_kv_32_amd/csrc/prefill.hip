@@ -44,12 +44,27 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const int t_begin = a.cu_seqlens[b];
   const int L = a.cu_seqlens[b + 1] - t_begin;
+  const int P = a.prefix_lens ? a.prefix_lens[b] : 0;     // token j of the prompt sits at position P + j
+  const int k_begin = a.cu_keys[b] + P;                    // its key index: k_begin + j
   const int p0 = blockIdx.y * ROPE_TOK;
   if (p0 >= L) return;
   const int ntok = min(ROPE_TOK, L - p0);
   {
     const int j = tid / (DR / 2), i = tid % (DR / 2);
-    if (j < ntok) rope_cos_sin(a.inv_freq, p0 + j, i, cs[j][i], sn[j][i]);
+    if (j < ntok) rope_cos_sin(a.inv_freq, P + p0 + j, i, cs[j][i], sn[j][i]);
+  }
+  if (a.prefix_lens) {
+    // the prompt's own latents join the prefix's in the key array (exact in
+    // bf16: a second term, if the rows have one, is zero)
+    const int pieces = a.c_keys_w / 8;
+    for (int idx = tid; idx < ntok * pieces; idx += blockDim.x) {
+      const int j = idx / pieces, v = idx % pieces;
+      const int kk = min(k_begin + p0 + j, a.T_keys - 1);
+      const u32x4 val = v < DC / 8
+          ? *reinterpret_cast<const u32x4 *>(a.c + (static_cast<size_t>(t_begin) + p0 + j) * DC + 8 * v)
+          : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4 *>(a.c_gather + static_cast<size_t>(kk) * a.c_keys_w + 8 * v) = val;
+    }
   }
   __syncthreads();
   const int H = a.H;
@@ -68,14 +83,110 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
     u32x4 pr = *reinterpret_cast<const u32x4 *>(a.k_pe + off);
 #pragma unroll
     for (int e = 0; e < 4; ++e) pr[e] = rope_rotate_pair_f16(pr[e], cs[j][4 * v + e], sn[j][4 * v + e]);
-    *reinterpret_cast<u32x4 *>(a.k_rot + off) = pr;
+    const int kk = min(k_begin + p0 + j, a.T_keys - 1);
+    *reinterpret_cast<u32x4 *>(a.k_rot + static_cast<size_t>(kk) * DR + 8 * v) = pr;
   }
   for (int j = 0; j < ntok; ++j) {
-    const int pos = p0 + j;
-    const size_t t = static_cast<size_t>(t_begin) + pos;
-    const int page = a.block_table[static_cast<size_t>(b) * a.max_blocks + pos / PAGE];
+    const int pos = P + p0 + j;
+    const size_t t = static_cast<size_t>(t_begin) + p0 + j;
+    // (a position past the block-table row -- a prefix and chunk longer
+    // than the row allows, which the caller must not pass -- is clamped to
+    // the row's last page instead of reading past it)
+    const int page = a.block_table[static_cast<size_t>(b) * a.max_blocks + min(pos / PAGE, a.max_blocks - 1)];
     store_cache_row(a.cache, a.kv_fp8, static_cast<size_t>(page) * PAGE + pos % PAGE, a.c + t * DC,
                     a.k_pe + t * DR, tid, cs[j], sn[j]);
+  }
+}
+
+// ---- chunks: key offsets cu_keys[b] = sum_{b' < b} (P_b' + L_b'), one
+// workgroup (contiguous ranges per thread, then a scan of the 256 range sums).
+__global__ __launch_bounds__(256) void prefill_keys_scan_kernel(const int32_t *cu_seqlens, const int32_t *prefix,
+                                                                int32_t *cu_keys, int B) {
+  __shared__ int part[256];
+  const int tid = threadIdx.x;
+  const int per = (B + 255) / 256, b0 = tid * per, b1 = min(B, b0 + per);
+  int s = 0;
+  for (int b = b0; b < b1; ++b) s += prefix[b] + cu_seqlens[b + 1] - cu_seqlens[b];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int v = part[i];
+      part[i] = run;
+      run += v;
+    }
+    cu_keys[B] = run;
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int b = b0; b < b1; ++b) {
+    cu_keys[b] = run;
+    run += prefix[b] + cu_seqlens[b + 1] - cu_seqlens[b];
+  }
+}
+
+// ---- chunks: the cached prefix rows into the key arrays.  Workgroup (b, y)
+// handles prefix positions 8 y .. 8 y + 7 of prompt b: latent to c_gather
+// (bf16 rows as stored; fp8 rows as two bf16 terms of code * group scale,
+// hi = bf16(x) and lo = bf16(x - hi), within 2^-17 of x, so that rounding
+// the dequantised latent before the up-projection -- where the per-head
+// products could cancel far below its size -- costs nothing visible), the
+// stored rotated key to k_rot in half.
+__global__ __launch_bounds__(256) void prefill_gather_kernel(PrefillArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int P = a.prefix_lens[b];
+  const int p0 = blockIdx.y * ROPE_TOK;
+  if (p0 >= P) return;
+  const int ntok = min(ROPE_TOK, P - p0);
+  const int k_begin = a.cu_keys[b];
+  const int j = tid >> 5, lane = tid & 31;                 // 32 threads per token
+  if (j >= ntok) return;
+  const int pos = p0 + j;
+  const int page = a.block_table[static_cast<size_t>(b) * a.max_blocks + min(pos / PAGE, a.max_blocks - 1)];
+  const size_t slot = static_cast<size_t>(page) * PAGE + pos % PAGE;
+  const size_t kk = static_cast<size_t>(min(k_begin + pos, a.T_keys - 1));
+  uint16_t *cdst = a.c_gather + kk * a.c_keys_w + 16 * lane;   // 16 latent values per thread
+  const uint16_t *rope_src;
+  if (a.kv_fp8) {
+    const uint8_t *row = a.cache + slot * FP8_ROW_BYTES;
+    const u32x4 codes = *reinterpret_cast<const u32x4 *>(row + 16 * lane);
+    const float sc = *reinterpret_cast<const float *>(row + DC + 2 * DR + 4 * (lane >> 3));
+    uint16_t hi16[16], lo16[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x2 c01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes[w]), false);
+      const f32x2 c23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes[w]), true);
+      const float x[4] = {c01[0] * sc, c01[1] * sc, c23[0] * sc, c23[1] * sc};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 h = to_bf16(x[e]);
+        hi16[4 * w + e] = bf16_bits(h);
+        lo16[4 * w + e] = bf16_bits(to_bf16(x[e] - static_cast<float>(h)));
+      }
+    }
+    *reinterpret_cast<u32x4 *>(cdst) = *reinterpret_cast<const u32x4 *>(hi16);
+    *reinterpret_cast<u32x4 *>(cdst + 8) = *reinterpret_cast<const u32x4 *>(hi16 + 8);
+    *reinterpret_cast<u32x4 *>(cdst + DC) = *reinterpret_cast<const u32x4 *>(lo16);
+    *reinterpret_cast<u32x4 *>(cdst + DC + 8) = *reinterpret_cast<const u32x4 *>(lo16 + 8);
+    rope_src = reinterpret_cast<const uint16_t *>(row + DC);
+  } else {
+    const uint16_t *row = reinterpret_cast<const uint16_t *>(a.cache) + slot * DROW;
+    *reinterpret_cast<u32x4 *>(cdst) = *reinterpret_cast<const u32x4 *>(row + 16 * lane);
+    *reinterpret_cast<u32x4 *>(cdst + 8) = *reinterpret_cast<const u32x4 *>(row + 16 * lane + 8);
+    rope_src = row + DC;
+  }
+  if (lane < DR / 8) {
+    // bf16 -> half: exact for magnitudes in [2^-14, 65504]
+    const u32x4 r = *reinterpret_cast<const u32x4 *>(rope_src + 8 * lane);
+    u32x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo16 = f16_bits(__uint_as_float(r[e] << 16));
+      const uint32_t hi16 = f16_bits(__uint_as_float(r[e] & 0xFFFF0000u));
+      h[e] = lo16 | (hi16 << 16);
+    }
+    *reinterpret_cast<u32x4 *>(a.k_rot + kk * DR + 8 * lane) = h;
   }
 }
 
@@ -93,7 +204,8 @@ __global__ __launch_bounds__(256) void transpose_wuk_kernel(const uint16_t *w, u
 
 // ---- per-head up-projection of the shared latent: out[t, h, :] =
 // c[t, :] . W[h] (K = 512, N = 128; W = W_UK^T or W_UV, both [H, 512, 128]),
-// bf16 operands, fp32 accumulation, written in fp16.
+// bf16 operands, fp32 accumulation, written in fp16.  KDIM = 1024 takes rows
+// [c_hi | c_lo] against [W; W]: out = c_hi W + c_lo W in one accumulation.
 //
 // Workgroup: 256 tokens x one head; wave w owns tokens 64 w .. 64 w + 63 (two
 // 32-row tiles) and all four 32-column tiles, so every weight fragment read
@@ -107,7 +219,6 @@ __global__ __launch_bounds__(256) void transpose_wuk_kernel(const uint16_t *w, u
 constexpr int PJ_TM = 256;                      // tokens per workgroup
 constexpr int PJ_MT = PJ_TM / 4 / 32;           // 32-row tiles per wave: 2
 constexpr int PJ_KC = 32;                       // K per chunk
-constexpr int PJ_NCH = DC / PJ_KC;              // 16 chunks
 constexpr int PJ_ABYTES = PJ_TM * PJ_KC * 2;    // 16 KB
 constexpr int PJ_BBYTES = PJ_KC * DV * 2;       // 8 KB
 constexpr int PJ_STAGE = PJ_ABYTES + PJ_BBYTES;
@@ -116,8 +227,10 @@ constexpr int PJ_CPW = PJ_STAGE / 1024 / 4;     // copies per wave per chunk: 6
 static_assert(PJ_STAGE % 4096 == 0, "a chunk splits evenly over the four waves");
 static_assert(PJ_TM * DV * 2 <= 3 * PJ_STAGE, "the output tile is staged in the ring");
 
+template <int KDIM>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, int T, int H) {
+  constexpr int PJ_NCH = KDIM / PJ_KC;         // chunks of 32 along K
   __shared__ __attribute__((aligned(16))) uint8_t ring[3 * PJ_STAGE];
   const int h = blockIdx.y, t0 = blockIdx.x * PJ_TM;
   const int l = threadIdx.x & 63;
@@ -135,12 +248,12 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
         const int r = 16 * j + (l >> 2), pos = l & 3;
         const int c = pos ^ ((r >> 2) & 3);
         const size_t t = static_cast<size_t>(min(t0 + r, T - 1));
-        dma16(reinterpret_cast<const uint8_t *>(act) + t * (DC * 2) + ch * (PJ_KC * 2) + 16 * c,
+        dma16(reinterpret_cast<const uint8_t *>(act) + t * (KDIM * 2) + ch * (PJ_KC * 2) + 16 * c,
               __builtin_amdgcn_readfirstlane(st + j * 1024));
       } else {
         const int kr = 4 * (j - PJ_ACOPIES) + (l >> 4), pos = l & 15;
         const int c = pos ^ (4 * (kr & 3));
-        dma16(wh + static_cast<size_t>(ch * PJ_KC + kr) * (DV * 2) + 16 * c,
+        dma16(wh + static_cast<size_t>((ch * PJ_KC + kr) % DC) * (DV * 2) + 16 * c,
               __builtin_amdgcn_readfirstlane(st + PJ_ABYTES + (j - PJ_ACOPIES) * 1024));
       }
     }
@@ -275,12 +388,17 @@ void prefill_attention_kernel(PrefillArgs a) {
   const int L = a.cu_seqlens[b + 1] - t_begin;
   const int q0 = tile * FA_Q;
   if (q0 >= L) return;
+  // query row j of the prompt sits at position P + j and sees the keys at
+  // positions 0 .. P + j (key k of the prompt: index k_begin + k)
+  const int P = a.prefix_lens ? a.prefix_lens[b] : 0;
+  const int k_begin = a.cu_keys[b];
+  const int k_last = min(k_begin + P + L, a.T_keys) - 1;
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hb = l >> 5;
-  const int qi = q0 + wave * 32 + (l & 31);                 // this lane's query row (position)
+  const int qi = q0 + wave * 32 + (l & 31);                 // this lane's query row
   const int H = a.H;
-  const int nkb = (min(L, q0 + FA_Q) + FA_KB - 1) / FA_KB;
+  const int nkb = (min(P + L, P + q0 + FA_Q) + FA_KB - 1) / FA_KB;
 
   // block copies (20 per block, 1 KB each): wave w issues K latent copies
   // 2 w, 2 w + 1 (rows 4 j + l / 16, piece l % 16), K rotary copy w (rows
@@ -293,7 +411,7 @@ void prefill_attention_kernel(PrefillArgs a) {
   const size_t row_hd = static_cast<size_t>(H) * (DNOPE * 2);    // bytes between tokens, per-head arrays
   auto issue = [&](int kb) {
     const uint32_t base = lds0 + (kb % 3) * FA_BUF;
-    const int tok0 = t_begin + kb * FA_KB, last = t_begin + L - 1;
+    const int tok0 = k_begin + kb * FA_KB, last = k_last;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int j = 2 * wave + k, r = 4 * j + (l >> 4), c = (l & 15) ^ (r & 15);
@@ -379,9 +497,9 @@ void prefill_attention_kernel(PrefillArgs a) {
       const f16x8 kr = *reinterpret_cast<const f16x8 *>(buf + off);
       s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kr, qf[ks], s, 0, 0, 0);
     }
-    // causal mask: key kb * 32 + tok(i) is visible to query qi while <= qi
-    const int lim = qi - kb * FA_KB - 16 * hb;                // visible while tok - 16 hb <= lim
-    if (kb * FA_KB + FA_KB - 1 > q0 + wave * 32) {
+    // causal mask: key kb * 32 + tok(i) is visible to query qi while <= P + qi
+    const int lim = P + qi - kb * FA_KB - 16 * hb;            // visible while tok - 16 hb <= lim
+    if (kb * FA_KB + FA_KB - 1 > P + q0 + wave * 32) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (4 * (i & 3) + 2 * (i >> 3) + ((i >> 2) & 1) > lim) s[i] = -INFINITY;
@@ -451,17 +569,42 @@ void prefill_attention_kernel(PrefillArgs a) {
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
-  if (a.max_len <= 0 || a.T <= 0) return hipSuccess;
+hipError_t launch_prefill(const PrefillArgs &a_in, hipStream_t stream) {
+  if (a_in.max_len <= 0 || a_in.T <= 0) return hipSuccess;
+  PrefillArgs a = a_in;
+  hipError_t e;
+  if (a.prefix_lens) {
+    // chunks over a cached prefix: key offsets, the prefix rows, then as below
+    // with the prompt's latents copied after its prefix's by the RoPE kernel
+    a.cu_keys = a.cu_keys_ws;
+    a.c_keys = a.c_gather;
+    a.c_keys_w = a.kv_fp8 ? 2 * DC : DC;
+    prefill_keys_scan_kernel<<<1, 256, 0, stream>>>(a.cu_seqlens, a.prefix_lens, a.cu_keys_ws, a.B);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.max_prefix > 0) {
+      prefill_gather_kernel<<<dim3(a.B, (a.max_prefix + ROPE_TOK - 1) / ROPE_TOK), 256, 0, stream>>>(a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  } else {
+    a.cu_keys = a.cu_seqlens;
+    a.c_keys = a.c;
+    a.c_keys_w = DC;
+    a.T_keys = a.T;
+  }
   prefill_rope_kernel<<<dim3(a.B, (a.max_len + ROPE_TOK - 1) / ROPE_TOK), 256, 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   transpose_wuk_kernel<<<dim3(DC / 32, DNOPE / 32, a.H), 256, 0, stream>>>(a.w_uk, a.w_ukt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 pgrid((a.T + PJ_TM - 1) / PJ_TM, a.H);
-  prefill_proj_kernel<<<pgrid, 256, 0, stream>>>(a.c, a.w_ukt, a.k_nope, a.T, a.H);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  prefill_proj_kernel<<<pgrid, 256, 0, stream>>>(a.c, a.w_uv, a.v, a.T, a.H);
+  const dim3 pgrid((a.T_keys + PJ_TM - 1) / PJ_TM, a.H);
+  if (a.c_keys_w == 2 * DC) {
+    prefill_proj_kernel<2 * DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_ukt, a.k_nope, a.T_keys, a.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    prefill_proj_kernel<2 * DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uv, a.v, a.T_keys, a.H);
+  } else {
+    prefill_proj_kernel<DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_ukt, a.k_nope, a.T_keys, a.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    prefill_proj_kernel<DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uv, a.v, a.T_keys, a.H);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long items = static_cast<long>((a.max_len + FA_Q - 1) / FA_Q) * a.H * a.B;
   if (items > 2147483647L) return hipErrorInvalidValue;

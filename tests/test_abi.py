@@ -158,6 +158,31 @@ def test_fp8_mfma_call_validates():
 
 
 @needs_lib
+def test_prefill_chunk_call_validates():
+    L = mla.lib()
+    f = L.mla_prefill_chunk
+
+    def call(B=2, T=8, max_len=4, total_keys=20, max_prefix=6, bs=64, dt=0, theta=10000.0, mbps=4, ws=NULL, wsb=0,
+             prefix=FAKE):
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, prefix, B, T, max_len, total_keys, max_prefix, 16,
+                 ctypes.c_float(0.07), ctypes.c_float(theta), FAKE, mbps, FAKE, dt, 16, bs, FAKE, ws, wsb, NULL)
+    assert call(prefix=NULL) == -1
+    assert call(prefix=FAKE + 4) == -1
+    assert call(total_keys=7) == -1          # fewer keys than chunk tokens
+    assert call(max_prefix=-1) == -1
+    assert call(max_prefix=257) == -1        # a prefix beyond the block-table row
+    assert call(max_len=257, T=300, total_keys=400) == -1
+    assert call(dt=3) == -1
+    assert call(theta=0.0) == -1
+    assert call(bs=32) == -2
+    assert call() == -3                      # no workspace
+    need = L.mla_prefill_chunk_workspace_bytes(8, 20, 2, 16)
+    assert need > L.mla_prefill_workspace_bytes(8, 16)
+    assert call(ws=FAKE, wsb=need - 256) == -3
+    assert L.mla_prefill_chunk_workspace_bytes(8, 7, 2, 16) == 0
+
+
+@needs_lib
 def test_multi_token_call_validates():
     L = mla.lib()
     dec = L.mla_decode_paged_multi
