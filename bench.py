@@ -78,6 +78,9 @@ def parse():
                     help="> 1: time the multi-token decode (q_len new tokens per sequence) on the same cache")
     ap.add_argument("--prefill", action="store_true",
                     help="time the explicit-form prefill of 4 prompts of 1024 tokens, 128 heads")
+    ap.add_argument("--prefill-chunk", action="store_true",
+                    help="time mla_prefill_chunk: 4 prompts, 1024-token chunks over 3072 cached rows each, "
+                         "128 heads")
     ap.add_argument("--long", action="store_true",
                     help="time the split-KV decode of 4 long sequences (1K-32K tokens), 128 heads, 256-token chunks")
     ap.add_argument("--fp8", action="store_true",
@@ -385,6 +388,104 @@ def main_prefill(args):
     print(json.dumps(out), flush=True)
 
 
+def main_prefill_chunk(args):
+    """--prefill-chunk: mla_prefill_chunk on 4 prompts whose first 3072 rows are already cached
+    (synthetic N(0, 1) bf16 rows) and whose next 1024 tokens are the chunk, 128 heads; value =
+    TFLOP/s of the algorithmic FLOPs (K and V up-projections of all 16,384 keys + the chunk's
+    attention over 3072 + j + 1 keys) against the bf16 MFMA peak."""
+    import torch
+    import mla_latent_kv_32_amd as mla
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    mla.lib()
+    dev = "cuda"
+    P, n, B, H = 3072, 1024, 4, 128
+    w = synth.prefill_workload(910, H, [n] * B)
+    rng = np.random.default_rng(911)
+    table, nblocks = synth.page_layout(rng, np.full(B, P + n, np.int32))
+    pool_np = synth.f32_to_bf16_bits(rng.standard_normal((nblocks, 64, 576)).astype(np.float32))
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    args_dev = [bf16(w[k]) for k in ("q_nope", "q_pe", "c", "k_pe", "w_uk", "w_uv")]
+    cu = torch.from_numpy(w["cu_seqlens"]).to(dev)
+    prefix = torch.full((B,), P, dtype=torch.int32, device=dev)
+    bt = torch.from_numpy(table).to(dev)
+    pool = bf16(pool_np)
+    T = w["T"]
+    total_keys = B * (P + n)
+    o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.mla_prefill_chunk_workspace_bytes(T, total_keys, B, H), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        mla.mla_prefill_chunk(*args_dev, cu, prefix, n, total_keys, P, w["scale"], w["theta"], bt, pool,
+                              mla.KV_BF16, o, workspace=ws)
+
+    for _ in range(args.warmup):
+        run()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    attn = B * (n * P + n * (n + 1) // 2) * H * 2.0 * (192 + 128)
+    proj = 2.0 * total_keys * 512 * 128 * H * 2
+    flops = attn + proj
+    achieved = flops / (us * 1e-6) / 1e12
+    out = {
+        "metric": "MLA explicit-form chunked prefill TFLOP/s, 4 x (3072 cached + 1024 new) tokens, H=128, 1 GPU",
+        "value": round(achieved, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us * 1e-3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill chunks of 1024 tokens over 3072 cached rows per prompt, 4 prompts, H=128, "
+                               "bf16 cache rows read and written", "chunk_tokens": T, "keys": total_keys, "H": H},
+        "flops": {"attention": attn, "up_projections": proj},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "scope": "the whole mla_prefill_chunk call (7 launches), HIP events around it"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_prefill_chunk(w, pool_np, table, P, o)
+        out["parity"] = out["cpu_baseline"]["parity"]
+        assert out["parity"]["ok"], "benchmarked output differs from the oracle"
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_prefill_chunk(w, pool_np, table, P, o):
+    """The CPU leg of --prefill-chunk: the oracle's chunk (fp64) for 2 heads of the first prompt,
+    timed and scaled per (prompt, head) to the whole call, and its output compared with the
+    benchmarked one at 2e-3 + 2e-2 |ref|."""
+    import oracle
+    t0 = time.perf_counter()
+    heads = [0, 77]
+    n = int(w["cu_seqlens"][1])
+    rows = oracle.gather_rows(pool_np, table, 0, P)
+    c_pre, kr_pre = oracle.rows_to_latent_rope(rows)
+    ref, _ = oracle.prefill_chunk_explicit(
+        oracle.bf16_to_f64(w["q_nope"][:n])[:, heads], oracle.bf16_to_f64(w["q_pe"][:n])[:, heads],
+        oracle.bf16_to_f64(w["c"][:n]), oracle.bf16_to_f64(w["k_pe"][:n]), c_pre, kr_pre,
+        oracle.bf16_to_f64(w["w_uk"])[heads], oracle.bf16_to_f64(w["w_uv"])[heads], w["scale"], w["theta"])
+    dt = time.perf_counter() - t0
+    got = o[:n][:, heads].float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    ok = bool((err <= 2e-3 + 2e-2 * np.abs(ref)).all())
+    B, H = w["B"], w["H"]
+    job_s = dt / len(heads) * B * H
+    flops_job = B * (n * P + n * (n + 1) // 2) * H * 2.0 * 320 + 2.0 * B * (P + n) * 512 * 128 * H * 2
+    return {"value": round(flops_job / job_s / 1e12, 6), "unit": "TFLOP/s", "cores": _oracle_cores(),
+            "cpu_model": _cpu_model(), "kind": "oracle",
+            "sample": f"prompt 0, heads {heads} of {B} x {H} (prompt, head) pairs, fp64, {dt:.2f} s; scaled to "
+                      f"the whole call ({job_s:.0f} s)",
+            "parity": {"checked": "o for prompt 0, heads 0 and 77", "max_abs_err": float(err.max()), "ok": ok}}
+
+
 def cpu_baseline_prefill(w, o):
     """The CPU leg of --prefill: the oracle's explicit-form prefill of prompt 1 (1024 tokens)
     for heads 0 and 127, timed (TFLOP/s of that sample's algorithmic FLOPs), and its output
@@ -604,6 +705,9 @@ def main():
         return
     if args.prefill:
         main_prefill(args)
+        return
+    if args.prefill_chunk:
+        main_prefill_chunk(args)
         return
     if args.fp8 or args.long:
         main_cache_workload(args, 4 if args.fp8 else 3)
