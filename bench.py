@@ -53,11 +53,11 @@ COPIES = 3
 # reported only while that source is unchanged.
 DECODE_TRAFFIC = {
     "sources_sha256": {
-        "mla_latent_kv_32_amd/csrc/decode.hip": "8c1a4207af77eac335021e4377d5752f06d60e51212ebe8e9c3376d933cb1a5e",
+        "mla_latent_kv_32_amd/csrc/decode.hip": "4e92000f3bc1c0c57cbd668270cdaccaf5cd5df113b33fb86da3486654f6d061",
         "mla_latent_kv_32_amd/csrc/common.h": "d18c3c18be49dc19eb359d77318930af1591e7ce2c3c3d6aa6fd5fd26f9de349",
     },
     "fetch_kib": 76278.4,
-    "write_kib": 32896.0,
+    "write_kib": 32950.7,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     "profile": "profiles/decode_bf16_B32_H128_ctx4096_hbm_counters.md",

@@ -540,7 +540,7 @@ struct DecoderPair {
       if (head < a.H) {
         uint16_t *dst = a.direct ? a.o_latent + (static_cast<size_t>(b) * a.H + head) * DC
                                  : a.o_part + ((static_cast<size_t>(b) * a.n_splits + split) * a.H + head) * DC;
-        *reinterpret_cast<u32x4 *>(dst + l * 8) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + l * 8));
       }
     }
   }
@@ -1084,7 +1084,10 @@ struct DecoderSolo {
   // Normalise and store: lse by the lanes of the first half; the tile goes
   // through LDS (row = head of the workgroup, 16-byte chunk c at position
   // c ^ (row & 15)) so that each global store writes one whole 1 KB row.
-  // Each wave reads back only the rows it wrote.
+  // Each wave reads back only the rows it wrote.  The rows are written once
+  // and read once, by the combine: non-temporal stores (streaming cache
+  // policy) shorten the kernel's end by about 1.6 us at 32 x 128 heads x 8
+  // chunks (33.6 MB of partials).
   __device__ __forceinline__ void finish(uint8_t *stage) {
     const int l = threadIdx.x & 63;
     const float l_tot = sum_xor32(l_run);
@@ -1124,7 +1127,7 @@ struct DecoderSolo {
       if (h < a.H) {
         uint16_t *dst = a.direct ? a.o_latent + (static_cast<size_t>(b) * a.H + h) * DC
                                  : a.o_part + ((static_cast<size_t>(b) * a.n_splits + split) * a.H + h) * DC;
-        *reinterpret_cast<u32x4 *>(dst + l * 8) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + l * 8));
       }
     }
   }

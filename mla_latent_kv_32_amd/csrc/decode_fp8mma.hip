@@ -600,7 +600,7 @@ struct DecoderF8 {
       if (h < a.H) {
         uint16_t *dst = a.direct ? a.o_latent + (static_cast<size_t>(b) * a.H + h) * DC
                                  : a.o_part + ((static_cast<size_t>(b) * a.n_splits + split) * a.H + h) * DC;
-        *reinterpret_cast<u32x4 *>(dst + l * 8) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + l * 8));
       }
     }
   }
