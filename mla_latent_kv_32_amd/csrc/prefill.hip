@@ -24,6 +24,8 @@
 //
 // Launches: RoPE + cache rows; W_UK transposed per head; the two
 // up-projections; causal attention.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "rope.h"
@@ -355,6 +357,7 @@ constexpr int FA_VB = FA_KB * DV * 2;           // 8 KB: V
 constexpr int FA_BUF = FA_KN + FA_KR + FA_VB;   // 20 KB per block
 constexpr int FA_CPW = FA_BUF / 1024 / 4;       // 5 copies per wave per block
 constexpr float FA_SLACK = 8.0f;                // lazy rescale margin (log2 units): P <= 2^8 in fp16
+constexpr int FA_GRP = 8;                       // (prompt, head) pairs per scheduling group
 static_assert(FA_Q * DV * 2 <= 3 * FA_BUF, "the output tile is staged in the block ring");
 
 __device__ __forceinline__ int fa_pi(int m) {
@@ -372,17 +375,22 @@ __device__ __forceinline__ float fa_sum_xor32(float v) {
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void prefill_attention_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[3 * FA_BUF];
-  // One workgroup per (prompt, head, query tile), the tiles of a (prompt,
-  // head) numbered consecutively, longest first; workgroups are dealt to the
-  // 8 XCDs round-robin by id, so id -> (XCD id % 8, position id / 8) is
-  // remapped to consecutive items per XCD: the tiles that read the same
-  // head's keys and values share one L2.
+  // One workgroup per (prompt, head, query tile).  Workgroups are dealt to
+  // the 8 XCDs round-robin by id, so id -> (XCD id % 8, position id / 8) is
+  // remapped to consecutive items per XCD; the items run in groups of
+  // FA_GRP (prompt, head) pairs, each group's tiles longest first (tile
+  // major): the tiles that read the same heads' keys and values share one
+  // L2 at about the same time, and every group, the last one included, ends
+  // on its shortest tiles.
   const int tiles = (a.max_len + FA_Q - 1) / FA_Q;
   const int G = gridDim.x;
   int item = blockIdx.x;
   if ((G & 7) == 0) item = (item & 7) * (G >> 3) + (item >> 3);
-  const int tile = tiles - 1 - item % tiles;
-  const int bh = item / tiles;
+  const int grp = item / (FA_GRP * tiles);
+  const int gr = item - grp * (FA_GRP * tiles);
+  const int gs = min(FA_GRP, a.B * a.H - grp * FA_GRP);       // pairs in this group
+  const int tile = tiles - 1 - gr / gs;
+  const int bh = grp * FA_GRP + gr % gs;
   const int b = bh / a.H, h = bh % a.H;
   const int t_begin = a.cu_seqlens[b];
   const int L = a.cu_seqlens[b + 1] - t_begin;
@@ -404,30 +412,42 @@ void prefill_attention_kernel(PrefillArgs a) {
   // 2 w, 2 w + 1 (rows 4 j + l / 16, piece l % 16), K rotary copy w (rows
   // 8 w + l / 8, piece l % 8) and V copies 2 w, 2 w + 1 (rows 4 j + l / 16);
   // rows past the prompt re-read its last row (their scores are masked).
+  // Per-lane source offsets from the block's first key row (the same for
+  // every whole block), wave-uniform block bases.
   const uint32_t lds0 = lds_addr(lds);
   const uint8_t *kn_src = reinterpret_cast<const uint8_t *>(a.k_nope) + static_cast<size_t>(h) * (DNOPE * 2);
   const uint8_t *kr_src = reinterpret_cast<const uint8_t *>(a.k_rot);
   const uint8_t *v_src = reinterpret_cast<const uint8_t *>(a.v) + static_cast<size_t>(h) * (DV * 2);
-  const size_t row_hd = static_cast<size_t>(H) * (DNOPE * 2);    // bytes between tokens, per-head arrays
-  auto issue = [&](int kb) {
-    const uint32_t base = lds0 + (kb % 3) * FA_BUF;
-    const int tok0 = k_begin + kb * FA_KB, last = k_last;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int j = 2 * wave + k, r = 4 * j + (l >> 4), c = (l & 15) ^ (r & 15);
-      const size_t t = static_cast<size_t>(min(tok0 + r, last));
-      dma16(kn_src + t * row_hd + 16 * c, __builtin_amdgcn_readfirstlane(base + j * 1024));
+  const uint32_t row_hd = static_cast<uint32_t>(H) * (DNOPE * 2);  // bytes between tokens, per-head arrays
+  auto copy_off = [&](int k, int nrow) -> uint32_t {
+    if (k < 2) {
+      const int r = 4 * (2 * wave + k) + (l >> 4), c = (l & 15) ^ (r & 15);
+      return static_cast<uint32_t>(min(r, nrow - 1)) * row_hd + 16 * c;
     }
-    {
+    if (k == 2) {
       const int r = 8 * wave + (l >> 3), c = (l & 7) ^ ((r >> 1) & 7);
-      const size_t t = static_cast<size_t>(min(tok0 + r, last));
-      dma16(kr_src + t * (DR * 2) + 16 * c, __builtin_amdgcn_readfirstlane(base + FA_KN + wave * 1024));
+      return static_cast<uint32_t>(min(r, nrow - 1) * (DR * 2) + 16 * c);
     }
+    const int r = 4 * (2 * wave + k - 3) + (l >> 4), c = (l & 15) ^ (4 * ((r >> 2) & 3));
+    return static_cast<uint32_t>(min(r, nrow - 1)) * row_hd + 16 * c;
+  };
+  uint32_t cpo[5];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int j = 2 * wave + k, r = 4 * j + (l >> 4), c = (l & 15) ^ (4 * ((r >> 2) & 3));
-      const size_t t = static_cast<size_t>(min(tok0 + r, last));
-      dma16(v_src + t * row_hd + 16 * c, __builtin_amdgcn_readfirstlane(base + FA_KN + FA_KR + j * 1024));
+  for (int k = 0; k < 5; ++k) cpo[k] = copy_off(k, FA_KB);
+  auto issue = [&](int kb, int buf) {
+    const uint32_t base = lds0 + buf * FA_BUF;
+    const int tok0 = k_begin + kb * FA_KB;
+    const uint8_t *kn = kn_src + static_cast<size_t>(tok0) * row_hd;
+    const uint8_t *kr = kr_src + static_cast<size_t>(tok0) * (DR * 2);
+    const uint8_t *vv = v_src + static_cast<size_t>(tok0) * row_hd;
+    const uint32_t dst[5] = {base + (2 * wave) * 1024, base + (2 * wave + 1) * 1024, base + FA_KN + wave * 1024,
+                             base + FA_KN + FA_KR + (2 * wave) * 1024, base + FA_KN + FA_KR + (2 * wave + 1) * 1024};
+    if (tok0 + FA_KB - 1 <= k_last) {
+#pragma unroll
+      for (int k = 0; k < 5; ++k) dma16_s(cpo[k], k < 2 ? kn : k == 2 ? kr : vv, dst[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 5; ++k) dma16_s(copy_off(k, k_last - tok0 + 1), k < 2 ? kn : k == 2 ? kr : vv, dst[k]);
     }
   };
 
@@ -474,6 +494,14 @@ void prefill_attention_kernel(PrefillArgs a) {
   const int d = (l & 15) >> 2;
   const int csub = 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
   const int v_off = FA_KN + FA_KR + (16 * hb + 4 * d) * (DV * 2) + 16 * csub + 8 * (l & 1);
+  // the same per k-step and column tile, kept in registers so that a block
+  // read is one LDS instruction with the buffer as its immediate offset
+  int k_offs[FA_KS], v_offs[DV / 32];
+#pragma unroll
+  for (int ks = 0; ks < FA_KS; ++ks)
+    k_offs[ks] = ks < DNOPE / 16 ? (kn_off ^ (32 * ks)) : (kr_off ^ (32 * (ks - DNOPE / 16)));
+#pragma unroll
+  for (int j = 0; j < DV / 32; ++j) v_offs[j] = v_off + 64 * (j ^ d);
 
   f32x16 o[DV / 32];
 #pragma unroll
@@ -481,20 +509,20 @@ void prefill_attention_kernel(PrefillArgs a) {
   float m_run = -FLT_MAX, l_run = 0.f;
   const float c = a.scale_log2;
 
-  issue(0);
-  if (nkb > 1) issue(1);
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) wait_vmcnt<FA_CPW>();
+  // Block kb in buffer kb % 3; the loop is unrolled three times so that the
+  // buffer is a constant in every LDS address.
+  auto block = [&](int kb, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (kb + 1 < nkb) wait_vmcnt<5>();
     else wait_vmcnt<0>();
     barrier_no_fence();        // block kb visible; every wave is done with block kb - 1
-    if (kb + 2 < nkb) issue(kb + 2);
-    const uint8_t *buf = lds + (kb % 3) * FA_BUF;
+    if (kb + 2 < nkb) issue(kb + 2, (BUF + 2) % 3);
+    const uint8_t *buf = lds + BUF * FA_BUF;
     // scores
     f32x16 s = {};
 #pragma unroll
     for (int ks = 0; ks < FA_KS; ++ks) {
-      const int off = ks < DNOPE / 16 ? (kn_off ^ (32 * ks)) : (kr_off ^ (32 * (ks - DNOPE / 16)));
-      const f16x8 kr = *reinterpret_cast<const f16x8 *>(buf + off);
+      const f16x8 kr = *reinterpret_cast<const f16x8 *>(buf + k_offs[ks]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kr, qf[ks], s, 0, 0, 0);
     }
     // causal mask: key kb * 32 + tok(i) is visible to query qi while <= P + qi
@@ -514,7 +542,7 @@ void prefill_attention_kernel(PrefillArgs a) {
       m_run = m_new;
       l_run *= alpha;
     }
-    if (__ballot(alpha != 1.0f)) {
+    if (kb > 0 && __ballot(alpha != 1.0f)) {
 #pragma unroll
       for (int j = 0; j < DV / 32; ++j) o[j] *= alpha;
     }
@@ -531,13 +559,21 @@ void prefill_attention_kernel(PrefillArgs a) {
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int j = 0; j < DV / 32; ++j) {
-        const uint8_t *r0 = buf + v_off + 2 * t * (DV * 2) + 64 * (j ^ d);
+        const uint8_t *r0 = buf + v_offs[j] + 2 * t * (DV * 2);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)r0);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(r0 + DV * 2));
         const f16x8 vf = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, p[t], o[j], 0, 0, 0);
       }
     }
+  };
+
+  issue(0, 0);
+  if (nkb > 1) issue(1, 1);
+  for (int kb = 0; kb < nkb; kb += 3) {
+    block(kb, std::integral_constant<int, 0>{});
+    if (kb + 1 < nkb) block(kb + 1, std::integral_constant<int, 1>{});
+    if (kb + 2 < nkb) block(kb + 2, std::integral_constant<int, 2>{});
   }
 
   // normalise; stage rows (query row = 32 wave + l % 32, 16-byte piece x at
