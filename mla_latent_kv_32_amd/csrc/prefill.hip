@@ -238,26 +238,34 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
   const int l = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint8_t *wh = reinterpret_cast<const uint8_t *>(w + static_cast<size_t>(h) * DC * DV);
+  const uint8_t *arow = reinterpret_cast<const uint8_t *>(act) + static_cast<size_t>(t0) * (KDIM * 2);
   const uint32_t ring_lds = lds_addr(ring);
-  // copy j (0..23) of a chunk: j < 16 -> A rows 16 j .. 16 j + 15; else B
-  // rows 4 (j - 16) .. + 3 (wave-uniform: j = 6 wave + k)
-  auto issue = [&](int ch) {
-    const uint32_t st = ring_lds + (ch % 3) * PJ_STAGE;
+  // copy j (0..23) of a chunk: j < 16 -> A rows 16 j .. 16 j + 15 (rows past
+  // the last token re-read it); else B rows 4 (j - 16) .. + 3 (wave-uniform:
+  // j = 6 wave + k).  Per-lane source offsets from the chunk's first column
+  // (A) or row (B), the same for every chunk; wave-uniform chunk bases.
+  uint32_t cpo[PJ_CPW];
+#pragma unroll
+  for (int k = 0; k < PJ_CPW; ++k) {
+    const int j = wave * PJ_CPW + k;
+    if (j < PJ_ACOPIES) {
+      const int r = 16 * j + (l >> 2), c = (l & 3) ^ ((r >> 2) & 3);
+      cpo[k] = static_cast<uint32_t>(min(r, T - 1 - t0)) * (KDIM * 2) + 16 * c;
+    } else {
+      const int kr = 4 * (j - PJ_ACOPIES) + (l >> 4), c = (l & 15) ^ (4 * (kr & 3));
+      cpo[k] = static_cast<uint32_t>(kr * (DV * 2) + 16 * c);
+    }
+  }
+  auto issue = [&](int ch, int stage) {
+    const uint32_t st = ring_lds + stage * PJ_STAGE;
+    const uint8_t *abase = arow + ch * (PJ_KC * 2);
+    const uint8_t *bbase = wh + static_cast<size_t>((ch * PJ_KC) % DC) * (DV * 2);
+    // A copies land at j KB, B copies at 16 KB + (j - 16) KB: j KB as well
+    static_assert(PJ_ABYTES == PJ_ACOPIES * 1024, "copy j lands at j KB of the stage");
 #pragma unroll
     for (int k = 0; k < PJ_CPW; ++k) {
       const int j = wave * PJ_CPW + k;
-      if (j < PJ_ACOPIES) {
-        const int r = 16 * j + (l >> 2), pos = l & 3;
-        const int c = pos ^ ((r >> 2) & 3);
-        const size_t t = static_cast<size_t>(min(t0 + r, T - 1));
-        dma16(reinterpret_cast<const uint8_t *>(act) + t * (KDIM * 2) + ch * (PJ_KC * 2) + 16 * c,
-              __builtin_amdgcn_readfirstlane(st + j * 1024));
-      } else {
-        const int kr = 4 * (j - PJ_ACOPIES) + (l >> 4), pos = l & 15;
-        const int c = pos ^ (4 * (kr & 3));
-        dma16(wh + static_cast<size_t>((ch * PJ_KC + kr) % DC) * (DV * 2) + 16 * c,
-              __builtin_amdgcn_readfirstlane(st + PJ_ABYTES + (j - PJ_ACOPIES) * 1024));
-      }
+      dma16_s(cpo[k], j < PJ_ACOPIES ? abase : bbase, st + j * 1024);
     }
   };
   f32x16 acc[PJ_MT][DV / 32];
@@ -265,42 +273,54 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
   for (int m = 0; m < PJ_MT; ++m)
 #pragma unroll
     for (int n = 0; n < DV / 32; ++n) acc[m][n] = f32x16{};
-  // A read of tile m: row 64 wave + 32 m + l % 32, piece 2 s + l / 32 (k-step s of the chunk)
+  // A read of tile m, k-step s: row ar0 + 32 m, piece 2 s + l / 32 at
+  // (2 s + l / 32) ^ ((row >> 2) & 3); the swizzle does not depend on m
   const int ar0 = 32 * PJ_MT * wave + (l & 31);
-  // B reads (transposed): lane 16 g + q reads rows 8 (g >> 1) + q / 4 (+ 4) of
-  // a k-step, columns 32 n + 16 (g & 1) + 4 (q & 3) .. + 4
+  const int ax = (l >> 5) ^ ((ar0 >> 2) & 3);
+  int a_off[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) a_off[s] = ar0 * (PJ_KC * 2) + ((ax ^ (2 * s)) << 4);
+  // B reads (transposed): lane 16 g + q reads rows 8 (g >> 1) + q / 4 (+ 4)
+  // of k-step s, columns 32 n + 16 (g & 1) + 4 (q & 3) .. + 4: piece
+  // 4 n + 2 (g & 1) + (q & 3) / 2 at 4 (n ^ (row & 3)) + ...; s and the + 4
+  // rows are immediates
   const int g = l >> 4, q = l & 15;
   const int krow = 8 * (g >> 1) + (q >> 2);
-  issue(0);
-  issue(1);
-  for (int ch = 0; ch < PJ_NCH; ++ch) {
+  int b_off[DV / 32];
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n)
+    b_off[n] = PJ_ABYTES + krow * (DV * 2) + ((4 * (n ^ (krow & 3)) + 2 * (g & 1) + ((q & 3) >> 1)) << 4) + (q & 1) * 8;
+  // chunk ch in stage ch % 3; the loop is unrolled three times so that the
+  // stage is a constant in every LDS address
+  auto chunk = [&](int ch, auto stc) {
+    constexpr int STG = decltype(stc)::value;
     if (ch + 1 < PJ_NCH) wait_vmcnt<PJ_CPW>();
     else wait_vmcnt<0>();
     barrier_no_fence();
-    if (ch + 2 < PJ_NCH) issue(ch + 2);
-    const uint8_t *st = ring + (ch % 3) * PJ_STAGE;
+    if (ch + 2 < PJ_NCH) issue(ch + 2, (STG + 2) % 3);
+    const uint8_t *st = ring + STG * PJ_STAGE;
 #pragma unroll
     for (int s = 0; s < PJ_KC / 16; ++s) {
-      const int piece = 2 * s + (l >> 5);
       bf16x8 av[PJ_MT];
 #pragma unroll
-      for (int m = 0; m < PJ_MT; ++m) {
-        const int ar = ar0 + 32 * m;
-        av[m] = *reinterpret_cast<const bf16x8 *>(st + ar * (PJ_KC * 2) + ((piece ^ ((ar >> 2) & 3)) << 4));
-      }
+      for (int m = 0; m < PJ_MT; ++m) av[m] = *reinterpret_cast<const bf16x8 *>(st + a_off[s] + m * 32 * (PJ_KC * 2));
 #pragma unroll
       for (int n = 0; n < DV / 32; ++n) {
-        const int chunk = 4 * n + 2 * (g & 1) + ((q & 3) >> 1);
-        const int k0 = 16 * s + krow, k1 = k0 + 4;
-        const uint8_t *b0 = st + PJ_ABYTES + k0 * (DV * 2) + ((chunk ^ (4 * (k0 & 3))) << 4) + (q & 1) * 8;
-        const uint8_t *b1 = st + PJ_ABYTES + k1 * (DV * 2) + ((chunk ^ (4 * (k1 & 3))) << 4) + (q & 1) * 8;
+        const uint8_t *b0 = st + b_off[n] + 16 * s * (DV * 2);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)b0);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)b1);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(b0 + 4 * (DV * 2)));
         const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int m = 0; m < PJ_MT; ++m) acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bv, acc[m][n], 0, 0, 0);
       }
     }
+  };
+  issue(0, 0);
+  issue(1, 1);
+  for (int ch = 0; ch < PJ_NCH; ch += 3) {
+    chunk(ch, std::integral_constant<int, 0>{});
+    if (ch + 1 < PJ_NCH) chunk(ch + 1, std::integral_constant<int, 1>{});
+    if (ch + 2 < PJ_NCH) chunk(ch + 2, std::integral_constant<int, 2>{});
   }
   // stage: row = token, 16-byte piece x at position x ^ (row & 15); then whole rows
   __syncthreads();
@@ -340,8 +360,8 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
 //            key step t as they stand (keys stored in natural order, the
 //            MFMA's K-row m reading key pi(m))
 // A block is three XOR-swizzled regions filled by 16-byte global->LDS copies
-// (20 per block, five per wave) into a ring of three buffers, two blocks in
-// flight while one is used:
+// (20 per block, five per wave) into a ring of FA_NBUF buffers, FA_NBUF - 1
+// blocks in flight while one is used:
 //   K latent part  32 rows x 256 B, piece c of row r at c ^ (r & 15)
 //   K rotary part  32 rows x 128 B, piece c of row r at c ^ ((r >> 1) & 7)
 //   V              32 rows x 256 B, piece c of row r at c ^ 4 ((r >> 2) & 3)
@@ -358,7 +378,8 @@ constexpr int FA_BUF = FA_KN + FA_KR + FA_VB;   // 20 KB per block
 constexpr int FA_CPW = FA_BUF / 1024 / 4;       // 5 copies per wave per block
 constexpr float FA_SLACK = 8.0f;                // lazy rescale margin (log2 units): P <= 2^8 in fp16
 constexpr int FA_GRP = 8;                       // (prompt, head) pairs per scheduling group
-static_assert(FA_Q * DV * 2 <= 3 * FA_BUF, "the output tile is staged in the block ring");
+constexpr int FA_NBUF = 3;                      // block ring
+static_assert(FA_Q * DV * 2 <= FA_NBUF * FA_BUF, "the output tile is staged in the block ring");
 
 __device__ __forceinline__ int fa_pi(int m) {
   return 16 * ((m >> 2) & 1) + 4 * (m & 3) + 2 * ((m >> 4) & 1) + ((m >> 3) & 1);
@@ -374,7 +395,7 @@ __device__ __forceinline__ float fa_sum_xor32(float v) {
 
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void prefill_attention_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * FA_BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[FA_NBUF * FA_BUF];
   // One workgroup per (prompt, head, query tile).  Workgroups are dealt to
   // the 8 XCDs round-robin by id, so id -> (XCD id % 8, position id / 8) is
   // remapped to consecutive items per XCD; the items run in groups of
@@ -509,22 +530,28 @@ void prefill_attention_kernel(PrefillArgs a) {
   float m_run = -FLT_MAX, l_run = 0.f;
   const float c = a.scale_log2;
 
-  // Block kb in buffer kb % 3; the loop is unrolled three times so that the
-  // buffer is a constant in every LDS address.
+  // Block kb in buffer kb % FA_NBUF; the loop is unrolled FA_NBUF times so
+  // that the buffer is a constant in every LDS address.
   auto block = [&](int kb, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    if (kb + 1 < nkb) wait_vmcnt<5>();
+    // block kb has landed once at most the copies of the blocks after it
+    // (5 per block and wave) are outstanding
+    const int ahead = min(FA_NBUF - 2, nkb - 1 - kb);
+    if (FA_NBUF > 3 && ahead >= 2) wait_vmcnt<10>();
+    else if (ahead >= 1) wait_vmcnt<5>();
     else wait_vmcnt<0>();
     barrier_no_fence();        // block kb visible; every wave is done with block kb - 1
-    if (kb + 2 < nkb) issue(kb + 2, (BUF + 2) % 3);
+    if (kb + FA_NBUF - 1 < nkb) issue(kb + FA_NBUF - 1, (BUF + FA_NBUF - 1) % FA_NBUF);
     const uint8_t *buf = lds + BUF * FA_BUF;
-    // scores
+    // scores: every key fragment of the block is read before the first
+    // MFMA, so that the chain of 12 MFMAs waits for the LDS once
+    f16x8 kf[FA_KS];
+#pragma unroll
+    for (int ks = 0; ks < FA_KS; ++ks) kf[ks] = *reinterpret_cast<const f16x8 *>(buf + k_offs[ks]);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s = {};
 #pragma unroll
-    for (int ks = 0; ks < FA_KS; ++ks) {
-      const f16x8 kr = *reinterpret_cast<const f16x8 *>(buf + k_offs[ks]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kr, qf[ks], s, 0, 0, 0);
-    }
+    for (int ks = 0; ks < FA_KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], s, 0, 0, 0);
     // causal mask: key kb * 32 + tok(i) is visible to query qi while <= P + qi
     const int lim = P + qi - kb * FA_KB - 16 * hb;            // visible while tok - 16 hb <= lim
     if (kb * FA_KB + FA_KB - 1 > P + q0 + wave * 32) {
@@ -568,12 +595,13 @@ void prefill_attention_kernel(PrefillArgs a) {
     }
   };
 
-  issue(0, 0);
-  if (nkb > 1) issue(1, 1);
-  for (int kb = 0; kb < nkb; kb += 3) {
+  for (int i = 0; i < FA_NBUF - 1; ++i)
+    if (i < nkb) issue(i, i);
+  for (int kb = 0; kb < nkb; kb += FA_NBUF) {
     block(kb, std::integral_constant<int, 0>{});
     if (kb + 1 < nkb) block(kb + 1, std::integral_constant<int, 1>{});
     if (kb + 2 < nkb) block(kb + 2, std::integral_constant<int, 2>{});
+    if (FA_NBUF > 3 && kb + 3 < nkb) block(kb + 3, std::integral_constant<int, 3 % FA_NBUF>{});
   }
 
   // normalise; stage rows (query row = 32 wave + l % 32, 16-byte piece x at
