@@ -472,18 +472,41 @@ void prefill_attention_kernel(PrefillArgs a) {
     }
   };
 
-  // query fragments: lane (q row, hb) holds dims 16 ks + 8 hb .. + 8; the
-  // bf16 q_nope converts to half (exact inside half's range), the rotated
-  // part is already half
+  // Query fragments: lane (q row, hb) holds dims 16 ks + 8 hb .. + 8.  The
+  // wave's 32 rows are first copied whole into the (still unused) ring with
+  // 16-byte global->LDS copies -- 4 q_nope rows (256 B) or 8 rotated rows
+  // (128 B) per copy, so every request reads whole rows -- piece c of row r
+  // at position c ^ (r & 15) (q_nope) or c ^ ((r >> 1) & 7) (rotated), then read
+  // into the MFMA layout.  The bf16 q_nope converts to half (exact inside
+  // half's range); the rotated part is already half.
   f16x8 qf[FA_KS];
   {
-    const size_t th = (static_cast<size_t>(t_begin) + min(qi, L - 1)) * H + h;
+    constexpr int QN = 32 * DNOPE * 2, QR = 32 * DR * 2;           // 8 KB, 4 KB per wave
+    static_assert(4 * (QN + QR) <= FA_NBUF * FA_BUF, "the query rows are staged in the block ring");
+    const uint32_t qbase = lds0 + wave * (QN + QR);
+    const int r0 = q0 + wave * 32;
+    const uint8_t *qn = reinterpret_cast<const uint8_t *>(a.q_nope);
+    const uint8_t *qr = reinterpret_cast<const uint8_t *>(a.q_rot);
+#pragma unroll
+    for (int k = 0; k < QN / 1024; ++k) {
+      const int r = 4 * k + (l >> 4), c = (l & 15) ^ (r & 15);
+      const size_t th = (static_cast<size_t>(t_begin) + min(r0 + r, L - 1)) * H + h;
+      dma16(qn + th * (DNOPE * 2) + 16 * c, qbase + k * 1024);
+    }
+#pragma unroll
+    for (int k = 0; k < QR / 1024; ++k) {
+      const int r = 8 * k + (l >> 3), c = (l & 7) ^ ((r >> 1) & 7);
+      const size_t th = (static_cast<size_t>(t_begin) + min(r0 + r, L - 1)) * H + h;
+      dma16(qr + th * (DR * 2) + 16 * c, qbase + QN + k * 1024);
+    }
+    wait_vmcnt<0>();           // this wave's rows (each wave reads only its own)
+    asm volatile("" ::: "memory");
+    const int r = l & 31;
 #pragma unroll
     for (int ks = 0; ks < FA_KS; ++ks) {
-      const uint16_t *src = ks < DNOPE / 16 ? a.q_nope + th * DNOPE + 16 * ks + 8 * hb
-                                            : a.q_rot + th * DR + 16 * (ks - DNOPE / 16) + 8 * hb;
-      const u32x4 raw = *reinterpret_cast<const u32x4 *>(src);
       if (ks < DNOPE / 16) {
+        const int c = 2 * ks + hb;
+        const u32x4 raw = *reinterpret_cast<const u32x4 *>(lds + wave * (QN + QR) + r * (DNOPE * 2) + ((c ^ (r & 15)) << 4));
         f16x8 h8;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -492,16 +515,14 @@ void prefill_attention_kernel(PrefillArgs a) {
         }
         qf[ks] = h8;
       } else {
-        qf[ks] = __builtin_bit_cast(f16x8, raw);
+        const int c = 2 * (ks - DNOPE / 16) + hb;
+        qf[ks] = *reinterpret_cast<const f16x8 *>(lds + wave * (QN + QR) + QN + r * (DR * 2) + ((c ^ ((r >> 1) & 7)) << 4));
       }
     }
-    // Wait for the query here, before any block copy is issued: the
-    // compiler does not see the copies (inline asm) and would otherwise
-    // place its waits for the query inside the loop, where they also wait
-    // for the copies of the blocks ahead.
-#pragma unroll
-    for (int ks = 0; ks < FA_KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
+  barrier_lds();               // every wave has its query fragments: the ring takes blocks now
+  for (int i = 0; i < FA_NBUF - 1; ++i)
+    if (i < nkb) issue(i, i);
 
   // per-lane read offsets within a block buffer
   const int m = fa_pi(l & 31);
@@ -595,8 +616,6 @@ void prefill_attention_kernel(PrefillArgs a) {
     }
   };
 
-  for (int i = 0; i < FA_NBUF - 1; ++i)
-    if (i < nkb) issue(i, i);
   for (int kb = 0; kb < nkb; kb += FA_NBUF) {
     block(kb, std::integral_constant<int, 0>{});
     if (kb + 1 < nkb) block(kb + 1, std::integral_constant<int, 1>{});
