@@ -65,11 +65,12 @@ def check_prefill(w, o, pool, pairs, rows_for=(), widen=True):
             assert_close(got_kr, rows[pos, 512:], what=f"k_rot b={b} pos={pos}")
 
 
-@pytest.mark.parametrize("H", [16, 128])
+@pytest.mark.parametrize("H", [5, 16, 128])
 @pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8])
 def test_prefill_matches_oracle(H, kv_dtype):
     """Ragged prompts around the 32-key blocks and 128-row query tiles,
-    including a 1-token and an empty prompt."""
+    including a 1-token and an empty prompt; H = 5 leaves the up-projection's
+    last pair of heads with one head."""
     lens = [1, 0, 31, 33, 128, 129, 300]
     w = synth.prefill_workload(700 + H + kv_dtype, H, lens, kv_dtype)
     o, pool = run_prefill(w)
