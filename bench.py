@@ -43,6 +43,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROW_BYTES = 576 * 2
 COPIES = 3
+WARM_S = 0.05                  # untimed replays of the timed steps before the timed region (clock warm-up)
 
 # HBM bytes the decode kernel moves per launch on this workload, from two
 # rocprofv3 --pmc passes over this benchmark (FETCH_SIZE, then WRITE_SIZE, KiB
@@ -777,6 +778,22 @@ def main():
         graph = None
         mode = f"eager launches (graph capture failed: {type(e).__name__})"
     torch.cuda.synchronize()
+    # Clock warm-up: the GPU reaches its steady clocks only after tens of
+    # milliseconds of continuous work.  Measured: a 20-step replay right
+    # after the warmup steps ran at 78-82 us per step, the same replay after
+    # 20 back-to-back untimed replays at 64-65 us.  So the captured steps are
+    # replayed, untimed and in groups of four, for WARM_S seconds first.
+    warm_replays = 0
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < WARM_S:
+        for _ in range(4):
+            if graph is not None:
+                graph.replay()
+            else:
+                for i in range(args.steps):
+                    step(i)
+        warm_replays += 4
+        torch.cuda.synchronize()
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     g0.record(stream)
@@ -867,6 +884,8 @@ def main():
         },
         "kernels_avg_us": {k: round(v, 3) for k, v in avg_us.items()},
         "timing": {"timed_region": mode, "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+                   "clock_warmup": f"{warm_replays} untimed replays of the {args.steps} steps ({WARM_S * 1e3:.0f} ms) "
+                                   "after the warmup steps, before the timed replay",
                    "one_graph_per_step_us": None if one_step_us is None else round(one_step_us, 3),
                    "eager_step_gpu_us": round(eager_step_us, 3),
                    "kernel_events": "HIP events on the launch stream around each call, launches queued "
