@@ -43,6 +43,16 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROW_BYTES = 576 * 2
 COPIES = 3
+
+
+def queue_sleep_cycles(steps, calls=3):
+    """GPU sleep (cycles) behind which `steps` eagerly launched steps of
+    `calls` library calls each (plus their event records) are queued before
+    the GPU reaches them: 2 ms plus 50 us of host time per call at 2 GHz.
+    A much longer sleep lets the GPU's clocks drop before the timed kernels
+    run: the decode's event time was 49.2 us behind a 100 ms sleep, 44.7 us
+    behind this one."""
+    return 4_000_000 + 100_000 * calls * steps
 WARM_S = 0.05                  # untimed replays of the timed steps before the timed region (clock warm-up)
 
 # HBM bytes the decode kernel moves per launch on this workload, from two
@@ -250,7 +260,7 @@ def main_multi(args):
             fn(i)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         torch.cuda.synchronize()
-        torch.cuda._sleep(200_000_000)
+        torch.cuda._sleep(queue_sleep_cycles(args.steps, 1))
         t0 = time.perf_counter()
         for i in range(args.steps):
             ev[i][0].record(stream)
@@ -359,7 +369,7 @@ def main_prefill(args):
         run()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    torch.cuda._sleep(200_000_000)
+    torch.cuda._sleep(queue_sleep_cycles(args.steps, 2))
     for i in range(args.steps):
         ev[i][0].record(stream)
         run()
@@ -429,7 +439,7 @@ def main_prefill_chunk(args):
         run()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    torch.cuda._sleep(200_000_000)
+    torch.cuda._sleep(queue_sleep_cycles(args.steps, 2))
     for i in range(args.steps):
         ev[i][0].record(stream)
         run()
@@ -570,7 +580,7 @@ def main_cache_workload(args, cfg):
         step(i)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    torch.cuda._sleep(200_000_000)      # every launch below is queued before the GPU reaches it
+    torch.cuda._sleep(queue_sleep_cycles(args.steps, 2))      # every launch below is queued before the GPU reaches it
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, ev[i])
@@ -582,7 +592,7 @@ def main_cache_workload(args, cfg):
         # the same combine on the partials the last call left, timed alone;
         # decode = call - combine
         ce = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        torch.cuda._sleep(200_000_000)
+        torch.cuda._sleep(queue_sleep_cycles(args.steps, 1))
         for e in ce:
             e[0].record(stream)
             mla.mla_decode_combine(ws, sl, S, o, lse, split_tokens=split)
@@ -835,7 +845,7 @@ def main():
     # events on the launch stream bracket kernel time only.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    torch.cuda._sleep(200_000_000)      # long enough for every launch below to be queued first
+    torch.cuda._sleep(queue_sleep_cycles(args.steps))   # every launch below is queued before the GPU reaches it
     for i in range(args.steps):
         step(i, events[i])
     torch.cuda.synchronize()
