@@ -360,7 +360,7 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
 //            key step t as they stand (keys stored in natural order, the
 //            MFMA's K-row m reading key pi(m))
 // A block is three XOR-swizzled regions filled by 16-byte global->LDS copies
-// (20 per block, five per wave) into a ring of FA_NBUF buffers, FA_NBUF - 1
+// (20 per block, five per wave) into a ring of three buffers, two
 // blocks in flight while one is used:
 //   K latent part  32 rows x 256 B, piece c of row r at c ^ (r & 15)
 //   K rotary part  32 rows x 128 B, piece c of row r at c ^ ((r >> 1) & 7)
@@ -378,8 +378,9 @@ constexpr int FA_BUF = FA_KN + FA_KR + FA_VB;   // 20 KB per block
 constexpr int FA_CPW = FA_BUF / 1024 / 4;       // 5 copies per wave per block
 constexpr float FA_SLACK = 8.0f;                // lazy rescale margin (log2 units): P <= 2^8 in fp16
 constexpr int FA_GRP = 8;                       // (prompt, head) pairs per scheduling group
-constexpr int FA_NBUF = 3;                      // block ring
+constexpr int FA_NBUF = 3;                      // block ring (a fourth buffer measured no gain)
 static_assert(FA_Q * DV * 2 <= FA_NBUF * FA_BUF, "the output tile is staged in the block ring");
+static_assert(FA_NBUF == 3, "the block loop below is unrolled over three buffers");
 
 __device__ __forceinline__ int fa_pi(int m) {
   return 16 * ((m >> 2) & 1) + 4 * (m & 3) + 2 * ((m >> 4) & 1) + ((m >> 3) & 1);
@@ -555,11 +556,9 @@ void prefill_attention_kernel(PrefillArgs a) {
   // that the buffer is a constant in every LDS address.
   auto block = [&](int kb, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    // block kb has landed once at most the copies of the blocks after it
-    // (5 per block and wave) are outstanding
-    const int ahead = min(FA_NBUF - 2, nkb - 1 - kb);
-    if (FA_NBUF > 3 && ahead >= 2) wait_vmcnt<10>();
-    else if (ahead >= 1) wait_vmcnt<5>();
+    // block kb has landed once at most the copies of block kb + 1 (5 per
+    // wave) are outstanding
+    if (kb + 1 < nkb) wait_vmcnt<5>();
     else wait_vmcnt<0>();
     barrier_no_fence();        // block kb visible; every wave is done with block kb - 1
     if (kb + FA_NBUF - 1 < nkb) issue(kb + FA_NBUF - 1, (BUF + FA_NBUF - 1) % FA_NBUF);
@@ -620,7 +619,6 @@ void prefill_attention_kernel(PrefillArgs a) {
     block(kb, std::integral_constant<int, 0>{});
     if (kb + 1 < nkb) block(kb + 1, std::integral_constant<int, 1>{});
     if (kb + 2 < nkb) block(kb + 2, std::integral_constant<int, 2>{});
-    if (FA_NBUF > 3 && kb + 3 < nkb) block(kb + 3, std::integral_constant<int, 3 % FA_NBUF>{});
   }
 
   // normalise; stage rows (query row = 32 wave + l % 32, 16-byte piece x at
