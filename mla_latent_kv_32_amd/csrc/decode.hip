@@ -728,6 +728,59 @@ struct DecoderSolo {
     for (int k = 0; k < NI; ++k) copy(c, k, voff, roff);
   }
 
+  // Blocks with every row inside the chunk take a shorter copy: a buffer
+  // resource based at this wave's first row of the block (row w), the row
+  // offsets of copies k = 1..7 (4 k rows) and of the rotary copy (7 w rows)
+  // in SGPRs set once per workgroup (a buffer load's SGPR offset moves the
+  // global address only, not the LDS one), so a copy is an M0 update and the
+  // load, where the clamped form forms each row's 64-bit address.
+  struct FullCopy {
+    i32x4 rsrc;           // raw buffer at row w of the block
+    uint32_t m0_lat;      // LDS address of slot row w
+    uint32_t m0_rope;     // LDS address of this wave's rotary rows in the slot
+  };
+  uint32_t soff_[NI];     // soff_[k]: 4 k rows (k < 8); soff_[8]: 7 w rows
+  __device__ __forceinline__ static uint32_t sgpr_const(uint32_t x) {
+    asm volatile("s_mov_b32 %0, %1" : "=s"(x) : "s"(x));
+    return x;
+  }
+  __device__ __forceinline__ void init_full_copy() {
+#pragma unroll
+    for (int k = 1; k < NI - 1; ++k) soff_[k] = sgpr_const(k * NW * ROW_BYTES);
+    soff_[NI - 1] = sgpr_const(__builtin_amdgcn_readfirstlane(7 * wave * ROW_BYTES));
+  }
+  __device__ __forceinline__ FullCopy full_copy_of(int blk, int phys, uint8_t *slot) const {
+    const int tok0 = t_begin + blk * TB;
+    const uint64_t p = reinterpret_cast<uint64_t>(a.cache) +
+                       (static_cast<uint64_t>(phys) * PAGE + (tok0 & 32) + wave) * ROW_BYTES;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p)));
+    r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xFFFF));
+    r[2] = -1;                    // num_records: no range check (offsets stay inside the page)
+    r[3] = 0x00020000;            // raw buffer, 32-bit data format
+    const uint32_t s = lds_addr(slot);
+    return FullCopy{r, static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(s + wave * S_LROW)),
+                    static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(s + S_LAT + wave * 1024))};
+  }
+  // Rotary copy offset of lane l relative to row w + 7 w = 8 w: row l / 8 of
+  // the wave's eight, chunk l % 8 stored at chunk (l % 8) ^ fr(row).
+  __device__ __forceinline__ uint32_t rope_voff_full(int l) const {
+    const int j = l >> 3;
+    return static_cast<uint32_t>(j * ROW_BYTES + LAT_BYTES + (((l & 7) ^ fr(wave * 8 + j)) << 4));
+  }
+  __device__ __forceinline__ void copy_full(const FullCopy &f, int k, uint32_t voff, uint32_t roff) const {
+    if (k == 0)
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                   : : "v"(voff), "s"(f.m0_lat), "s"(f.rsrc) : "memory", "m0");
+    else if (k < TB / NW)
+      asm volatile("s_add_i32 m0, %1, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %3, %4 offen lds"
+                   : : "v"(voff), "s"(f.m0_lat), "i"(k * NW * S_LROW), "s"(f.rsrc), "s"(soff_[k])
+                   : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+                   : : "v"(roff), "s"(f.m0_rope), "s"(f.rsrc), "s"(soff_[NI - 1]) : "memory", "m0");
+  }
+
   // MFMAs are written out so that their order is the program order (the
   // loads between them are pinned by the memory clobber) and so that the
   // score accumulator stays in VGPRs (the builtin would take the accumulator
@@ -902,9 +955,11 @@ struct DecoderSolo {
   // masked beforehand (mask_scores).  Operands are read in order and used in
   // swapped pairs (MFMA slot 2m takes read 2m + 1, slot 2m + 1 read 2m), so a
   // single LDS wait before each pair covers both of its reads.
-  template <bool COPY>
+  // COPY: 0 no copies, 1 the clamped copies of `cp`, 2 the full-block
+  // copies of `fc`.
+  template <int COPY>
   __device__ __forceinline__ void phase(const uint8_t *slot_s, const uint8_t *slot_v, f32x16 &s, bool first,
-                                        const Copy &cp) {
+                                        const Copy &cp, const FullCopy &fc) {
     const int l = lane_id();
     const int kb = k_base(l), krb = kr_base(l);
     constexpr int RK = 4, RV = 4, NV = 2 * NT;
@@ -923,17 +978,19 @@ struct DecoderSolo {
     rescale(first ? 1.0f : st.alpha);
     const int vb = v_base(l);
     uint32_t voff = 0, roff = 0;
-    if (COPY) {
-      voff = static_cast<uint32_t>(opaque(l) << 4);
-      roff = rope_voff(cp, l);
-    }
+    if (COPY) voff = static_cast<uint32_t>(opaque(l) << 4);
+    if (COPY == 1) roff = rope_voff(cp, l);
+    if (COPY == 2) roff = rope_voff_full(l);
 #pragma unroll
     for (int n = 0; n < RV; ++n) vf[n] = vread(slot_v, vb, n);
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
       if (n + RV < NV) vf[n + RV] = vread(slot_v, vb, n + RV);
       mfma_o(o[(n ^ 1) & 15], vf[n ^ 1], st.p[(n ^ 1) >> 4], n == 0, false);
-      if (COPY && n % 3 == 1 && n / 3 < NI) copy(cp, n / 3, voff, roff);   // copies k = 0..8 at n = 3 k + 1
+      if (COPY && n % 3 == 1 && n / 3 < NI) {                               // copies k = 0..8 at n = 3 k + 1
+        if (COPY == 1) copy(cp, n / 3, voff, roff);
+        else copy_full(fc, n / 3, voff, roff);
+      }
     }
     s = sn;
   }
@@ -1347,18 +1404,28 @@ void decode_solo_kernel(DecodeArgs a) {
   barrier_no_fence();         // blocks 0 and 1 visible
   f32x16 s = dec.scores(slot(0));
   int i = 0;
-  for (; i + 3 < nblk; ++i) {
+  // Only the chunk's last block can have rows past its end: the copies of
+  // every other block take the full-block form.
+  dec.init_full_copy();
+  for (; i + 4 < nblk; ++i) {
     const int phys = dec.page_of(i + 3);
     wait_vmcnt<NI>();
     barrier_no_fence();
-    dec.phase<true>(slot(i + 1), slot(i), s, i == 0, dec.copy_of(i + 3, phys, slot(i + 3)));
+    dec.phase<2>(slot(i + 1), slot(i), s, i == 0, DecoderSolo::Copy{}, dec.full_copy_of(i + 3, phys, slot(i + 3)));
+  }
+  if (i + 3 < nblk) {
+    const int phys = dec.page_of(i + 3);
+    wait_vmcnt<NI>();
+    barrier_no_fence();
+    dec.phase<1>(slot(i + 1), slot(i), s, i == 0, dec.copy_of(i + 3, phys, slot(i + 3)), DecoderSolo::FullCopy{});
+    ++i;
   }
   for (; i + 1 < nblk; ++i) {
     if (i + 2 < nblk) wait_vmcnt<NI>();
     else wait_vmcnt<0>();
     barrier_no_fence();
     dec.mask_scores(s, dec.mask_limit(DecoderSolo::lane_id(), i));
-    dec.phase<false>(slot(i + 1), slot(i), s, i == 0, DecoderSolo::Copy{});
+    dec.phase<0>(slot(i + 1), slot(i), s, i == 0, DecoderSolo::Copy{}, DecoderSolo::FullCopy{});
   }
   {
     DecoderSolo::Soft st;
