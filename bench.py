@@ -64,11 +64,11 @@ WARM_S = 0.05                  # untimed replays of the timed steps before the t
 # reported only while that source is unchanged.
 DECODE_TRAFFIC = {
     "sources_sha256": {
-        "mla_latent_kv_32_amd/csrc/decode.hip": "4e92000f3bc1c0c57cbd668270cdaccaf5cd5df113b33fb86da3486654f6d061",
-        "mla_latent_kv_32_amd/csrc/common.h": "d18c3c18be49dc19eb359d77318930af1591e7ce2c3c3d6aa6fd5fd26f9de349",
+        "mla_latent_kv_32_amd/csrc/decode.hip": "eabcde87c81d4c960950e2248195a50984005c9952cfbcabe3d1fece8e8a37cb",
+        "mla_latent_kv_32_amd/csrc/common.h": "f88b1789f340fb1101b55bbc780bc0e7c7204bb6939f3677d3b26086ff681a29",
     },
-    "fetch_kib": 76278.4,
-    "write_kib": 32950.7,
+    "fetch_kib": 76314.1,
+    "write_kib": 33113.4,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     "profile": "profiles/decode_bf16_B32_H128_ctx4096_hbm_counters.md",

@@ -24,6 +24,7 @@
 //
 // Launches: RoPE + cache rows; W_UK transposed per head; the two
 // up-projections; causal attention.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -209,139 +210,196 @@ __global__ __launch_bounds__(256) void transpose_wuk_kernel(const uint16_t *w, u
 // bf16 operands, fp32 accumulation, written in fp16.  KDIM = 1024 takes rows
 // [c_hi | c_lo] against [W; W]: out = c_hi W + c_lo W in one accumulation.
 //
-// Workgroup: 256 tokens x one head; wave w owns tokens 64 w .. 64 w + 63 (two
-// 32-row tiles) and all four 32-column tiles, so every weight fragment read
-// from LDS feeds two MFMAs.  K runs in chunks of 32 through a 3-stage LDS
-// ring fed by 16-byte global->LDS copies (two chunks in flight while one is
-// multiplied).  A chunk: 256 rows x 64 bytes, 16-byte piece c of row r at
-// position c ^ ((r >> 2) & 3), so a read of one piece of 16 consecutive rows
-// meets 16 bank quads.  B chunk: 32 rows x 256 bytes, piece c of row k at
-// c ^ 4 (k & 3), read transposed (ds_read_b64_tr_b16) as in the absorption
-// GEMMs.  The output tile goes through the ring to whole-row stores.
-constexpr int PJ_TM = 256;                      // tokens per workgroup
-constexpr int PJ_MT = PJ_TM / 4 / 32;           // 32-row tiles per wave: 2
-constexpr int PJ_KC = 32;                       // K per chunk
-constexpr int PJ_ABYTES = PJ_TM * PJ_KC * 2;    // 16 KB
-constexpr int PJ_BBYTES = PJ_KC * DV * 2;       // 8 KB
-constexpr int PJ_STAGE = PJ_ABYTES + PJ_BBYTES;
-constexpr int PJ_ACOPIES = PJ_ABYTES / 1024;    // 16 one-KB copies of A per chunk
-constexpr int PJ_CPW = PJ_STAGE / 1024 / 4;     // copies per wave per chunk: 6
-static_assert(PJ_STAGE % 4096 == 0, "a chunk splits evenly over the four waves");
-static_assert(PJ_TM * DV * 2 <= 3 * PJ_STAGE, "the output tile is staged in the ring");
+// The product is formed transposed, out^T[col, t] = W[h]^T[col, :] .
+// c^T[:, t], so that the latent -- the operand every head shares -- is the
+// MFMA's B operand and stays in registers for all the heads of a workgroup:
+// wave w holds the latent rows of its MT 32-token tiles (the B fragments of
+// every k-step, 256 accumulation registers) from the start, and only the
+// weights stream through LDS.  Workgroup: 4 x 32 MT tokens (256 for K = 512,
+// 128 for K = 1024) x a group of heads.  The weights of the group's heads run
+// through a 6-stage ring of 64-row chunks (16 KB: 64 rows x 256 bytes,
+// 16-byte piece c of row k at c ^ 4 (k & 3)), read transposed
+// (ds_read_b64_tr_b16) as the A operand, each fragment feeding MT MFMAs.
+// The accumulators of a head (32x32 tiles, registers: column 8 (i / 4) +
+// 4 (l / 32) + i % 4 of the tile, token l % 32) leave as fp16: a swap
+// between lanes l and l + 32 gives each lane 8 consecutive columns, each
+// wave stages its own rows in LDS and stores them as whole 256-byte rows
+// (stores of 32-byte row pieces straight from the registers took half as
+// long again).  Compared with 256-token x 1-head tiles streaming both
+// operands, the latent is read from L2 once per head group instead of once
+// per head, and the weights once per 256 tokens.
+constexpr int PJ_KC = 64;                           // weight rows per chunk
+constexpr int PJ_CBYTES = PJ_KC * DV * 2;           // 16 KB
+constexpr int PJ_NST = 6;                           // ring stages
+constexpr int PJ_CPW = PJ_CBYTES / 1024 / 4;        // copies per wave per chunk: 4
+static_assert((PJ_NST - 2) * PJ_CPW <= 63, "the chunks in flight fit the vmcnt counter");
+
+__host__ __device__ constexpr int proj_tokens(int kdim) { return 4 * 32 * (1024 / kdim); }
 
 template <int KDIM>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
-void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, int T, int H) {
-  constexpr int PJ_NCH = KDIM / PJ_KC;         // chunks of 32 along K
-  __shared__ __attribute__((aligned(16))) uint8_t ring[3 * PJ_STAGE];
-  const int h = blockIdx.y, t0 = blockIdx.x * PJ_TM;
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, int T, int H, int hpw) {
+  constexpr int MT = 1024 / KDIM;                  // 32-token tiles per wave: 2 or 1
+  constexpr int KS = KDIM / 16;                    // k-steps: 32 or 64
+  constexpr int NCH = KDIM / PJ_KC;                // chunks per head: 8 or 16
+  constexpr int TM = proj_tokens(KDIM);            // tokens per workgroup
+  constexpr int NN = DV / 32;                      // column tiles: 4
+  static_assert(MT * KS * 4 == 256, "the latent fragments fill the accumulation registers");
+  constexpr int PJ_STORES = 8 * MT;                // whole-row stores per wave and head (4 rows each)
+  __shared__ __attribute__((aligned(16))) uint8_t ring[PJ_NST * PJ_CBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t ostage[TM * DV * 2];   // the head's output rows
+
+  // workgroups are dealt to the 8 XCDs round-robin: consecutive indices per
+  // XCD, token tile fastest, so the workgroups of one XCD share a head group
+  const int G = gridDim.x;
+  const int item = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int tiles = (T + TM - 1) / TM;
+  const int t0 = (item % tiles) * TM, h0 = (item / tiles) * hpw;
+  const int nh = min(hpw, H - h0);
   const int l = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint8_t *wh = reinterpret_cast<const uint8_t *>(w + static_cast<size_t>(h) * DC * DV);
-  const uint8_t *arow = reinterpret_cast<const uint8_t *>(act) + static_cast<size_t>(t0) * (KDIM * 2);
+  uint8_t *const otile = ostage + wave * (32 * MT * DV * 2);
+
+  // the latent fragments: lat[m][ks] = c[t, 16 ks + 8 (l / 32) .. + 7] for
+  // token t = t0 + 32 (MT wave + m) + l % 32 (rows past T re-read row T - 1)
+  bf16x8 lat[MT][KS];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int t = min(t0 + 32 * (MT * wave + m) + (l & 31), T - 1);
+    const uint16_t *row = act + static_cast<size_t>(t) * KDIM + 8 * (l >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) lat[m][ks] = *reinterpret_cast<const bf16x8 *>(row + 16 * ks);
+  }
+
+  // chunk g of the group: head h0 + g / NCH, weight rows 64 (g % NCH) % 512;
+  // copy k of wave w moves rows 16 w + 4 k .. + 3 (lane: row + l / 16, piece
+  // (l % 16) ^ 4 (row & 3), stored at position l % 16)
   const uint32_t ring_lds = lds_addr(ring);
-  // copy j (0..23) of a chunk: j < 16 -> A rows 16 j .. 16 j + 15 (rows past
-  // the last token re-read it); else B rows 4 (j - 16) .. + 3 (wave-uniform:
-  // j = 6 wave + k).  Per-lane source offsets from the chunk's first column
-  // (A) or row (B), the same for every chunk; wave-uniform chunk bases.
   uint32_t cpo[PJ_CPW];
 #pragma unroll
   for (int k = 0; k < PJ_CPW; ++k) {
-    const int j = wave * PJ_CPW + k;
-    if (j < PJ_ACOPIES) {
-      const int r = 16 * j + (l >> 2), c = (l & 3) ^ ((r >> 2) & 3);
-      cpo[k] = static_cast<uint32_t>(min(r, T - 1 - t0)) * (KDIM * 2) + 16 * c;
-    } else {
-      const int kr = 4 * (j - PJ_ACOPIES) + (l >> 4), c = (l & 15) ^ (4 * (kr & 3));
-      cpo[k] = static_cast<uint32_t>(kr * (DV * 2) + 16 * c);
-    }
+    const int kr = 4 * (PJ_CPW * wave + k) + (l >> 4);
+    cpo[k] = static_cast<uint32_t>(kr * (DV * 2) + 16 * ((l & 15) ^ (4 * (kr & 3))));
   }
-  auto issue = [&](int ch, int stage) {
-    const uint32_t st = ring_lds + stage * PJ_STAGE;
-    const uint8_t *abase = arow + ch * (PJ_KC * 2);
-    const uint8_t *bbase = wh + static_cast<size_t>((ch * PJ_KC) % DC) * (DV * 2);
-    // A copies land at j KB, B copies at 16 KB + (j - 16) KB: j KB as well
-    static_assert(PJ_ABYTES == PJ_ACOPIES * 1024, "copy j lands at j KB of the stage");
+  const int total = nh * NCH;
+  auto issue = [&](int g) {
+    const int hh = g / NCH, c = g - hh * NCH;
+    const uint8_t *src = reinterpret_cast<const uint8_t *>(w + static_cast<size_t>(h0 + hh) * DC * DV) +
+                         static_cast<size_t>((c * PJ_KC) % DC) * (DV * 2);
+    const uint32_t st = ring_lds + (g % PJ_NST) * PJ_CBYTES + wave * (PJ_CPW * 1024);
 #pragma unroll
-    for (int k = 0; k < PJ_CPW; ++k) {
-      const int j = wave * PJ_CPW + k;
-      dma16_s(cpo[k], j < PJ_ACOPIES ? abase : bbase, st + j * 1024);
-    }
+    for (int k = 0; k < PJ_CPW; ++k) dma16_s(cpo[k], src, st + k * 1024);
   };
-  f32x16 acc[PJ_MT][DV / 32];
+
+  // transposed weight reads: lane 16 gq + q reads rows 8 (gq >> 1) + q / 4
+  // (and + 4) of a k-step, columns 32 n + 16 (gq & 1) + 4 (q & 3) .. + 4
+  const int gq = l >> 4, q = l & 15;
+  const int krow = 8 * (gq >> 1) + (q >> 2);
+  int b_off[NN];
 #pragma unroll
-  for (int m = 0; m < PJ_MT; ++m)
+  for (int n = 0; n < NN; ++n)
+    b_off[n] = krow * (DV * 2) + ((4 * (n ^ (krow & 3)) + 2 * (gq & 1) + ((q & 3) >> 1)) << 4) + (q & 1) * 8;
+  // operand j = NN s + n of a chunk: k-step s, column tile n
+  constexpr int NJ = (PJ_KC / 16) * NN;            // 16 per chunk
+  constexpr int R = 3;                             // operands read ahead of their MFMAs
+  auto read_w = [&](const uint8_t *st, int j) {
+    const uint8_t *b0 = st + b_off[j % NN] + 16 * (j / NN) * (DV * 2);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)b0);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(b0 + 4 * (DV * 2)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // Ring: chunks 0 .. NST - 2 go out first; the barrier that publishes
+  // chunk g + 1 sits in chunk g once its last operand read is issued (so the
+  // reads of chunk g + 1's first R operands overlap chunk g's last MFMAs),
+  // and it sends chunk g + NST - 1 into the slot of chunk g - 1, whose reads
+  // every wave finished before the previous barrier.
 #pragma unroll
-    for (int n = 0; n < DV / 32; ++n) acc[m][n] = f32x16{};
-  // A read of tile m, k-step s: row ar0 + 32 m, piece 2 s + l / 32 at
-  // (2 s + l / 32) ^ ((row >> 2) & 3); the swizzle does not depend on m
-  const int ar0 = 32 * PJ_MT * wave + (l & 31);
-  const int ax = (l >> 5) ^ ((ar0 >> 2) & 3);
-  int a_off[2];
+  for (int g = 0; g < PJ_NST - 1; ++g)
+    if (g < total) issue(g);
+  if (PJ_NST - 2 < total) wait_vmcnt<(PJ_NST - 2) * PJ_CPW>();
+  else wait_vmcnt<0>();
+  barrier_no_fence();
+  bf16x8 nxt[R];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) a_off[s] = ar0 * (PJ_KC * 2) + ((ax ^ (2 * s)) << 4);
-  // B reads (transposed): lane 16 g + q reads rows 8 (g >> 1) + q / 4 (+ 4)
-  // of k-step s, columns 32 n + 16 (g & 1) + 4 (q & 3) .. + 4: piece
-  // 4 n + 2 (g & 1) + (q & 3) / 2 at 4 (n ^ (row & 3)) + ...; s and the + 4
-  // rows are immediates
-  const int g = l >> 4, q = l & 15;
-  const int krow = 8 * (g >> 1) + (q >> 2);
-  int b_off[DV / 32];
+  for (int j = 0; j < R; ++j) nxt[j] = read_w(ring, j);
+
+  f32x16 acc[MT][NN];
+  for (int hh = 0; hh < nh; ++hh) {
+    // the chunks of a head unrolled: every k-step names its latent fragment
 #pragma unroll
-  for (int n = 0; n < DV / 32; ++n)
-    b_off[n] = PJ_ABYTES + krow * (DV * 2) + ((4 * (n ^ (krow & 3)) + 2 * (g & 1) + ((q & 3) >> 1)) << 4) + (q & 1) * 8;
-  // chunk ch in stage ch % 3; the loop is unrolled three times so that the
-  // stage is a constant in every LDS address
-  auto chunk = [&](int ch, auto stc) {
-    constexpr int STG = decltype(stc)::value;
-    if (ch + 1 < PJ_NCH) wait_vmcnt<PJ_CPW>();
-    else wait_vmcnt<0>();
-    barrier_no_fence();
-    if (ch + 2 < PJ_NCH) issue(ch + 2, (STG + 2) % 3);
-    const uint8_t *st = ring + STG * PJ_STAGE;
+    for (int c = 0; c < NCH; ++c) {
+      const int g = hh * NCH + c;
+      const uint8_t *st = ring + (g % PJ_NST) * PJ_CBYTES;
+      bf16x8 wv[NJ];
 #pragma unroll
-    for (int s = 0; s < PJ_KC / 16; ++s) {
-      bf16x8 av[PJ_MT];
+      for (int j = 0; j < R; ++j) wv[j] = nxt[j];
 #pragma unroll
-      for (int m = 0; m < PJ_MT; ++m) av[m] = *reinterpret_cast<const bf16x8 *>(st + a_off[s] + m * 32 * (PJ_KC * 2));
+      for (int j = 0; j < NJ; ++j) {
+        if (j + R < NJ) wv[j + R] = read_w(st, j + R);
+        if (j == NJ - R && g + 1 < total) {
+          // copies of chunks g + 2 .. g + NST - 2 may stay in flight, and in
+          // the first NST - 2 chunks of a head also the previous head's
+          // stores, which went out after the copies of chunk g + 1
+          if (g + PJ_NST - 2 >= total) wait_vmcnt<0>();
+          else if (c < PJ_NST - 2 && hh > 0) wait_vmcnt<(PJ_NST - 3) * PJ_CPW + PJ_STORES>();
+          else wait_vmcnt<(PJ_NST - 3) * PJ_CPW>();
+          barrier_no_fence();            // chunk g + 1 landed
+          if (g + PJ_NST - 1 < total) issue(g + PJ_NST - 1);
+          const uint8_t *st1 = ring + ((g + 1) % PJ_NST) * PJ_CBYTES;
 #pragma unroll
-      for (int n = 0; n < DV / 32; ++n) {
-        const uint8_t *b0 = st + b_off[n] + 16 * s * (DV * 2);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)b0);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(b0 + 4 * (DV * 2)));
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          for (int jj = 0; jj < R; ++jj) nxt[jj] = read_w(st1, jj);
+        }
+        const int ks = c * (PJ_KC / 16) + j / NN, n = j % NN;
 #pragma unroll
-        for (int m = 0; m < PJ_MT; ++m) acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[m], bv, acc[m][n], 0, 0, 0);
+        for (int m = 0; m < MT; ++m) {
+          if (ks == 0)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                         : "=&v"(acc[m][n]) : "v"(wv[j]), "a"(lat[m][ks]) : "memory");
+          else
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+v"(acc[m][n]) : "v"(wv[j]), "a"(lat[m][ks]) : "memory");
+        }
       }
     }
-  };
-  issue(0, 0);
-  issue(1, 1);
-  for (int ch = 0; ch < PJ_NCH; ch += 3) {
-    chunk(ch, std::integral_constant<int, 0>{});
-    if (ch + 1 < PJ_NCH) chunk(ch + 1, std::integral_constant<int, 1>{});
-    if (ch + 2 < PJ_NCH) chunk(ch + 2, std::integral_constant<int, 2>{});
-  }
-  // stage: row = token, 16-byte piece x at position x ^ (row & 15); then whole rows
-  __syncthreads();
-  const int hb = l >> 5, r = l & 31;
+    {
+      // the last MFMA's result wait states, then the head's tile out: each
+      // wave stages its own rows in LDS (fp16, row = token, 16-byte piece x
+      // at position x ^ (row & 15)) and stores them as whole rows.  Rows
+      // past T hold row T - 1's values (their latent re-read row T - 1) and
+      // are stored there again, so every lane stores and the number of
+      // stores per head is fixed (the vmcnt waits above count them).
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+      const int h = h0 + hh;
 #pragma unroll
-  for (int m = 0; m < PJ_MT; ++m)
+      for (int m = 0; m < MT; ++m) {
+        const int r = 32 * m + (l & 31);
 #pragma unroll
-    for (int n = 0; n < DV / 32; ++n)
+        for (int n = 0; n < NN; ++n) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = ar0 - (l & 31) + 32 * m + (i >> 2) * 8 + hb * 4 + (i & 3), col = 32 * n + r;
-        *reinterpret_cast<uint16_t *>(ring + row * (DV * 2) + (((col >> 3) ^ (row & 15)) << 4) + 2 * (col & 7)) =
-            f16_bits(acc[m][n][i]);
+          for (int p = 0; p < 2; ++p) {
+            // registers 8 p .. 8 p + 7: columns 16 p + {0..3, 8..11} (l < 32)
+            // or 16 p + {4..7, 12..15}; swap so that lane l < 32 holds
+            // 16 p + 0..7 and lane l + 32 16 p + 8..15
+            uint32_t v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = f16_bits(acc[m][n][8 * p + 2 * e]) | (static_cast<uint32_t>(f16_bits(acc[m][n][8 * p + 2 * e + 1])) << 16);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+            const int x = 4 * n + 2 * p + (l >> 5);
+            *reinterpret_cast<u32x4 *>(otile + r * (DV * 2) + ((x ^ (r & 15)) << 4)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+          }
+        }
       }
-  __syncthreads();
 #pragma unroll
-  for (int k = 0; k < PJ_TM * 16 / 256; ++k) {
-    const int p = threadIdx.x + 256 * k, row = p >> 4, x = p & 15;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(ring + row * (DV * 2) + ((x ^ (row & 15)) << 4));
-    if (t0 + row < T)
-      *reinterpret_cast<u32x4 *>(out + (static_cast<size_t>(t0 + row) * H + h) * DV + 8 * x) = v;
+      for (int k = 0; k < PJ_STORES; ++k) {
+        const int r = 4 * k + (l >> 4), x = l & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(otile + r * (DV * 2) + ((x ^ (r & 15)) << 4));
+        const int t = min(t0 + 32 * MT * wave + r, T - 1);
+        *reinterpret_cast<u32x4 *>(out + (static_cast<size_t>(t) * H + h) * DV + 8 * x) = v;
+      }
+    }
   }
 }
 
@@ -676,15 +734,19 @@ hipError_t launch_prefill(const PrefillArgs &a_in, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   transpose_wuk_kernel<<<dim3(DC / 32, DNOPE / 32, a.H), 256, 0, stream>>>(a.w_uk, a.w_ukt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 pgrid((a.T_keys + PJ_TM - 1) / PJ_TM, a.H);
+  // heads per workgroup: enough workgroups for the 256 compute units, at
+  // most 16 heads each
+  const int ptiles = (a.T_keys + proj_tokens(a.c_keys_w) - 1) / proj_tokens(a.c_keys_w);
+  const int hpw = std::max(1, std::min(16, a.H * ptiles / 256));
+  const dim3 pgrid(ptiles * ((a.H + hpw - 1) / hpw));
   if (a.c_keys_w == 2 * DC) {
-    prefill_proj_kernel<2 * DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_ukt, a.k_nope, a.T_keys, a.H);
+    prefill_proj_kernel<2 * DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_ukt, a.k_nope, a.T_keys, a.H, hpw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    prefill_proj_kernel<2 * DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uv, a.v, a.T_keys, a.H);
+    prefill_proj_kernel<2 * DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uv, a.v, a.T_keys, a.H, hpw);
   } else {
-    prefill_proj_kernel<DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_ukt, a.k_nope, a.T_keys, a.H);
+    prefill_proj_kernel<DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_ukt, a.k_nope, a.T_keys, a.H, hpw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    prefill_proj_kernel<DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uv, a.v, a.T_keys, a.H);
+    prefill_proj_kernel<DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uv, a.v, a.T_keys, a.H, hpw);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long items = static_cast<long>((a.max_len + FA_Q - 1) / FA_Q) * a.H * a.B;
