@@ -401,7 +401,7 @@ int mla_decode_combine_absorb_out(const void *workspace, size_t workspace_bytes,
  *               mla_rope_append_cache
  *   o           [T, H, 128] bf16 output
  *   workspace   device buffer of mla_prefill_workspace_bytes(T, H) bytes
- *               (rotated queries and keys, per-head K and V, W_UK transposed)
+ *               (rotated queries and keys, per-head K and V)
  * Empty prompts write nothing.  Errors as for the decode calls.
  * Precision: the attention runs on IEEE-half operands with fp32
  * accumulation (rotated query and key, K_nope, V and the softmax weights),

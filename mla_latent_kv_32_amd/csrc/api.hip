@@ -435,8 +435,7 @@ int mla_decode_combine_absorb_out(const void *workspace, size_t workspace_bytes,
 size_t mla_prefill_workspace_bytes(int total_tokens, int H) {
   if (total_tokens < 1 || H < 1) return 0;
   const size_t T = static_cast<size_t>(total_tokens), h = static_cast<size_t>(H);
-  return align256(T * h * MLA_D_R * 2) + align256(T * MLA_D_R * 2) + 2 * align256(T * h * MLA_D_NOPE * 2) +
-         align256(h * MLA_D_C * MLA_D_NOPE * 2);
+  return align256(T * h * MLA_D_R * 2) + align256(T * MLA_D_R * 2) + 2 * align256(T * h * MLA_D_NOPE * 2);
 }
 
 int mla_prefill(const void *q_nope, const void *q_pe, const void *c_kv, const void *k_pe, const void *w_uk,
@@ -486,8 +485,6 @@ int mla_prefill(const void *q_nope, const void *q_pe, const void *c_kv, const vo
   a.k_nope = reinterpret_cast<uint16_t *>(p);
   p += align256(T * h * MLA_D_NOPE * 2);
   a.v = reinterpret_cast<uint16_t *>(p);
-  p += align256(T * h * MLA_D_NOPE * 2);
-  a.w_ukt = reinterpret_cast<uint16_t *>(p);
   return status_of(mla::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -496,7 +493,7 @@ size_t mla_prefill_chunk_workspace_bytes(int total_tokens, int total_keys, int B
   const size_t T = static_cast<size_t>(total_tokens), K = static_cast<size_t>(total_keys),
                h = static_cast<size_t>(H);
   return align256(T * h * MLA_D_R * 2) + align256(K * MLA_D_R * 2) + 2 * align256(K * h * MLA_D_NOPE * 2) +
-         align256(h * MLA_D_C * MLA_D_NOPE * 2) + align256(K * 2 * MLA_D_C * 2) +
+         align256(K * 2 * MLA_D_C * 2) +
          align256((static_cast<size_t>(B) + 1) * sizeof(int32_t));
 }
 
@@ -554,8 +551,6 @@ int mla_prefill_chunk(const void *q_nope, const void *q_pe, const void *c_kv, co
   p += align256(K * h * MLA_D_NOPE * 2);
   a.v = reinterpret_cast<uint16_t *>(p);
   p += align256(K * h * MLA_D_NOPE * 2);
-  a.w_ukt = reinterpret_cast<uint16_t *>(p);
-  p += align256(h * MLA_D_C * MLA_D_NOPE * 2);
   a.c_gather = reinterpret_cast<uint16_t *>(p);
   p += align256(K * 2 * MLA_D_C * 2);
   a.cu_keys_ws = reinterpret_cast<int32_t *>(p);

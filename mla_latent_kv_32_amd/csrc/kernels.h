@@ -146,7 +146,6 @@ struct PrefillArgs {
   uint16_t *k_rot;              // [T_keys, 64] fp16
   uint16_t *k_nope;             // [T_keys, H, 128] fp16
   uint16_t *v;                  // [T_keys, H, 128] fp16
-  uint16_t *w_ukt;              // [H, 512, 128] = W_UK transposed per head
   uint16_t *c_gather;           // [T_keys, c_keys_w] bf16 (chunks only: c_keys points here)
   int32_t *cu_keys_ws;          // [B + 1] (chunks only: cu_keys points here)
 };

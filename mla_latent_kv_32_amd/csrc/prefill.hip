@@ -22,8 +22,7 @@
 // queries must stay below that magnitude (unit-scale activations are five
 // orders of magnitude inside it); P stays at most 2^8 by the lazy rescale.
 //
-// Launches: RoPE + cache rows; W_UK transposed per head; the two
-// up-projections; causal attention.
+// Launches: RoPE + cache rows; the two up-projections; causal attention.
 #include <algorithm>
 #include <type_traits>
 
@@ -193,20 +192,9 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(PrefillArgs a) {
   }
 }
 
-// ---- W_UK[h] [128, 512] -> W_UK[h]^T [512, 128] (32 x 32 tiles through LDS)
-__global__ __launch_bounds__(256) void transpose_wuk_kernel(const uint16_t *w, uint16_t *wt) {
-  __shared__ uint16_t tile[32][33];
-  const int k0 = blockIdx.x * 32, n0 = blockIdx.y * 32, h = blockIdx.z;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;           // 32 x 8
-  const uint16_t *src = w + static_cast<size_t>(h) * DNOPE * DC;
-  uint16_t *dst = wt + static_cast<size_t>(h) * DC * DNOPE;
-  for (int r = ty; r < 32; r += 8) tile[r][tx] = src[static_cast<size_t>(n0 + r) * DC + k0 + tx];
-  __syncthreads();
-  for (int r = ty; r < 32; r += 8) dst[static_cast<size_t>(k0 + r) * DNOPE + n0 + tx] = tile[tx][r];
-}
-
 // ---- per-head up-projection of the shared latent: out[t, h, :] =
-// c[t, :] . W[h] (K = 512, N = 128; W = W_UK^T or W_UV, both [H, 512, 128]),
+// c[t, :] . W[h] (K = 512, N = 128; W = W_UK^T, read from W_UK [H, 128, 512]
+// as stored, or W_UV [H, 512, 128]),
 // bf16 operands, fp32 accumulation, written in fp16.  KDIM = 1024 takes rows
 // [c_hi | c_lo] against [W; W]: out = c_hi W + c_lo W in one accumulation.
 //
@@ -236,7 +224,12 @@ static_assert((PJ_NST - 2) * PJ_CPW <= 63, "the chunks in flight fit the vmcnt c
 
 __host__ __device__ constexpr int proj_tokens(int kdim) { return 4 * 32 * (1024 / kdim); }
 
-template <int KDIM>
+// WCOL: the weights arrive column-major per head, [H, 128, 512] (W_UK as
+// stored, row = output column), instead of [H, 512, 128] (W_UV): a chunk is
+// then 128 column rows x 128 bytes (64 k), 16-byte piece p of column row r
+// at position p ^ ((r >> 1) & 7), and the A operand is a plain 16-byte read
+// (lane: column row l % 32 of the tile, k-piece 2 s + l / 32).
+template <int KDIM, bool WCOL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, int T, int H, int hpw) {
   constexpr int MT = 1024 / KDIM;                  // 32-token tiles per wave: 2 or 1
@@ -273,19 +266,26 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
 
   // chunk g of the group: head h0 + g / NCH, weight rows 64 (g % NCH) % 512;
   // copy k of wave w moves rows 16 w + 4 k .. + 3 (lane: row + l / 16, piece
-  // (l % 16) ^ 4 (row & 3), stored at position l % 16)
+  // (l % 16) ^ 4 (row & 3), stored at position l % 16); column-major
+  // weights: column rows 32 w + 8 k .. + 7 (lane: row + l / 8, piece
+  // (l % 8) ^ ((row >> 1) & 7), stored at position l % 8)
   const uint32_t ring_lds = lds_addr(ring);
   uint32_t cpo[PJ_CPW];
 #pragma unroll
   for (int k = 0; k < PJ_CPW; ++k) {
-    const int kr = 4 * (PJ_CPW * wave + k) + (l >> 4);
-    cpo[k] = static_cast<uint32_t>(kr * (DV * 2) + 16 * ((l & 15) ^ (4 * (kr & 3))));
+    if (WCOL) {
+      const int cr = 8 * (PJ_CPW * wave + k) + (l >> 3);
+      cpo[k] = static_cast<uint32_t>(cr * (DC * 2) + 16 * ((l & 7) ^ ((cr >> 1) & 7)));
+    } else {
+      const int kr = 4 * (PJ_CPW * wave + k) + (l >> 4);
+      cpo[k] = static_cast<uint32_t>(kr * (DV * 2) + 16 * ((l & 15) ^ (4 * (kr & 3))));
+    }
   }
   const int total = nh * NCH;
   auto issue = [&](int g) {
     const int hh = g / NCH, c = g - hh * NCH;
     const uint8_t *src = reinterpret_cast<const uint8_t *>(w + static_cast<size_t>(h0 + hh) * DC * DV) +
-                         static_cast<size_t>((c * PJ_KC) % DC) * (DV * 2);
+                         static_cast<size_t>((c * PJ_KC) % DC) * (WCOL ? 2 : DV * 2);
     const uint32_t st = ring_lds + (g % PJ_NST) * PJ_CBYTES + wave * (PJ_CPW * 1024);
 #pragma unroll
     for (int k = 0; k < PJ_CPW; ++k) dma16_s(cpo[k], src, st + k * 1024);
@@ -302,7 +302,15 @@ void prefill_proj_kernel(const uint16_t *act, const uint16_t *w, uint16_t *out, 
   // operand j = NN s + n of a chunk: k-step s, column tile n
   constexpr int NJ = (PJ_KC / 16) * NN;            // 16 per chunk
   constexpr int R = 3;                             // operands read ahead of their MFMAs
+  // column-major weights: lane l reads column row 32 n + l % 32 (swizzle
+  // f = ((l % 32) >> 1) & 7 whatever n), piece 2 s + l / 32 at position
+  // (2 s + l / 32) ^ f; one offset per k-step, the column tile an immediate
+  int c_off[PJ_KC / 16];
+#pragma unroll
+  for (int s4 = 0; s4 < PJ_KC / 16; ++s4)
+    c_off[s4] = (l & 31) * (PJ_KC * 2) + (((2 * s4 + (l >> 5)) ^ (((l & 31) >> 1) & 7)) << 4);
   auto read_w = [&](const uint8_t *st, int j) {
+    if (WCOL) return *reinterpret_cast<const bf16x8 *>(st + c_off[j / NN] + (j % NN) * 32 * (PJ_KC * 2));
     const uint8_t *b0 = st + b_off[j % NN] + 16 * (j / NN) * (DV * 2);
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)b0);
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(b0 + 4 * (DV * 2)));
@@ -732,21 +740,19 @@ hipError_t launch_prefill(const PrefillArgs &a_in, hipStream_t stream) {
   }
   prefill_rope_kernel<<<dim3(a.B, (a.max_len + ROPE_TOK - 1) / ROPE_TOK), 256, 0, stream>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  transpose_wuk_kernel<<<dim3(DC / 32, DNOPE / 32, a.H), 256, 0, stream>>>(a.w_uk, a.w_ukt);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   // heads per workgroup: enough workgroups for the 256 compute units, at
   // most 16 heads each
   const int ptiles = (a.T_keys + proj_tokens(a.c_keys_w) - 1) / proj_tokens(a.c_keys_w);
   const int hpw = std::max(1, std::min(16, a.H * ptiles / 256));
   const dim3 pgrid(ptiles * ((a.H + hpw - 1) / hpw));
   if (a.c_keys_w == 2 * DC) {
-    prefill_proj_kernel<2 * DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_ukt, a.k_nope, a.T_keys, a.H, hpw);
+    prefill_proj_kernel<2 * DC, true><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uk, a.k_nope, a.T_keys, a.H, hpw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    prefill_proj_kernel<2 * DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uv, a.v, a.T_keys, a.H, hpw);
+    prefill_proj_kernel<2 * DC, false><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uv, a.v, a.T_keys, a.H, hpw);
   } else {
-    prefill_proj_kernel<DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_ukt, a.k_nope, a.T_keys, a.H, hpw);
+    prefill_proj_kernel<DC, true><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uk, a.k_nope, a.T_keys, a.H, hpw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    prefill_proj_kernel<DC><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uv, a.v, a.T_keys, a.H, hpw);
+    prefill_proj_kernel<DC, false><<<pgrid, 256, 0, stream>>>(a.c_keys, a.w_uv, a.v, a.T_keys, a.H, hpw);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long items = static_cast<long>((a.max_len + FA_Q - 1) / FA_Q) * a.H * a.B;
