@@ -100,6 +100,18 @@ def test_prefill_long_prompts_full_heads():
     check_prefill(w, o, pool, [(0, range(0, 128, 9)), (3, range(4, 128, 8))], widen=False)
 
 
+def test_prefill_head_groups_with_a_partial_last_group():
+    """100 heads over 4,072 keys: the up-projections take 6 heads per
+    workgroup (16 token tiles, 17 head groups), so the last group holds 4
+    heads, and the last token tile is ragged (4,072 = 15 x 256 + 232).
+    Every token of heads on both sides of group boundaries and of the last
+    group, in the first and the shortest prompt, at the stated bf16 bound."""
+    w = synth.prefill_workload(750, 100, [1024, 1024, 1024, 1000])
+    o, pool = run_prefill(w)
+    assert not torch.isnan(o.float()).any().item()
+    check_prefill(w, o, pool, [(0, [0, 5, 6, 95, 96, 99]), (3, [11, 12, 97])], widen=False)
+
+
 def test_prefill_long_ragged_prompt():
     """One 4001-token prompt (126 key blocks, a ragged last query tile and
     page) beside a short one: every token of two heads against the oracle,
