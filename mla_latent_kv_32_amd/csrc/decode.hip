@@ -91,6 +91,23 @@ __device__ __forceinline__ float max_xor16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// Maxima of scores that are finite or -inf: v_max3_f32 / v_max_f32 as
+// written (the fmaxf form quiets signalling NaNs first, one extra
+// instruction per operand).
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -610,6 +627,11 @@ struct DecoderSolo {
   // m_run): running max (log2 units), this lane's share of the sum of the
   // bf16-rounded weights and of the unrounded weights.
   float m_run, l_run, e_run;
+  // Per-lane LDS offsets of the score (latent, rotary) and value operand
+  // reads within a slot, formed once: recomputing them in every block cost
+  // about 20 VALU instructions per block.
+  int kb_, krb_, vb_;
+  uint32_t voff_, roff_full_;   // full-block copy offsets (latent rows, rotary rows)
 
   __device__ DecoderSolo(const DecodeArgs &args, int b_, int split_, int grp_, int S, int t0, int t1)
       : a(args), wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)), b(b_), split(split_), grp(grp_),
@@ -646,6 +668,12 @@ struct DecoderSolo {
     e_run = 0.f;
 #pragma unroll
     for (int j = 0; j < NT; ++j) o[j] = f32x16{};
+    const int l = lane_id();
+    kb_ = k_base(l);
+    krb_ = kr_base(l);
+    vb_ = v_base(l);
+    voff_ = static_cast<uint32_t>(l << 4);
+    roff_full_ = rope_voff_full(l);
   }
 
   // Query through LDS.  Read straight into the MFMA layout, every query load
@@ -832,7 +860,7 @@ struct DecoderSolo {
     return S_LAT + r * ROPE_BYTES + (((l >> 5) ^ fr(r)) << 4);
   }
   __device__ __forceinline__ static bf16x8 kread(const uint8_t *slot, int kb, int krb, int ks) {
-    const uint8_t *p = ks < KSL ? slot + kb + 32 * ks : slot + (opaque(krb) ^ ((ks - KSL) * 32));
+    const uint8_t *p = ks < KSL ? slot + kb + 32 * ks : slot + (krb ^ ((ks - KSL) * 32));
     return *reinterpret_cast<const bf16x8 *>(p);
   }
   // Value operand n = 16 t + j (column tile j, token step t; A of
@@ -873,12 +901,11 @@ struct DecoderSolo {
         for (int i = 0; i < 16; ++i)
           if (4 * (i & 3) + 2 * (i >> 3) + ((i >> 2) & 1) >= lim) s[i] = -INFINITY;
       }
-      st.mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      st.mx = vmax3(vmax3(s[0], s[1], s[2]), vmax3(s[3], s[4], s[5]), vmax(s[6], s[7]));
     } else if (k == 1) {
-      st.mx = fmaxf(st.mx, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
-                                 fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+      st.mx = vmax3(vmax3(st.mx, s[8], s[9]), vmax3(s[10], s[11], s[12]), vmax3(s[13], s[14], s[15]));
     } else if (k == 2) {
-      const float m_new = fmaxf(m_run, max_xor32(st.mx) * c);
+      const float m_new = vmax(m_run, vmax_xor32(st.mx) * c);
       const bool up = m_new > m_run + SOLO_SLACK;
       const float e = __builtin_amdgcn_exp2f(m_run - m_new);       // 0 on the first block (m_run = -FLT_MAX)
       st.alpha = up ? e : 1.0f;
@@ -961,7 +988,7 @@ struct DecoderSolo {
   __device__ __forceinline__ void phase(const uint8_t *slot_s, const uint8_t *slot_v, f32x16 &s, bool first,
                                         const Copy &cp, const FullCopy &fc) {
     const int l = lane_id();
-    const int kb = k_base(l), krb = kr_base(l);
+    const int kb = kb_, krb = krb_;
     constexpr int RK = 4, RV = 4, NV = 2 * NT;
     bf16x8 kr[KS], vf[NV];
     f32x16 sn;
@@ -976,11 +1003,16 @@ struct DecoderSolo {
       __builtin_amdgcn_sched_barrier(0);
     }
     rescale(first ? 1.0f : st.alpha);
-    const int vb = v_base(l);
+    const int vb = vb_;
     uint32_t voff = 0, roff = 0;
-    if (COPY) voff = static_cast<uint32_t>(opaque(l) << 4);
-    if (COPY == 1) roff = rope_voff(cp, l);
-    if (COPY == 2) roff = rope_voff_full(l);
+    if (COPY == 1) {
+      voff = static_cast<uint32_t>(opaque(l) << 4);
+      roff = rope_voff(cp, l);
+    }
+    if (COPY == 2) {
+      voff = voff_;
+      roff = roff_full_;
+    }
 #pragma unroll
     for (int n = 0; n < RV; ++n) vf[n] = vread(slot_v, vb, n);
 #pragma unroll
