@@ -796,17 +796,28 @@ struct DecoderSolo {
     const int j = l >> 3;
     return static_cast<uint32_t>(j * ROW_BYTES + LAT_BYTES + (((l & 7) ^ fr(wave * 8 + j)) << 4));
   }
+  // M0 (the LDS address of a copy) is set one copy ahead: copy k issues its
+  // load and then sets M0 for copy k + 1, so the MFMAs between two copies
+  // stand in for the wait state an M0 write needs before an LDS DMA.  The
+  // compiler itself never uses M0 in these kernels, so the value survives
+  // between the statements.
+  __device__ __forceinline__ void copy_full_m0(const FullCopy &f) const {
+    asm volatile("s_mov_b32 m0, %0" : : "s"(f.m0_lat) : "memory", "m0");
+  }
   __device__ __forceinline__ void copy_full(const FullCopy &f, int k, uint32_t voff, uint32_t roff) const {
     if (k == 0)
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                   : : "v"(voff), "s"(f.m0_lat), "s"(f.rsrc) : "memory", "m0");
-    else if (k < TB / NW)
-      asm volatile("s_add_i32 m0, %1, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %3, %4 offen lds"
-                   : : "v"(voff), "s"(f.m0_lat), "i"(k * NW * S_LROW), "s"(f.rsrc), "s"(soff_[k])
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds\n\ts_add_i32 m0, %2, %3"
+                   : : "v"(voff), "s"(f.rsrc), "s"(f.m0_lat), "i"(NW * S_LROW) : "memory", "m0");
+    else if (k < TB / NW - 1)
+      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds\n\ts_add_i32 m0, %3, %4"
+                   : : "v"(voff), "s"(f.rsrc), "s"(soff_[k]), "s"(f.m0_lat), "i"((k + 1) * NW * S_LROW)
                    : "memory", "m0");
+    else if (k == TB / NW - 1)
+      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds\n\ts_mov_b32 m0, %3"
+                   : : "v"(voff), "s"(f.rsrc), "s"(soff_[k]), "s"(f.m0_rope) : "memory", "m0");
     else
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
-                   : : "v"(roff), "s"(f.m0_rope), "s"(f.rsrc), "s"(soff_[NI - 1]) : "memory", "m0");
+      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+                   : : "v"(roff), "s"(f.rsrc), "s"(soff_[NI - 1]) : "memory", "m0");
   }
 
   // MFMAs are written out so that their order is the program order (the
@@ -1012,6 +1023,7 @@ struct DecoderSolo {
     if (COPY == 2) {
       voff = voff_;
       roff = roff_full_;
+      copy_full_m0(fc);
     }
 #pragma unroll
     for (int n = 0; n < RV; ++n) vf[n] = vread(slot_v, vb, n);
