@@ -842,6 +842,26 @@ struct DecoderSolo {
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" MLA_MFMA_WAIT
                    : "+{v[16:31]}"(s) : "v"(k), "v"(q) : "memory");
   }
+  // The same chain pinned to v[16:31] (PAR 0) or v[32:47] (PAR 1), with no
+  // result wait states on its last MFMA: the phase loop alternates the two so
+  // that a block's scores stay where the chain left them (no copy), and the
+  // first read of them comes a value phase later.
+  template <int PAR>
+  __device__ __forceinline__ static void mfma_sp(f32x16 &s, bf16x8 k, bf16x8 q, bool first) {
+    if (PAR == 0) {
+      if (first)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                     : "=&{v[16:31]}"(s) : "v"(k), "v"(q) : "memory");
+      else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+{v[16:31]}"(s) : "v"(k), "v"(q) : "memory");
+    } else {
+      if (first)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                     : "=&{v[32:47]}"(s) : "v"(k), "v"(q) : "memory");
+      else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+{v[32:47]}"(s) : "v"(k), "v"(q) : "memory");
+    }
+  }
   __device__ __forceinline__ static void mfma_o(f32x16 &acc, bf16x8 v, bf16x8 p, bool nop, bool last) {
     if (nop)
       asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p) : "memory");
@@ -995,9 +1015,11 @@ struct DecoderSolo {
   // single LDS wait before each pair covers both of its reads.
   // COPY: 0 no copies, 1 the clamped copies of `cp`, 2 the full-block
   // copies of `fc`.
-  template <int COPY>
+  // PAR < 0: the new scores replace s (a copy out of the chain's registers);
+  // PAR 0 / 1: they go to *s_out, left in the chain's registers (mfma_sp).
+  template <int COPY, int PAR = -1>
   __device__ __forceinline__ void phase(const uint8_t *slot_s, const uint8_t *slot_v, f32x16 &s, bool first,
-                                        const Copy &cp, const FullCopy &fc) {
+                                        const Copy &cp, const FullCopy &fc, f32x16 *s_out = nullptr) {
     const int l = lane_id();
     const int kb = kb_, krb = krb_;
     constexpr int RK = 4, RV = 4, NV = 2 * NT;
@@ -1009,7 +1031,8 @@ struct DecoderSolo {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + RK < KS) kr[ks + RK] = kread(slot_s, kb, krb, ks + RK);
-      mfma_s(sn, kr[ks ^ 1], qf[ks ^ 1], ks == 0, ks == KS - 1);
+      if (PAR < 0) mfma_s(sn, kr[ks ^ 1], qf[ks ^ 1], ks == 0, ks == KS - 1);
+      else mfma_sp<PAR>(sn, kr[ks ^ 1], qf[ks ^ 1], ks == 0);
       if ((ks & 1) == 0 && ks / 2 < 13) soft_step(ks / 2, s, st, false, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1036,7 +1059,8 @@ struct DecoderSolo {
         else copy_full(fc, n / 3, voff, roff);
       }
     }
-    s = sn;
+    if (PAR < 0) s = sn;
+    else *s_out = sn;
   }
 
   // ---- fp8 cache.  A packed row is [512 E4M3 codes | 64 bf16 rotary values
@@ -1451,6 +1475,25 @@ void decode_solo_kernel(DecodeArgs a) {
   // Only the chunk's last block can have rows past its end: the copies of
   // every other block take the full-block form.
   dec.init_full_copy();
+  // two blocks per iteration, the scores alternating between the chain's two
+  // register ranges (s: v[32:47], s1: v[16:31])
+  f32x16 s1;
+  for (; i + 5 < nblk; i += 2) {
+    {
+      const int phys = dec.page_of(i + 3);
+      wait_vmcnt<NI>();
+      barrier_no_fence();
+      dec.phase<2, 0>(slot(i + 1), slot(i), s, i == 0, DecoderSolo::Copy{},
+                      dec.full_copy_of(i + 3, phys, slot(i + 3)), &s1);
+    }
+    {
+      const int phys = dec.page_of(i + 4);
+      wait_vmcnt<NI>();
+      barrier_no_fence();
+      dec.phase<2, 1>(slot(i + 2), slot(i + 1), s1, false, DecoderSolo::Copy{},
+                      dec.full_copy_of(i + 4, phys, slot(i + 4)), &s);
+    }
+  }
   for (; i + 4 < nblk; ++i) {
     const int phys = dec.page_of(i + 3);
     wait_vmcnt<NI>();
