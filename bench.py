@@ -64,11 +64,11 @@ WARM_S = 0.05                  # untimed replays of the timed steps before the t
 # reported only while that source is unchanged.
 DECODE_TRAFFIC = {
     "sources_sha256": {
-        "mla_latent_kv_32_amd/csrc/decode.hip": "eabcde87c81d4c960950e2248195a50984005c9952cfbcabe3d1fece8e8a37cb",
+        "mla_latent_kv_32_amd/csrc/decode.hip": "c74dea56c899e6bdff6b35a184fdb77fb08f270e5f17dfe2e0c6358f6aa998b0",
         "mla_latent_kv_32_amd/csrc/common.h": "f88b1789f340fb1101b55bbc780bc0e7c7204bb6939f3677d3b26086ff681a29",
     },
-    "fetch_kib": 76314.1,
-    "write_kib": 33113.4,
+    "fetch_kib": 76343.6,
+    "write_kib": 33098.3,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     "profile": "profiles/decode_bf16_B32_H128_ctx4096_hbm_counters.md",
